@@ -1,0 +1,48 @@
+"""Writes tests/golden/seeds.json: for every named workload, the first hidden-state seed whose
+tokens all have a router-logit gap of at least 1e-3 between the k-th and (k+1)-th largest logit,
+so that the selected expert set cannot flip under fp32-vs-fp64 accumulation.
+
+Calls only the oracle (for the logits) and the input generator.  Run from the repo root:
+    python tests/golden/make_seeds.py
+"""
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+from oracle import oracle as O  # noqa: E402
+from moe_speculative_decode_amd import synth  # noqa: E402
+
+MIN_GAP = 1e-3
+
+
+def accept(cfg, max_tries=100):
+    layer_router = synth.Layer(cfg, experts=[]).router
+    d = O.layer_desc(cfg)
+    tried = []
+    for seed in range(max_tries):
+        x = synth.make_hidden(cfg, seed)
+        _, ids, w, gap = O.route(d, x, layer_router)
+        tried.append(float(gap.min()))
+        if gap.min() >= MIN_GAP:
+            comp = O.compact(ids, w, cfg.num_experts)
+            return {"hidden_seed": seed, "min_gap": float(gap.min()), "U": comp["U"],
+                    "rejected_min_gaps": tried[:-1]}
+    raise RuntimeError("no accepted seed for %s" % cfg.name)
+
+
+def main():
+    out = {}
+    for name, cfg in synth.CONFIGS.items():
+        out[name] = accept(cfg)
+        print(name, out[name])
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "seeds.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
+if __name__ == "__main__":
+    main()

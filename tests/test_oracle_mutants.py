@@ -1,0 +1,62 @@
+"""Plants plausible mistakes in a private copy of the oracle source, on the CPU, and checks that
+the pins in test_oracle_pins.py catch every one of them.  The oracle under test/oracle is never
+modified; each mutant is compiled into a temporary directory and swapped in with oracle.use()."""
+import os
+import shutil
+
+import pytest
+
+from oracle import oracle as O
+from moe_speculative_decode_amd import synth
+from tests import test_oracle_pins as P
+
+MUTANTS = {
+    "silu_sign": ("a[r] = g[r] / (1.0 + exp(-g[r])) * v[r];", "a[r] = g[r] / (1.0 + exp(g[r])) * v[r];"),
+    "no_shared": ("            for (int h = 0; h < H; ++h) ym[h] += o[h];\n", "\n"),
+    "no_renorm": ("w[j] = p[j].v / kept;", "w[j] = p[j].v;"),
+    "tie_order": ("return (x->id > y->id) - (x->id < y->id);", "return (x->id < y->id) - (x->id > y->id);"),
+    "nibble_swap": ("(c & 1) ? (byte >> 4) : (byte & 15)", "(c & 1) ? (byte & 15) : (byte >> 4)"),
+    "scale_index": ("A->scales[r * (A->cols / 32) + c / 32]", "A->scales[r * (A->cols / 32) + c / 64]"),
+    "gate_up_swapped": ("omat Wg = expert_mat(wf, W->gate, W->gate_s, ids[j], I, H);",
+                        "omat Wg = expert_mat(wf, W->up, W->up_s, ids[j], I, H);"),
+    "no_route_weight": ("ym[h] += w[j] * o[h];", "ym[h] += o[h];"),
+    "wrong_expert": ("omat Wd = expert_mat(wf, W->down, W->down_s, ids[j], H, I);",
+                     "omat Wd = expert_mat(wf, W->down, W->down_s, ids[0], H, I);"),
+    "bf16_shift": ("return dec_f32((uint32_t)b << 16);", "return dec_f32((uint32_t)b << 15);"),
+    "e2m1_bias": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e - 2)"),
+    "compact_slot": ("row_slot[row] = p % k;", "row_slot[row] = p / k;"),
+    "gap_index": ("ls[k - 1].v - ls[k].v", "ls[k - 2].v - ls[k].v"),
+    "softmax_sign": ("p[e].v = exp(l[e] - lmax) / z;", "p[e].v = exp(lmax - l[e]) / z;"),
+}
+
+# pins that run quickly; together they must catch each mutant
+PINS = [
+    P.test_e2m1_table,
+    P.test_mxfp4_nibble_and_scale_layout,
+    lambda: P.test_bf16_decoder_all_patterns(),
+    lambda: P.test_routing_vs_full_sort(synth.BF16),
+    P.test_tie_break_lower_id_first,
+    lambda: P.test_dense_brute_force(synth.BF16, 64, 16, 4, 32, 32, (2, 3)),
+    lambda: P.test_dense_brute_force(synth.MXFP4, 64, 16, 4, 32, 64, (3, 3)),
+    lambda: P.test_closed_form_swiglu(synth.BF16, 2.0, 0.5),
+    lambda: P.test_compaction_vs_sets(6, 8, 512),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(O.SRC).read()
+    assert src.count(old) == 1, "mutation site vanished: " + name
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    lib = O.build(force=True, src=str(path), out=str(tmp_path / "libmutant.so"))
+    caught = []
+    with O.use(lib):
+        for pin in PINS:
+            try:
+                pin()
+            except AssertionError:
+                caught.append(getattr(pin, "__name__", "lambda"))
+    assert caught, "mutant %s passed every pin" % name
+    shutil.rmtree(tmp_path, ignore_errors=True)
