@@ -1,0 +1,149 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) routed-expert MoE decode layer.
+ *
+ * The operation is one MoE layer of Ling-3.0-flash at decode: M tokens (1 for plain batch-1
+ * decode, or a packed speculative-verify window of several tokens) go through a router gate,
+ * softmax top-k routing with renormalised weights, SwiGLU routed experts and one shared expert,
+ * and a weighted combine.
+ *   - shapes: hidden 2,560, eight of 512 routed experts plus one shared expert per token
+ *     ("3 ways to boost MoE inference on NVIDIA DGX Spark", section "Model and baseline
+ *     configuration"); moe_intermediate_size 768 ("Chasing the Batch-1 Floor: Ling-3.0-flash
+ *     Speculative Decode on Blackwell", section "Where the time goes now");
+ *   - router chain norm -> gate matvec -> top-k, gate weight in bf16 with fp32 accumulation
+ *     (same page, sections "PDL: stacking the latency floors of small kernels" and
+ *     "bf16 router gate and lm_head");
+ *   - silu(gate) * up computed in float and rounded once (same page, "Two fusions and a retune");
+ *   - the combine is one fp32 sum of weight x expert output with a single final cast (same page,
+ *     PDL section);
+ *   - a packed ragged verify batch described by cu_seqlens-style offsets ("DSpark in SGLang",
+ *     section "Ragged verify under full CUDA graphs");
+ *   - MXFP4 expert weights ("3 ways to boost MoE inference on NVIDIA DGX Spark", "Optimization 1"),
+ *     laid out per the OCP Microscaling v1.0 format: E2M1 codes, two per byte with element 2i in
+ *     the low nibble, and one E8M0 scale byte per 32 consecutive elements along K.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is DEVICE memory owned by the caller; pointers are borrowed only until
+ *     the enqueued work finishes.  Struct arguments (moe_desc_t, moe_weights_t, moe_dispatch_t)
+ *     are host memory, read during the call and not retained.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls only enqueue
+ *     work on it: they never synchronise, never allocate, never read device memory on the host,
+ *     and can be captured into a hipGraph.
+ *   - Arguments are validated on the host before anything is enqueued; a call that returns a
+ *     negative status has enqueued nothing.  MOE_ERR_HIP reports a failed launch.  Faults inside
+ *     the kernels surface at the caller's next synchronisation, as for any HIP kernel.
+ *   - The workspace `ws` (size from moe_workspace_bytes) must be zero-filled once before its first
+ *     use; every call leaves its counters at zero again.  Calls that share a workspace must be
+ *     ordered (the same stream, or synchronised); calls with distinct workspaces may overlap.
+ *   - The library keeps no mutable global state; it is safe to call from several host threads.
+ *   - Matrices are row-major [out][in] with the input dimension K contiguous (nn.Linear layout).
+ *     Every pointer must be 16-byte aligned.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element storage formats. */
+typedef enum {
+    MOE_FMT_F32 = 0,   /* IEEE binary32 */
+    MOE_FMT_BF16 = 1,  /* bfloat16 */
+    MOE_FMT_MXFP4 = 2  /* OCP MX v1.0 FP4 (E2M1) codes + E8M0 scale per 32 elements of K */
+} moe_format_t;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,      /* a required pointer is NULL */
+    MOE_ERR_SHAPE = -2,     /* a size is out of range or not a supported multiple */
+    MOE_ERR_FORMAT = -3,    /* unsupported format or format pair */
+    MOE_ERR_WORKSPACE = -4, /* ws_bytes smaller than moe_workspace_bytes(desc) */
+    MOE_ERR_OFFSETS = -5,   /* R out of range (host); or, in the device status word, offsets that
+                               are not 0 = o[0] <= o[1] <= ... <= o[R] = M */
+    MOE_ERR_HIP = -6,       /* a HIP runtime call failed */
+    MOE_ERR_ALIGN = -7      /* a pointer is not 16-byte aligned */
+} moe_status_t;
+
+/* Largest supported values (checked on the host). */
+#define MOE_MAX_TOKENS 16   /* tokens per call (M) */
+#define MOE_MAX_EXPERTS 512 /* routed experts (E) */
+#define MOE_MAX_TOPK 16     /* experts per token (k) */
+
+/* Layer description.  H, I, Is multiples of 8 (of 32 for MXFP4); H <= 4096; I, Is <= 2048;
+   1 <= k <= min(E, 16); E <= 512; 1 <= max_tokens <= 16; max_tokens * H * (bytes per activation)
+   <= 96 KiB (the token rows are staged in LDS). */
+typedef struct {
+    int32_t hidden;        /* H */
+    int32_t num_experts;   /* E */
+    int32_t top_k;         /* k */
+    int32_t inter;         /* I, routed expert intermediate size */
+    int32_t shared_inter;  /* Is, shared expert intermediate size; 0 = no shared expert */
+    int32_t max_tokens;    /* largest M the workspace is sized for */
+    int32_t act_format;    /* x, router weight and y: MOE_FMT_BF16, or MOE_FMT_F32 with F32 weights */
+    int32_t weight_format; /* routed and shared expert weights: F32 (with F32 act), BF16 or MXFP4 */
+} moe_desc_t;
+
+/* Expert weights.  Routed stacks are expert-major: gate, up [E][I][H]; down [E][H][I].
+   Shared expert: sh_gate, sh_up [Is][H]; sh_down [H][Is].  For MXFP4 the data pointers hold the
+   packed codes (K/2 bytes per row) and the *_s pointers the scales ([rows][K/32] bytes); the *_s
+   pointers are ignored (may be NULL) for the other formats. */
+typedef struct {
+    const void *gate, *up, *down;
+    const uint8_t *gate_s, *up_s, *down_s;
+    const void *sh_gate, *sh_up, *sh_down;
+    const uint8_t *sh_gate_s, *sh_up_s, *sh_down_s;
+} moe_weights_t;
+
+/* Optional device outputs describing the dispatch of a call (each member nullable).
+   Units are the distinct routed experts of the batch in ascending id order, then the shared
+   expert (id reported as E).  Pair rows are the (token, slot) pairs grouped by unit, ascending
+   token inside a unit; the shared unit's rows hold every token with slot k and weight 1.
+   ("Chasing the Batch-1 Floor", "Two fusions and a retune": stable per-expert order, 512 routed
+   + 1 shared dispatch axis.)  Sizes for U distinct experts: */
+typedef struct {
+    int32_t* unit_count;  /* [1]   U */
+    int32_t* unit_expert; /* [U+1] (allocate min(M*k, E) + 1) */
+    int32_t* unit_off;    /* [U+2] unit u owns rows [unit_off[u], unit_off[u+1]) (alloc min(M*k,E)+2) */
+    int32_t* row_token;   /* [M*k+M] */
+    int32_t* row_slot;    /* [M*k+M] */
+    float* row_weight;    /* [M*k+M] routing weight of the row */
+    int32_t* req_unique;  /* [R] distinct routed experts per request; needs req_offsets */
+} moe_dispatch_t;
+
+/* Workspace size in bytes for this description, or 0 when the description is invalid. */
+size_t moe_workspace_bytes(const moe_desc_t* d);
+
+/* Router only: logits = x [M][H] . w_router [E][H]^T with fp32 accumulation, then per token the k
+   largest logits (ties: lower expert id) and weights softmax-renormalised over those k.
+   topk_ids [M][k] and topk_w [M][k] receive them in descending weight order.  `disp` (nullable)
+   additionally receives the batch dispatch.  Same routing as inside moe_decode_forward. */
+int moe_route(const moe_desc_t* d, int32_t M, const void* x, const void* w_router, int32_t* topk_ids,
+              float* topk_w, const moe_dispatch_t* disp, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer: y [M][H] = sum_j w[m,j] * expert_{id[m,j]}(x_m) + shared(x_m), where
+   expert(x) = Wd (silu(Wg x) * (Wu x)).  Each distinct selected expert's weights are read from
+   memory once per call, however many of the M tokens chose it.
+   req_offsets: device int32 [R+1] packed-request offsets (0 = o[0] <= ... <= o[R] = M, requests may
+   be empty, 1 <= R <= MOE_MAX_TOKENS) or NULL (then R is ignored).  They do not change y; they feed disp->req_unique and are checked on the
+   device (a violation sets MOE_ERR_OFFSETS in the status word, see moe_read_status).
+   topk_ids_out, topk_w_out, disp: nullable extra outputs as in moe_route. */
+int moe_decode_forward(const moe_desc_t* d, int32_t M, const void* x, const void* w_router,
+                       const moe_weights_t* w, const int32_t* req_offsets, int32_t R, void* y,
+                       int32_t* topk_ids_out, float* topk_w_out, const moe_dispatch_t* disp, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Debug helper, NOT for the hot path: synchronises `stream`, copies the workspace's device status
+   word to *status (0 or a negative moe_status_t of the latest failing call), then clears it. */
+int moe_read_status(void* ws, void* stream, int32_t* status);
+
+/* Static description of a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

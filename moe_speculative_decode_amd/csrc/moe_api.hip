@@ -1,0 +1,226 @@
+// C ABI of the routed-expert MoE decode layer: argument validation, workspace layout and the
+// launch sequence.  Everything here runs on the host and enqueues work only; nothing reads device
+// memory or synchronises, except moe_read_status which says so in its name.
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+using moe::Params;
+using moe::Workspace;
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool is_aligned(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// byte offsets of the workspace regions for a description (validated by the caller)
+struct Layout {
+    size_t status, route_cnt, n_units, tile_cnt, logits, unit_expert, unit_mask, unit_off, pair_row, row_w, act,
+        part, total;
+};
+
+Layout layout(const moe_desc_t& d) {
+    const size_t Mx = (size_t)d.max_tokens, E = (size_t)d.num_experts, k = (size_t)d.top_k, H = (size_t)d.hidden;
+    const size_t ka = (size_t)(d.inter > d.shared_inter ? d.inter : d.shared_inter);
+    const size_t rows = Mx * (k + 1);
+    const size_t ntiles = (H + moe::kCombineTile - 1) / moe::kCombineTile;
+    Layout L;
+    size_t o = 0;
+    L.status = o;
+    L.route_cnt = o + 4;
+    L.n_units = o + 8;
+    o += kAlign;
+    L.tile_cnt = o;
+    o = up(o + 4 * ntiles);
+    L.logits = o;
+    o = up(o + 4 * Mx * E);
+    L.unit_expert = o;
+    o = up(o + 4 * (E + 1));
+    L.unit_mask = o;
+    o = up(o + 4 * (E + 1));
+    L.unit_off = o;
+    o = up(o + 4 * (E + 2));
+    L.pair_row = o;
+    o = up(o + 4 * Mx * k);
+    L.row_w = o;
+    o = up(o + 4 * rows);
+    L.act = o;
+    o = up(o + 4 * rows * ka);
+    L.part = o;
+    o = up(o + 4 * rows * H);
+    L.total = o;
+    return L;
+}
+
+int check_desc(const moe_desc_t* d) {
+    if (!d) return MOE_ERR_NULL;
+    const bool f32 = d->act_format == MOE_FMT_F32;
+    if (d->act_format != MOE_FMT_F32 && d->act_format != MOE_FMT_BF16) return MOE_ERR_FORMAT;
+    if (f32 && d->weight_format != MOE_FMT_F32) return MOE_ERR_FORMAT;
+    if (!f32 && d->weight_format != MOE_FMT_BF16 && d->weight_format != MOE_FMT_MXFP4) return MOE_ERR_FORMAT;
+    const int mult = d->weight_format == MOE_FMT_MXFP4 ? 32 : 8;
+    if (d->hidden <= 0 || d->hidden > 4096 || d->hidden % mult) return MOE_ERR_SHAPE;
+    if (d->num_experts <= 0 || d->num_experts > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+    if (d->top_k <= 0 || d->top_k > MOE_MAX_TOPK || d->top_k > d->num_experts) return MOE_ERR_SHAPE;
+    if (d->inter <= 0 || d->inter > 2048 || d->inter % mult) return MOE_ERR_SHAPE;
+    if (d->shared_inter < 0 || d->shared_inter > 2048 || d->shared_inter % mult) return MOE_ERR_SHAPE;
+    if (d->max_tokens <= 0 || d->max_tokens > MOE_MAX_TOKENS) return MOE_ERR_SHAPE;
+    // the gate/up kernel stages all M token rows in LDS
+    const size_t xbytes = (size_t)d->max_tokens * d->hidden * (f32 ? 4 : 2);
+    if (xbytes > 96 * 1024) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+int fill_common(Params& p, const moe_desc_t* d, int32_t M, const void* x, const void* wr, void* ws, size_t ws_bytes) {
+    int st = check_desc(d);
+    if (st) return st;
+    if (M < 1 || M > d->max_tokens) return MOE_ERR_SHAPE;
+    if (!x || !wr || !ws) return MOE_ERR_NULL;
+    if (!is_aligned(x) || !is_aligned(wr) || !is_aligned(ws)) return MOE_ERR_ALIGN;
+    const Layout L = layout(*d);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    memset(&p, 0, sizeof(p));
+    p.H = d->hidden;
+    p.E = d->num_experts;
+    p.k = d->top_k;
+    p.I = d->inter;
+    p.Is = d->shared_inter;
+    p.M = M;
+    p.act_fmt = d->act_format;
+    p.w_fmt = d->weight_format;
+    p.act_stride = d->inter > d->shared_inter ? d->inter : d->shared_inter;
+    p.x = x;
+    p.wr = wr;
+    char* b = (char*)ws;
+    Workspace& W = p.ws;
+    W.status = (uint32_t*)(b + L.status);
+    W.route_cnt = (uint32_t*)(b + L.route_cnt);
+    W.n_units = (int32_t*)(b + L.n_units);
+    W.tile_cnt = (uint32_t*)(b + L.tile_cnt);
+    W.logits = (float*)(b + L.logits);
+    W.unit_expert = (int32_t*)(b + L.unit_expert);
+    W.unit_mask = (uint32_t*)(b + L.unit_mask);
+    W.unit_off = (int32_t*)(b + L.unit_off);
+    W.pair_row = (int32_t*)(b + L.pair_row);
+    W.row_w = (float*)(b + L.row_w);
+    W.act = (float*)(b + L.act);
+    W.part = (float*)(b + L.part);
+    return MOE_OK;
+}
+
+int check_weights(const moe_desc_t* d, const moe_weights_t* w) {
+    if (!w) return MOE_ERR_NULL;
+    const bool mx = d->weight_format == MOE_FMT_MXFP4;
+    const void* need[] = {w->gate, w->up, w->down};
+    for (const void* q : need) {
+        if (!q) return MOE_ERR_NULL;
+        if (!is_aligned(q)) return MOE_ERR_ALIGN;
+    }
+    if (mx) {
+        const void* sc[] = {w->gate_s, w->up_s, w->down_s};
+        for (const void* q : sc) {
+            if (!q) return MOE_ERR_NULL;
+            if (!is_aligned(q)) return MOE_ERR_ALIGN;
+        }
+    }
+    if (d->shared_inter > 0) {
+        const void* sh[] = {w->sh_gate, w->sh_up, w->sh_down};
+        for (const void* q : sh) {
+            if (!q) return MOE_ERR_NULL;
+            if (!is_aligned(q)) return MOE_ERR_ALIGN;
+        }
+        if (mx) {
+            const void* ss[] = {w->sh_gate_s, w->sh_up_s, w->sh_down_s};
+            for (const void* q : ss) {
+                if (!q) return MOE_ERR_NULL;
+                if (!is_aligned(q)) return MOE_ERR_ALIGN;
+            }
+        }
+    }
+    return MOE_OK;
+}
+
+int num_cus(int* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (hipDeviceGetAttribute(out, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MOE_ERR_HIP;
+    if (*out <= 0) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_desc_t* d) {
+    if (check_desc(d)) return 0;
+    return layout(*d).total;
+}
+
+int moe_route(const moe_desc_t* d, int32_t M, const void* x, const void* w_router, int32_t* topk_ids, float* topk_w,
+              const moe_dispatch_t* disp, void* ws, size_t ws_bytes, void* stream) {
+    Params p;
+    int st = fill_common(p, d, M, x, w_router, ws, ws_bytes);
+    if (st) return st;
+    if (!topk_ids || !topk_w) return MOE_ERR_NULL;
+    p.topk_ids = topk_ids;
+    p.topk_w = topk_w;
+    if (disp) p.disp = *disp;
+    p.disp.req_unique = nullptr;
+    int cus = 0;
+    if ((st = num_cus(&cus))) return st;
+    return moe::launch_layer(p, true, cus, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_decode_forward(const moe_desc_t* d, int32_t M, const void* x, const void* w_router, const moe_weights_t* w,
+                       const int32_t* req_offsets, int32_t R, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                       const moe_dispatch_t* disp, void* ws, size_t ws_bytes, void* stream) {
+    Params p;
+    int st = fill_common(p, d, M, x, w_router, ws, ws_bytes);
+    if (st) return st;
+    if ((st = check_weights(d, w))) return st;
+    if (!y) return MOE_ERR_NULL;
+    if (!is_aligned(y)) return MOE_ERR_ALIGN;
+    if (req_offsets && (R < 1 || R > MOE_MAX_TOKENS)) return MOE_ERR_OFFSETS;
+    p.w = *w;
+    p.req_off = req_offsets;
+    p.R = req_offsets ? R : 0;
+    p.y = y;
+    p.topk_ids = topk_ids_out;
+    p.topk_w = topk_w_out;
+    if (disp) p.disp = *disp;
+    if (!req_offsets) p.disp.req_unique = nullptr;
+    int cus = 0;
+    if ((st = num_cus(&cus))) return st;
+    return moe::launch_layer(p, false, cus, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_read_status(void* ws, void* stream, int32_t* status) {
+    if (!ws || !status) return MOE_ERR_NULL;
+    uint32_t v = 0;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+    if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+    const uint32_t zero = 0;
+    if (hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return MOE_ERR_HIP;
+    *status = (v & moe::kStatusOffsets) ? MOE_ERR_OFFSETS : MOE_OK;
+    return MOE_OK;
+}
+
+const char* moe_status_string(int status) {
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or not a supported multiple";
+    case MOE_ERR_FORMAT: return "unsupported format or format pair";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
+    case MOE_ERR_OFFSETS: return "request offsets out of range or not monotone from 0 to M";
+    case MOE_ERR_HIP: return "a HIP runtime call failed";
+    case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

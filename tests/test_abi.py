@@ -1,0 +1,109 @@
+"""The C ABI library loads, exports every entry point the header declares, and rejects invalid
+arguments on the host before anything is launched (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_speculative_decode_amd as mdl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_decode.h")
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^(?:size_t|int|const char\*)\s+(moe_\w+)\(", text, flags=re.M)
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) == set(mdl.EXPORTED)
+    L = mdl.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # the exports are plain C symbols (no C++ mangling)
+    nm = os.popen("nm -D --defined-only %s" % mdl.LIB_PATH).read()
+    for n in names:
+        assert re.search(r"\bT %s$" % n, nm, flags=re.M), n
+
+
+def ling(**kw):
+    d = dict(hidden=2560, num_experts=512, top_k=8, inter=768, shared_inter=768, max_tokens=16,
+             act_format=mdl.MOE_FMT_BF16, weight_format=mdl.MOE_FMT_BF16)
+    d.update(kw)
+    return mdl.moe_desc_t(**d)
+
+
+def test_workspace_bytes():
+    n = mdl.moe_workspace_bytes(ling())
+    # at least logits + SwiGLU rows + partial rows for 16 tokens
+    assert n >= 4 * (16 * 512 + 16 * 9 * 768 + 16 * 9 * 2560)
+    assert mdl.moe_workspace_bytes(ling(max_tokens=1)) < n
+    for bad in (ling(top_k=0), ling(top_k=600), ling(num_experts=513), ling(hidden=2564), ling(max_tokens=17),
+                ling(act_format=mdl.MOE_FMT_F32), ling(weight_format=7), ling(inter=0),
+                ling(weight_format=mdl.MOE_FMT_MXFP4, hidden=2560 + 8), ling(hidden=8192)):
+        assert mdl.moe_workspace_bytes(bad) == 0
+
+
+def call_route(desc, M=1, x=FAKE, wr=FAKE, ids=FAKE, w=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return mdl.lib().moe_route(ctypes.byref(desc), M, x, wr, ids, w, None, ws, ws_bytes, None)
+
+
+def call_fwd(desc, M=1, weights=None, y=FAKE, off=None, R=0, ws_bytes=1 << 30, x=FAKE):
+    W = weights if weights is not None else mdl.moe_weights_t(*([FAKE] * 12))
+    return mdl.lib().moe_decode_forward(ctypes.byref(desc), M, x, FAKE, ctypes.byref(W), off, R, y, None, None,
+                                        None, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,M,status", [
+    (dict(), 0, mdl.MOE_ERR_SHAPE),
+    (dict(), 17, mdl.MOE_ERR_SHAPE),
+    (dict(max_tokens=4), 5, mdl.MOE_ERR_SHAPE),
+    (dict(top_k=513), 1, mdl.MOE_ERR_SHAPE),
+    (dict(act_format=mdl.MOE_FMT_F32), 1, mdl.MOE_ERR_FORMAT),
+    (dict(weight_format=mdl.MOE_FMT_MXFP4, inter=776), 1, mdl.MOE_ERR_SHAPE),
+])
+def test_route_rejects(kw, M, status):
+    assert call_route(ling(**kw), M=M) == status
+
+
+def test_route_null_align_workspace():
+    d = ling()
+    assert call_route(d, x=None) == mdl.MOE_ERR_NULL
+    assert call_route(d, ids=None) == mdl.MOE_ERR_NULL
+    assert call_route(d, x=FAKE + 4) == mdl.MOE_ERR_ALIGN
+    assert call_route(d, ws_bytes=mdl.moe_workspace_bytes(d) - 1) == mdl.MOE_ERR_WORKSPACE
+    assert mdl.lib().moe_route(None, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == mdl.MOE_ERR_NULL
+
+
+def test_forward_rejects():
+    d = ling()
+    assert call_fwd(d, y=None) == mdl.MOE_ERR_NULL
+    assert call_fwd(d, y=FAKE + 8) == mdl.MOE_ERR_ALIGN
+    W = mdl.moe_weights_t(*([FAKE] * 12))
+    W.down = None
+    assert call_fwd(d, weights=W) == mdl.MOE_ERR_NULL
+    W = mdl.moe_weights_t(*([FAKE] * 12))
+    W.sh_up = None
+    assert call_fwd(d, weights=W) == mdl.MOE_ERR_NULL
+    assert call_fwd(ling(shared_inter=0), weights=W) != mdl.MOE_ERR_NULL  # no shared expert: not needed
+    W = mdl.moe_weights_t(*([FAKE] * 12))
+    W.gate_s = None
+    assert call_fwd(ling(weight_format=mdl.MOE_FMT_MXFP4), weights=W) == mdl.MOE_ERR_NULL
+    W = mdl.moe_weights_t(*([FAKE] * 12))
+    W.up = FAKE + 2
+    assert call_fwd(d, weights=W) == mdl.MOE_ERR_ALIGN
+    assert call_fwd(d, off=FAKE, R=0) == mdl.MOE_ERR_OFFSETS
+    assert call_fwd(d, off=FAKE, R=17) == mdl.MOE_ERR_OFFSETS
+    assert call_fwd(d, ws_bytes=100) == mdl.MOE_ERR_WORKSPACE
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert mdl.moe_status_string(s) and mdl.moe_status_string(s) != "unknown status"
+    assert mdl.moe_status_string(-99) == "unknown status"
+    with pytest.raises(mdl.MoeError):
+        mdl._check(mdl.MOE_ERR_SHAPE, "x")
