@@ -64,7 +64,9 @@ typedef enum {
     MOE_ERR_OFFSETS = -5,   /* R out of range (host); or, in the device status word, offsets that
                                are not 0 = o[0] <= o[1] <= ... <= o[R] = M */
     MOE_ERR_HIP = -6,       /* a HIP runtime call failed */
-    MOE_ERR_ALIGN = -7      /* a pointer is not 16-byte aligned */
+    MOE_ERR_ALIGN = -7,     /* a pointer is not 16-byte aligned */
+    MOE_ERR_TIMEOUT = -8    /* device status only: a cross-workgroup wait gave up (its results are
+                               invalid); happens only if the grid is not fully resident */
 } moe_status_t;
 
 /* Largest supported values (checked on the host). */
@@ -136,7 +138,8 @@ int moe_decode_forward(const moe_desc_t* d, int32_t M, const void* x, const void
                        size_t ws_bytes, void* stream);
 
 /* Debug helper, NOT for the hot path: synchronises `stream`, copies the workspace's device status
-   word to *status (0 or a negative moe_status_t of the latest failing call), then clears it. */
+   word to *status (MOE_OK, MOE_ERR_OFFSETS or MOE_ERR_TIMEOUT, accumulated over the calls since the
+   last read), then clears it. */
 int moe_read_status(void* ws, void* stream, int32_t* status);
 
 /* Static description of a status code. */

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libmoe_decode.so")
 MOE_FMT_F32, MOE_FMT_BF16, MOE_FMT_MXFP4 = 0, 1, 2
 MOE_OK = 0
 MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_FORMAT, MOE_ERR_WORKSPACE = -1, -2, -3, -4
-MOE_ERR_OFFSETS, MOE_ERR_HIP, MOE_ERR_ALIGN = -5, -6, -7
+MOE_ERR_OFFSETS, MOE_ERR_HIP, MOE_ERR_ALIGN, MOE_ERR_TIMEOUT = -5, -6, -7, -8
 MOE_MAX_TOKENS, MOE_MAX_EXPERTS, MOE_MAX_TOPK = 16, 512, 16
 
 EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_decode_forward", "moe_read_status", "moe_status_string")

@@ -18,35 +18,21 @@ bool is_aligned(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 // byte offsets of the workspace regions for a description (validated by the caller)
 struct Layout {
-    size_t status, route_cnt, n_units, tile_cnt, logits, unit_expert, unit_mask, unit_off, pair_row, row_w, act,
-        part, total;
+    size_t hdr, ctr, logits, act, part, total;
 };
 
 Layout layout(const moe_desc_t& d) {
     const size_t Mx = (size_t)d.max_tokens, E = (size_t)d.num_experts, k = (size_t)d.top_k, H = (size_t)d.hidden;
     const size_t ka = (size_t)(d.inter > d.shared_inter ? d.inter : d.shared_inter);
     const size_t rows = Mx * (k + 1);
-    const size_t ntiles = (H + moe::kCombineTile - 1) / moe::kCombineTile;
     Layout L;
     size_t o = 0;
-    L.status = o;
-    L.route_cnt = o + 4;
-    L.n_units = o + 8;
-    o += kAlign;
-    L.tile_cnt = o;
-    o = up(o + 4 * ntiles);
+    L.hdr = o;
+    o += moe::kHdrBytes;
+    L.ctr = o;
+    o = up(o + 2 * sizeof(uint32_t) * (size_t)moe::kSetWords);
     L.logits = o;
     o = up(o + 4 * Mx * E);
-    L.unit_expert = o;
-    o = up(o + 4 * (E + 1));
-    L.unit_mask = o;
-    o = up(o + 4 * (E + 1));
-    L.unit_off = o;
-    o = up(o + 4 * (E + 2));
-    L.pair_row = o;
-    o = up(o + 4 * Mx * k);
-    L.row_w = o;
-    o = up(o + 4 * rows);
     L.act = o;
     o = up(o + 4 * rows * ka);
     L.part = o;
@@ -96,16 +82,9 @@ int fill_common(Params& p, const moe_desc_t* d, int32_t M, const void* x, const 
     p.wr = wr;
     char* b = (char*)ws;
     Workspace& W = p.ws;
-    W.status = (uint32_t*)(b + L.status);
-    W.route_cnt = (uint32_t*)(b + L.route_cnt);
-    W.n_units = (int32_t*)(b + L.n_units);
-    W.tile_cnt = (uint32_t*)(b + L.tile_cnt);
+    W.hdr = (uint32_t*)(b + L.hdr);
+    W.ctr = (uint32_t*)(b + L.ctr);
     W.logits = (float*)(b + L.logits);
-    W.unit_expert = (int32_t*)(b + L.unit_expert);
-    W.unit_mask = (uint32_t*)(b + L.unit_mask);
-    W.unit_off = (int32_t*)(b + L.unit_off);
-    W.pair_row = (int32_t*)(b + L.pair_row);
-    W.row_w = (float*)(b + L.row_w);
     W.act = (float*)(b + L.act);
     W.part = (float*)(b + L.part);
     return MOE_OK;
@@ -170,9 +149,10 @@ int moe_route(const moe_desc_t* d, int32_t M, const void* x, const void* w_route
     p.topk_w = topk_w;
     if (disp) p.disp = *disp;
     p.disp.req_unique = nullptr;
+    p.route_only = 1;
     int cus = 0;
     if ((st = num_cus(&cus))) return st;
-    return moe::launch_layer(p, true, cus, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return moe::launch_layer(p, cus, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int moe_decode_forward(const moe_desc_t* d, int32_t M, const void* x, const void* w_router, const moe_weights_t* w,
@@ -195,7 +175,7 @@ int moe_decode_forward(const moe_desc_t* d, int32_t M, const void* x, const void
     if (!req_offsets) p.disp.req_unique = nullptr;
     int cus = 0;
     if ((st = num_cus(&cus))) return st;
-    return moe::launch_layer(p, false, cus, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return moe::launch_layer(p, cus, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int moe_read_status(void* ws, void* stream, int32_t* status) {
@@ -205,7 +185,7 @@ int moe_read_status(void* ws, void* stream, int32_t* status) {
     if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
     const uint32_t zero = 0;
     if (hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return MOE_ERR_HIP;
-    *status = (v & moe::kStatusOffsets) ? MOE_ERR_OFFSETS : MOE_OK;
+    *status = (v & moe::kStatusTimeout) ? MOE_ERR_TIMEOUT : ((v & moe::kStatusOffsets) ? MOE_ERR_OFFSETS : MOE_OK);
     return MOE_OK;
 }
 
@@ -219,6 +199,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_OFFSETS: return "request offsets out of range or not monotone from 0 to M";
     case MOE_ERR_HIP: return "a HIP runtime call failed";
     case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MOE_ERR_TIMEOUT: return "a cross-workgroup wait timed out (grid not fully resident?)";
     default: return "unknown status";
     }
 }

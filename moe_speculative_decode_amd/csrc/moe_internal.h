@@ -1,4 +1,4 @@
-// Internal interface between the C ABI (moe_api.hip) and the kernels (moe_layer.hip).
+// Internal interface between the C ABI (moe_api.hip) and the kernel (moe_layer.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,34 +11,48 @@ namespace moe {
 constexpr int kMaxTokens = MOE_MAX_TOKENS;
 constexpr int kMaxExperts = MOE_MAX_EXPERTS;
 constexpr int kMaxTopK = MOE_MAX_TOPK;
-constexpr int kThreads = 256;       // threads per workgroup of every kernel (4 wave64)
+constexpr int kThreads = 256;  // threads per workgroup (4 wave64)
 constexpr int kWaves = kThreads / 64;
-constexpr int kCombineTile = 64;    // rows of y finished together by the last contributing workgroup
+constexpr int kCombineTile = 64;  // rows of y finished together by their last contributing workgroup
+constexpr int kMaxTiles = 64;     // ceil(4096 / kCombineTile)
 
-// status bits OR-ed into the workspace status word by the kernels
+// Cross-workgroup counters.  Each counter owns a 256-byte line (atomics on one line serialise).
+// Two sets alternate between consecutive calls: call c counts in set c & 1 and clears set
+// (c + 1) & 1, which the previous call used and the next call will use.
+constexpr int kLineWords = 64;
+constexpr int kRouteSubs = 8;  // arrivals at the routing barrier are split over 8 sub-counters
+constexpr int kLineRouteTop = kRouteSubs;
+constexpr int kLineShared = kRouteSubs + 1;
+constexpr int kLineUnit0 = kRouteSubs + 2;            // kMaxExperts unit counters
+constexpr int kLineTile0 = kLineUnit0 + kMaxExperts;  // kMaxTiles tile counters
+constexpr int kSetLines = kLineTile0 + kMaxTiles;
+constexpr int kSetWords = kSetLines * kLineWords;
+
+// workspace header words
+constexpr int kHdrStatus = 0;  // OR of status bits
+constexpr int kHdrCall = 1;    // number of calls made with this workspace
+constexpr int kHdrBytes = 256;
+
+// status bits set by the kernel
 constexpr uint32_t kStatusOffsets = 1u;
+constexpr uint32_t kStatusTimeout = 2u;
 
-// Device-side views of the caller's workspace.  All counters are zero between calls.
 struct Workspace {
-    uint32_t* status;     // [1]
-    uint32_t* route_cnt;  // [1]   router workgroups finished
-    uint32_t* tile_cnt;   // [ceil(H / kCombineTile)] down-projection rows finished per y tile
-    float* logits;        // [max_tokens][E]
-    // dispatch tables (written by the router's last workgroup)
-    int32_t* n_units;     // [1]   U (routed units; the shared unit, if any, follows them)
-    int32_t* unit_expert; // [E + 1]
-    uint32_t* unit_mask;  // [E + 1] token bitmask of the unit
-    int32_t* unit_off;    // [E + 2] first pair row of the unit
-    int32_t* pair_row;    // [max_tokens][k] pair row of (token, slot)
-    float* row_w;         // [max_tokens * (k + 1)] routing weight of a pair row
-    float* act;           // [max_tokens * (k + 1)][max(I, Is)] SwiGLU outputs per pair row (fp32)
-    float* part;          // [max_tokens * (k + 1)][H] down-projection outputs per pair row (fp32)
+    uint32_t* hdr;    // [kHdrBytes / 4]
+    uint32_t* ctr;    // [2][kSetWords]
+    float* logits;    // [max_tokens][E]
+    float* act;       // [max_tokens * (k + 1)][act_stride]  SwiGLU output per pair row
+    float* part;      // [max_tokens * (k + 1)][H]           down projection per pair row
 };
 
 struct Params {
     int H, E, k, I, Is, M;
     int act_fmt, w_fmt;
-    int act_stride;       // row stride (elements) of Workspace::act
+    int act_stride;   // row stride (elements) of Workspace::act = max(I, Is)
+    int route_only;   // 1: routing outputs only (moe_route)
+    // LDS layout (bytes from the dynamic LDS base)
+    int lds_x, lds_sh, lds_act, lds_total;
+    int sh_rows;      // shared-expert down rows prefetched per workgroup (ceil(H / grid))
     const void* x;
     const void* wr;
     moe_weights_t w;
@@ -51,7 +65,7 @@ struct Params {
     Workspace ws;
 };
 
-// Launch sequence (implemented in moe_layer.hip).  `route_only` stops after routing.
-hipError_t launch_layer(const Params& p, bool route_only, int num_cus, hipStream_t stream);
+// Enqueues one call.  Fills the LDS layout fields of a copy of `p`.
+hipError_t launch_layer(const Params& p, int num_cus, hipStream_t stream);
 
 }  // namespace moe

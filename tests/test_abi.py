@@ -102,7 +102,7 @@ def test_forward_rejects():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert mdl.moe_status_string(s) and mdl.moe_status_string(s) != "unknown status"
     assert mdl.moe_status_string(-99) == "unknown status"
     with pytest.raises(mdl.MoeError):

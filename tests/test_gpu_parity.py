@@ -43,6 +43,7 @@ SMALL = [
 def _check_case(case, disp=None):
     y, ids, w = case.run(disp=disp)
     torch.cuda.synchronize()
+    assert mdl.moe_read_status(case.ws) == mdl.MOE_OK
     err, rms = G.y_error(y, case.y_ref)
     G.log(case.cfg.name, "M=%d U=%d err/rms=%.3e rms=%.3e" % (case.M, case.comp_ref["U"], err, rms))
     G.check_routing(ids, w, case.ids_ref, case.w_ref)
