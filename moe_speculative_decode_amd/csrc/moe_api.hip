@@ -32,7 +32,7 @@ Layout layout(const moe_desc_t& d) {
     L.ctr = o;
     o = up(o + 2 * sizeof(uint32_t) * (size_t)moe::kSetWords);
     L.logits = o;
-    o = up(o + 4 * Mx * E);
+    o = up(o + 4 * Mx * ((E + 3) / 4 * 4));
     L.act = o;
     o = up(o + 4 * rows * ka);
     L.part = o;

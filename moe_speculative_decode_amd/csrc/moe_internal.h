@@ -51,7 +51,8 @@ struct Params {
     int act_stride;   // row stride (elements) of Workspace::act = max(I, Is)
     int route_only;   // 1: routing outputs only (moe_route)
     // LDS layout (bytes from the dynamic LDS base)
-    int lds_x, lds_sh, lds_act, lds_total;
+    int lds_x, lds_sh, lds_act, lds_dn, lds_total;
+    int lds_dn_bytes; // LDS window for this workgroup's routed down rows
     int sh_rows;      // shared-expert down rows prefetched per workgroup (ceil(H / grid))
     const void* x;
     const void* wr;
