@@ -11,10 +11,10 @@ namespace moe {
 constexpr int kMaxTokens = MOE_MAX_TOKENS;
 constexpr int kMaxExperts = MOE_MAX_EXPERTS;
 constexpr int kMaxTopK = MOE_MAX_TOPK;
-constexpr int kThreads = 256;  // threads per workgroup (4 wave64)
-constexpr int kWaves = kThreads / 64;
-constexpr int kCombineTile = 64;  // rows of y finished together by their last contributing workgroup
-constexpr int kMaxTiles = 64;     // ceil(4096 / kCombineTile)
+constexpr int kWaves = 8;                 // waves per workgroup; one workgroup per CU
+constexpr int kThreads = 64 * kWaves;     // 512
+constexpr int kMaxGrid = 1024;            // workgroups (CUs) the counter sets are sized for
+constexpr int kLdsBytes = 160 * 1024;     // LDS of one CU (gfx950)
 
 // Cross-workgroup counters.  Each counter owns a 256-byte line (atomics on one line serialise).
 // Two sets alternate between consecutive calls: call c counts in set c & 1 and clears set
@@ -22,10 +22,10 @@ constexpr int kMaxTiles = 64;     // ceil(4096 / kCombineTile)
 constexpr int kLineWords = 64;
 constexpr int kRouteSubs = 8;  // arrivals at the routing barrier are split over 8 sub-counters
 constexpr int kLineRouteTop = kRouteSubs;
-constexpr int kLineShared = kRouteSubs + 1;
-constexpr int kLineUnit0 = kRouteSubs + 2;            // kMaxExperts unit counters
-constexpr int kLineTile0 = kLineUnit0 + kMaxExperts;  // kMaxTiles tile counters
-constexpr int kSetLines = kLineTile0 + kMaxTiles;
+constexpr int kLineShared = kRouteSubs + 1;               // shared-expert SwiGLU rows finished
+constexpr int kLineUnit0 = kRouteSubs + 2;                // [kMaxExperts] routed SwiGLU rows finished
+constexpr int kLineOwner0 = kLineUnit0 + kMaxExperts;     // [kMaxGrid] partial rows landed per y slice
+constexpr int kSetLines = kLineOwner0 + kMaxGrid;
 constexpr int kSetWords = kSetLines * kLineWords;
 
 // workspace header words
@@ -40,7 +40,7 @@ constexpr uint32_t kStatusTimeout = 2u;
 struct Workspace {
     uint32_t* hdr;    // [kHdrBytes / 4]
     uint32_t* ctr;    // [2][kSetWords]
-    float* logits;    // [max_tokens][E]
+    float* logits;    // [max_tokens][E] (rows padded to 4)
     float* act;       // [max_tokens * (k + 1)][act_stride]  SwiGLU output per pair row
     float* part;      // [max_tokens * (k + 1)][H]           down projection per pair row
 };
@@ -50,10 +50,10 @@ struct Params {
     int act_fmt, w_fmt;
     int act_stride;   // row stride (elements) of Workspace::act = max(I, Is)
     int route_only;   // 1: routing outputs only (moe_route)
-    // LDS layout (bytes from the dynamic LDS base)
-    int lds_x, lds_sh, lds_act, lds_dn, lds_total;
-    int lds_dn_bytes; // LDS window for this workgroup's routed down rows
-    int sh_rows;      // shared-expert down rows prefetched per workgroup (ceil(H / grid))
+    // LDS layout, byte offsets from the dynamic LDS base (filled by launch_layer)
+    int lds_tab, lds_x, lds_cst, lds_sh, lds_ysh, lds_dn, lds_total;
+    int cst_bytes;    // staging area (routing scratch, SwiGLU results, down partials)
+    int dn_bytes;     // routed down-row window (also the shared-expert activation staging)
     const void* x;
     const void* wr;
     moe_weights_t w;
@@ -66,7 +66,7 @@ struct Params {
     Workspace ws;
 };
 
-// Enqueues one call.  Fills the LDS layout fields of a copy of `p`.
+// Enqueues one call.
 hipError_t launch_layer(const Params& p, int num_cus, hipStream_t stream);
 
 }  // namespace moe
