@@ -95,8 +95,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true", help="run a plain 1 GiB device copy (counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md, "
-              "'How the layer would shard')", file=sys.stderr)
+        print("bench.py measures one GPU only: the layer has no multi-GPU path (one GPU's share is "
+              "the whole layer here)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
