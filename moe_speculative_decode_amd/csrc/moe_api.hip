@@ -32,7 +32,7 @@ Layout layout(const moe_desc_t& d) {
     L.ctr = o;
     o = up(o + 2 * sizeof(uint32_t) * (size_t)moe::kSetWords);
     L.logits = o;
-    o = up(o + 4 * Mx * ((E + 3) / 4 * 4));
+    o = up(o + 8 * Mx * ((E + 3) / 4 * 4));
     L.act = o;
     o = up(o + 4 * rows * ka);
     L.part = o;
@@ -84,7 +84,7 @@ int fill_common(Params& p, const moe_desc_t* d, int32_t M, const void* x, const 
     Workspace& W = p.ws;
     W.hdr = (uint32_t*)(b + L.hdr);
     W.ctr = (uint32_t*)(b + L.ctr);
-    W.logits = (float*)(b + L.logits);
+    W.logits = (uint64_t*)(b + L.logits);
     W.act = (float*)(b + L.act);
     W.part = (float*)(b + L.part);
     return MOE_OK;

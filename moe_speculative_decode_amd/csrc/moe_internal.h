@@ -20,10 +20,8 @@ constexpr int kLdsBytes = 160 * 1024;     // LDS of one CU (gfx950)
 // Two sets alternate between consecutive calls: call c counts in set c & 1 and clears set
 // (c + 1) & 1, which the previous call used and the next call will use.
 constexpr int kLineWords = 64;
-constexpr int kRouteSubs = 8;  // arrivals at the routing barrier are split over 8 sub-counters
-constexpr int kLineRouteTop = kRouteSubs;
-constexpr int kLineShared = kRouteSubs + 1;               // shared-expert SwiGLU rows finished
-constexpr int kLineUnit0 = kRouteSubs + 2;                // [kMaxExperts] routed SwiGLU rows finished
+constexpr int kLineShared = 0;                            // shared-expert SwiGLU rows finished
+constexpr int kLineUnit0 = 1;                             // [kMaxExperts] routed SwiGLU rows finished
 constexpr int kLineOwner0 = kLineUnit0 + kMaxExperts;     // [kMaxGrid] partial rows landed per y slice
 constexpr int kSetLines = kLineOwner0 + kMaxGrid;
 constexpr int kSetWords = kSetLines * kLineWords;
@@ -40,7 +38,7 @@ constexpr uint32_t kStatusTimeout = 2u;
 struct Workspace {
     uint32_t* hdr;    // [kHdrBytes / 4]
     uint32_t* ctr;    // [2][kSetWords]
-    float* logits;    // [max_tokens][E] (rows padded to 4)
+    uint64_t* logits; // [max_tokens][E] (rows padded to 4): fp32 logit bits | (call index + 1) << 32
     float* act;       // [max_tokens * (k + 1)][act_stride]  SwiGLU output per pair row
     float* part;      // [max_tokens * (k + 1)][H]           down projection per pair row
 };
@@ -53,7 +51,8 @@ struct Params {
     // LDS layout, byte offsets from the dynamic LDS base (filled by launch_layer)
     int lds_tab, lds_x, lds_cst, lds_sh, lds_ysh, lds_dn, lds_total;
     int cst_bytes;    // staging area (routing scratch, SwiGLU results, down partials)
-    int dn_bytes;     // routed down-row window (also the shared-expert activation staging)
+    int dn_bytes;     // routed down-row window
+    int slice_mode;   // 1: every workgroup computes its y slice of every routed unit (small M*k)
     const void* x;
     const void* wr;
     moe_weights_t w;

@@ -40,6 +40,7 @@ namespace {
 #define LDS __attribute__((address_space(3)))
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -110,17 +111,10 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
 
-__device__ __forceinline__ uint64_t lanes_below() {
-    const int lane = threadIdx.x & 63;
-    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
-}
 
 // ------------------------------------------------------------------------------------------
 // number formats and weight geometry
 // ------------------------------------------------------------------------------------------
-
-__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -147,7 +141,7 @@ struct Geo<MOE_FMT_F32> {
 };
 template <>
 struct Geo<MOE_FMT_BF16> {
-    static constexpr int EPC = 8, LPR_G = 64, RL_G = 2, LPR_D = 32, RL_D = 2;
+    static constexpr int EPC = 8, LPR_G = 64, RL_G = 1, LPR_D = 32, RL_D = 2;
 };
 template <>
 struct Geo<MOE_FMT_MXFP4> {
@@ -178,6 +172,15 @@ __device__ __forceinline__ void settle(Chunk& r) {
         asm volatile("" : "+v"(r.q), "+v"(r.s));
     else
         asm volatile("" : "+v"(r.q));
+}
+
+// Chunks past the end of a row are loaded from the row's last chunk (so every load is in bounds
+// and the number of loads in flight is static) and zeroed here, once the load has landed, so the
+// compute loops need no per-chunk branch.
+template <int WF>
+__device__ __forceinline__ void settle_mask(Chunk& r, bool valid) {
+    settle<WF>(r);
+    if (!valid) r.q = u32x4{0u, 0u, 0u, 0u};
 }
 
 // chunk c of a weight row in global memory (streamed once: non-temporal)
@@ -235,44 +238,51 @@ __device__ __forceinline__ float dot_x(const Chunk& r, const LDS char* xrow, int
     return acc;
 }
 
-// Dot of weight chunk c with the matching elements of an fp32 row (LDS) -- the SwiGLU output
-// consumed by the down projection.
+// Dot of weight chunk c with the matching elements of a SwiGLU output row in LDS, fp32
+// accumulation.  For bf16 and MXFP4 weights the row is staged as two bfloat16 planes, hi = the
+// fp32 value with its low 16 bits cleared and lo = the rest rounded to bfloat16 (at `lo_off` bytes
+// from the row), so hi + lo carries ~16 significant bits and every product pair is one
+// v_dot2_f32_bf16; for binary32 weights it is staged as fp32.
 template <int WF>
-__device__ __forceinline__ float dot_a(const Chunk& r, const LDS float* arow, int c, float acc) {
+__device__ __forceinline__ float dot_a(const Chunk& r, const LDS char* arow, int lo_off, int c, float acc) {
     if constexpr (WF == MOE_FMT_BF16) {
-        const LDS f32x4* ap = (const LDS f32x4*)(arow + 8 * c);
-        const f32x4 a0 = ap[0], a1 = ap[1];
+        const u32x4 hi = *(const LDS u32x4*)(arow + 16 * c);
+        const u32x4 lo = *(const LDS u32x4*)(arow + lo_off + 16 * c);
         const uint32_t w0 = r.q[0], w1 = r.q[1], w2 = r.q[2], w3 = r.q[3];
-        acc = fmaf(bf16lo(w0), a0[0], acc);
-        acc = fmaf(bf16hi(w0), a0[1], acc);
-        acc = fmaf(bf16lo(w1), a0[2], acc);
-        acc = fmaf(bf16hi(w1), a0[3], acc);
-        acc = fmaf(bf16lo(w2), a1[0], acc);
-        acc = fmaf(bf16hi(w2), a1[1], acc);
-        acc = fmaf(bf16lo(w3), a1[2], acc);
-        acc = fmaf(bf16hi(w3), a1[3], acc);
+        const uint32_t h0 = hi[0], h1 = hi[1], h2 = hi[2], h3 = hi[3];
+        const uint32_t l0 = lo[0], l1 = lo[1], l2 = lo[2], l3 = lo[3];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(h0), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(h1), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(h2), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(h3), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(l0), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(l1), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(l2), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(l3), acc, false);
     } else if constexpr (WF == MOE_FMT_MXFP4) {
-        const LDS f32x4* ap = (const LDS f32x4*)(arow + 32 * c);
         const float sc = e8m0_to_f32(r.s);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
+            const u32x4 hi = *(const LDS u32x4*)(arow + 64 * c + 16 * d);
+            const u32x4 lo = *(const LDS u32x4*)(arow + lo_off + 64 * c + 16 * d);
             const uint32_t w = r.q[d];
-            const f32x4 a0 = ap[2 * d], a1 = ap[2 * d + 1];
-            const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
-            const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
-            const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
-            const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
-            acc = fmaf(p0[0], a0[0], acc);
-            acc = fmaf(p0[1], a0[1], acc);
-            acc = fmaf(p1[0], a0[2], acc);
-            acc = fmaf(p1[1], a0[3], acc);
-            acc = fmaf(p2[0], a1[0], acc);
-            acc = fmaf(p2[1], a1[1], acc);
-            acc = fmaf(p3[0], a1[2], acc);
-            acc = fmaf(p3[1], a1[3], acc);
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+            const uint32_t h0 = hi[0], h1 = hi[1], h2 = hi[2], h3 = hi[3];
+            const uint32_t l0 = lo[0], l1 = lo[1], l2 = lo[2], l3 = lo[3];
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(h0), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(h1), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(h2), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(h3), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(l0), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(l1), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(l2), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(l3), acc, false);
         }
     } else {
-        const f32x4 a = *(const LDS f32x4*)(arow + 4 * c);
+        const f32x4 a = *(const LDS f32x4*)(arow + 16 * c);
         const uint32_t w0 = r.q[0], w1 = r.q[1], w2 = r.q[2], w3 = r.q[3];
         acc = fmaf(__uint_as_float(w0), a[0], acc);
         acc = fmaf(__uint_as_float(w1), a[1], acc);
@@ -284,18 +294,19 @@ __device__ __forceinline__ float dot_a(const Chunk& r, const LDS float* arow, in
 
 __device__ __forceinline__ float silu_mul(float g, float v) { return g / (1.0f + __expf(-g)) * v; }
 
-// LDS tables of the batch dispatch, in words
-constexpr int kTabMask = 0;                                  // [kMaxExperts + 1] token bitmask per unit
-constexpr int kTabOff = kTabMask + kMaxExperts + 1;          // [kMaxExperts + 2] first pair row per unit
-constexpr int kTabExp = kTabOff + kMaxExperts + 2;           // [kMaxExperts + 1] expert id per unit
-constexpr int kTabPair = kTabExp + kMaxExperts + 1;          // [kMaxTokens * kMaxTopK] pair row of (m, j)
+// LDS tables of the batch dispatch, in words (at most kMaxUnits routed units plus the shared one)
+constexpr int kMaxUnits = kMaxTokens * kMaxTopK;
+constexpr int kTabMask = 0;                                  // [kMaxUnits + 1] token bitmask per unit
+constexpr int kTabOff = kTabMask + kMaxUnits + 1;            // [kMaxUnits + 2] first pair row per unit
+constexpr int kTabExp = kTabOff + kMaxUnits + 2;             // [kMaxUnits + 1] expert id per unit
+constexpr int kTabPair = kTabExp + kMaxUnits + 1;            // [kMaxTokens * kMaxTopK] pair row of (m, j)
 constexpr int kTabRowW = kTabPair + kMaxTokens * kMaxTopK;   // [kMaxTokens * (kMaxTopK + 1)] weight per row
 constexpr int kTabMisc = kTabRowW + kMaxTokens * (kMaxTopK + 1);  // [8] U, flags
 constexpr int kTabWords = (kTabMisc + 8 + 3) / 4 * 4;
 // routing scratch (token masks, expert row offsets, per-token ids / weights / logits), in the
 // staging area
 constexpr int kSelBytes = (2 * kMaxExperts + 3 * kMaxTokens * kMaxTopK) * 4;
-constexpr int kMaxPre = 4;  // routed down-row segments prefetched into LDS per workgroup
+constexpr int kMaxPre = 4;  // routed down-row segments prefetched into LDS per workgroup (unit-major)
 
 constexpr int kSpinLimit = 1 << 20;  // ~1 s of polling; normal waits are microseconds
 
@@ -355,6 +366,26 @@ __device__ __forceinline__ void wait_geq(const uint32_t* c, uint32_t target, uin
 }
 __device__ __forceinline__ uint32_t* line(uint32_t* set, int l) { return set + (int64_t)l * kLineWords; }
 
+// Every wave of the workgroup continues once the first U unit counters have reached `target` and
+// the shared expert's counter `sh_target` (bounded).
+__device__ __forceinline__ void wait_units(uint32_t* set, int U, uint32_t target, uint32_t sh_target, uint32_t* status) {
+    if (wave_id() == 0) {
+        const int lane = threadIdx.x & 63;
+        for (int it = 0;; ++it) {
+            bool ok = lane != 0 || ld_dev(line(set, kLineShared)) >= sh_target;
+            for (int u = lane; u < U; u += 64) ok = ok && ld_dev(line(set, kLineUnit0 + u)) >= target;
+            if (__ballot(!ok) == 0ull) break;
+            if (it >= kSpinLimit) {
+                if (lane == 0) atomicOr(status, kStatusTimeout);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    __syncthreads();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Starts an asynchronous copy of n bytes (a multiple of 16) from global memory to LDS with every
 // wave of the workgroup.  The data is usable after the issuing waves' next s_waitcnt vmcnt(0) and
 // a workgroup barrier.
@@ -372,8 +403,10 @@ __device__ __forceinline__ void async_to_lds(char* lds, const uint8_t* src, int 
 // fp32 logits rows are padded to whole 16-byte chunks
 __host__ __device__ __forceinline__ int logit_stride(int E) { return (E + 3) / 4 * 4; }
 
-// Stages `tcount` fp32 rows of K elements (global rows of `stride` floats from `src`) into LDS
-// [tcount][K] with 16-byte device-scope loads.
+// Stages `tcount` fp32 SwiGLU rows of K elements (global rows of `stride` floats from `src`) into
+// LDS rows of 4 * K bytes with 16-byte device-scope loads.  SPLIT: each LDS row holds the bfloat16
+// planes hi (K values) then lo (K values) that dot_a reads; otherwise the fp32 values.
+template <bool SPLIT>
 __device__ __forceinline__ void stage_rows(LDS float* dst, const float* src, int stride, int tcount, int K) {
     const __amdgpu_buffer_rsrc_t r = dev_rsrc(src, (uint32_t)(tcount * stride * 4));
     const int q4 = K / 4, n = tcount * q4;
@@ -390,7 +423,23 @@ __device__ __forceinline__ void stage_rows(LDS float* dst, const float* src, int
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int i = i0 + u * kThreads;
-            if (i < n) ((LDS f32x4*)dst)[i] = v[u];
+            if (i < n) {
+                if constexpr (SPLIT) {
+                    const int t = i / q4, c4 = i - t * q4;
+                    uint32_t h[4], l[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t bits = __float_as_uint(v[u][e]);
+                        h[e] = bits >> 16;
+                        l[e] = f32_to_bf16_rne(v[u][e] - __uint_as_float(bits & 0xFFFF0000u));
+                    }
+                    LDS char* row = (LDS char*)dst + (int64_t)t * K * 4;
+                    *(LDS u32x2*)(row + 8 * c4) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                    *(LDS u32x2*)(row + 2 * K + 8 * c4) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+                } else {
+                    ((LDS f32x4*)dst)[i] = v[u];
+                }
+            }
         }
     }
 }
@@ -399,18 +448,35 @@ __device__ __forceinline__ void stage_rows(LDS float* dst, const float* src, int
 // routing: top-k of one token with one wave, batch compaction with one workgroup
 // ------------------------------------------------------------------------------------------
 
-// Top-k of one token's E logits with one wave.  Lane l owns experts 8l .. 8l+7, read with two
-// 16-byte device-scope loads.  Order: larger logit first, equal logits -> lower expert id first.
-// Every round takes the wave-wide maximum of the lanes' current maxima; among equal maxima the
-// lowest lane holds the lowest id, and inside a lane the lowest index is kept, so ties resolve
-// to the lower id.  The winning lane drops that logit and recomputes its maximum.  Writes ids,
-// logits and softmax-over-the-k weights in order.  Every id written is in [0, E).
-__device__ __forceinline__ void wave_topk(const float* lrow, int E, int k, LDS int* out_id, LDS float* out_w,
-                                          LDS float* out_v) {
+// Top-k of one token's E logits with one wave, once every logit of this call has arrived (bounded
+// polling on the tags; on a timeout the status word is flagged and the selection proceeds).  Lane l
+// owns experts 8l .. 8l+7, read with four 16-byte device-scope loads.  Order: larger logit first,
+// equal logits -> lower expert id first.  Every round takes the wave-wide maximum of the lanes'
+// current maxima; among equal maxima the lowest lane holds the lowest id, and inside a lane the
+// lowest index is kept, so ties resolve to the lower id.  The winning lane drops that logit and
+// recomputes its maximum.  Writes ids, logits and softmax-over-the-k weights in order.  Every id
+// written is in [0, E).
+__device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, uint32_t tag, uint32_t* status,
+                                          LDS int* out_id, LDS float* out_w, LDS float* out_v) {
     const int lane = threadIdx.x & 63;
-    const __amdgpu_buffer_rsrc_t rs = dev_rsrc(lrow, (uint32_t)E * 4);  // loads past E return 0
-    const f32x4 a = ld_dev16(rs, (uint32_t)lane * 32), b = ld_dev16(rs, (uint32_t)lane * 32 + 16);
-    float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const __amdgpu_buffer_rsrc_t rs = dev_rsrc(lrow, (uint32_t)E * 8);  // loads past E return 0
+    float v[8];
+    for (int it = 0;; ++it) {
+        bool ok = true;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const u32x4 q = __builtin_bit_cast(u32x4, ld_dev16(rs, (uint32_t)lane * 64 + 16 * h));
+            v[2 * h] = __uint_as_float(q[0]);
+            v[2 * h + 1] = __uint_as_float(q[2]);
+            ok = ok && (8 * lane + 2 * h >= E || q[1] == tag) && (8 * lane + 2 * h + 1 >= E || q[3] == tag);
+        }
+        if (__ballot(!ok) == 0ull) break;
+        if (it >= kSpinLimit) {
+            if (lane == 0) atomicOr(status, kStatusTimeout);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         if (8 * lane + i >= E) v[i] = -INFINITY;
@@ -455,24 +521,23 @@ __device__ __forceinline__ void wave_topk(const float* lrow, int E, int k, LDS i
     }
 }
 
-// Exclusive prefix over the lanes of a non-negative count below 2^BITS, and the wave total.
-template <int BITS>
-__device__ __forceinline__ int wave_excl(int c, int* total) {
-    int pre = 0, tot = 0;
-    const uint64_t below = lanes_below();
-#pragma unroll
-    for (int bit = 0; bit < BITS; ++bit) {
-        const uint64_t b = __ballot((c >> bit) & 1);
-        pre += __popcll(b & below) << bit;
-        tot += __popcll(b) << bit;
-    }
-    *total = tot;
-    return pre;
+// Inclusive prefix sum over the 64 lanes (DPP: shifts inside each 16-lane row, then row
+// broadcasts).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += dpp_rows<0x142, 0xA>(0, v);                                 // row_bcast:15 into rows 1, 3
+    v += dpp_rows<0x143, 0xC>(0, v);                                 // row_bcast:31 into rows 2, 3
+    return v;
 }
 
-// Top-k of all M tokens and the batch compaction into this workgroup's LDS tables.  Workgroup 0
-// (`publish_outputs`) also writes the caller-visible routing outputs.  Returns U.
-__device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, LDS char* sel, bool publish_outputs) {
+// Top-k of all M tokens (each top-k wave waits for its token's logits of this call, tagged `tag`)
+// and the batch compaction into this workgroup's LDS tables.  Workgroup 0 (`publish_outputs`)
+// also writes the caller-visible routing outputs.  Returns U.
+__device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, LDS char* sel, bool publish_outputs,
+                                                 uint32_t tag) {
     const int E = p.E, M = p.M, k = p.k, NP = M * k;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const bool has_sh = p.Is > 0;
@@ -488,7 +553,8 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
     LDS float* s_roww = (LDS float*)(tab + kTabRowW);
 
     for (int m = wave; m < M; m += kWaves)
-        wave_topk(p.ws.logits + (int64_t)m * logit_stride(E), E, k, sid + m * k, sw + m * k, sv + m * k);
+        wave_topk(p.ws.logits + (int64_t)m * logit_stride(E), E, k, tag, p.ws.hdr + kHdrStatus, sid + m * k,
+                  sw + m * k, sv + m * k);
     __syncthreads();
     MOE_TRACE(13);
     if (wave == 0) {
@@ -505,9 +571,13 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
             npres += tm[i] ? 1 : 0;
             nrows += __popc(tm[i]);
         }
-        int U, tot_rows;
-        int u = wave_excl<4>(npres, &U);            // first unit index of this lane
-        int off = wave_excl<8>(nrows, &tot_rows);   // first pair row of this lane
+        // one scan of (units << 16 | pair rows): both stay below 2^16
+        const int packed = (npres << 16) | nrows;
+        const int incl = wave_incl_scan(packed);
+        const int excl = incl - packed;
+        const int U = __builtin_amdgcn_readlane(incl, 63) >> 16;
+        int u = excl >> 16;       // first unit index of this lane
+        int off = excl & 0xFFFF;  // first pair row of this lane
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int e = 8 * lane + i;
@@ -596,11 +666,14 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
 // streaming GEMV pieces
 // ------------------------------------------------------------------------------------------
 
-// Router rows [e0, e1): one wave per row, every token; fp32 logits by device-scope stores.  Each
-// wave's first row was loaded before the token rows landed in LDS (`first`).  The weight is in
+// Router rows [e0, e1): one wave per row, every token.  Each logit goes out as one 64-bit
+// device-scope store of its fp32 bits and `tag` (the call index + 1), so a reader that sees the tag
+// sees the value: no acknowledgement wait and no separate arrival flag.  Each wave's first row was
+// loaded before the token rows landed in LDS (`first`).  The weight is in
 // the activation format, so its geometry is the gate/up geometry of that format.
 template <int AF, int NJ>
-__device__ __forceinline__ void router_rows(const Params& p, const LDS char* xs, int e0, int e1, const Chunk (&first)[NJ]) {
+__device__ __forceinline__ void router_rows(const Params& p, const LDS char* xs, int e0, int e1, const Chunk (&first)[NJ],
+                                            uint32_t tag) {
     constexpr int XB = AF == MOE_FMT_F32 ? 4 : 2;
     const int H = p.H, E = p.E, M = p.M;
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -615,17 +688,16 @@ __device__ __forceinline__ void router_rows(const Params& p, const LDS char* xs,
                 ld_chunk<AF>(r[j], (const uint8_t*)p.wr + (int64_t)e * H * XB, nullptr, min(lane + 64 * j, nch - 1));
         }
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) settle<AF>(r[j]);
+        for (int j = 0; j < NJ; ++j) settle_mask<AF>(r[j], lane + 64 * j < nch);
         for (int m = 0; m < M; ++m) {
             const LDS char* xrow = xs + (int64_t)m * H * XB;
             float acc = 0.0f;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int c = lane + 64 * j;
-                if (c < nch) acc = dot_x<AF, AF>(r[j], xrow, c, acc);
-            }
+            for (int j = 0; j < NJ; ++j) acc = dot_x<AF, AF>(r[j], xrow, min(lane + 64 * j, nch - 1), acc);
             const float s = wave_sum_hi(acc);
-            if (lane == 63) st_dev(p.ws.logits + (int64_t)m * logit_stride(E) + e, s);
+            if (lane == 63)
+                __hip_atomic_store(p.ws.logits + (int64_t)m * logit_stride(E) + e,
+                                   ((uint64_t)tag << 32) | __float_as_uint(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -641,21 +713,22 @@ struct GUTask {
     int slot;           // staging row of the task's first row
 };
 
-// This wave's gate/up tasks q = qa + wave, qa + wave + kWaves, ... < qb.  info(q, task) describes
-// task q.  silu(g) * v of staged row s and the unit's i-th token goes to stage[s * M + i].  Each
+// This wave's gate/up tasks q = qa + wslot, qa + wslot + kWaves, ... < qb.  info(q, task) describes
+// task q.  out(s, i, v) receives silu(g) * v of the task's row s - t.slot and the unit's i-th token
+// (in the row's last lane).  Each
 // wave keeps the next task's loads in flight while it computes the current one; the prefetch is
 // unconditional (the last task re-reads itself) so the number of loads in flight is static and
 // the compiler waits for exactly the task it needs.
-template <int AF, int WF, int NJ, typename Info>
-__device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, LDS float* stage, int qa, int qb,
-                                           Info info) {
+template <int AF, int WF, int NJ, typename Info, typename Out>
+__device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, int qa, int qb, int wslot, Info info,
+                                           Out out) {
     constexpr int LPR = Geo<WF>::LPR_G, RL = Geo<WF>::RL_G;
     constexpr int XB = AF == MOE_FMT_F32 ? 4 : 2;
     const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
-    const int H = p.H, M = p.M;
+    const int H = p.H;
     const int nch = H / Geo<WF>::EPC;
     const int64_t rb = row_bytes<WF>(H), sb = H / 32;
-    int q = qa + wave_id();
+    int q = qa + wslot;
     if (q >= qb) return;
     Chunk ga[RL][NJ], ua[RL][NJ], gb[RL][NJ], ub[RL][NJ];
     GUTask ta, tb;
@@ -671,39 +744,46 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
             }
         }
     };
-    auto settle_all = [](Chunk(&g)[RL][NJ], Chunk(&u)[RL][NJ]) {
+    auto settle_all = [&](Chunk(&g)[RL][NJ], Chunk(&u)[RL][NJ]) {
 #pragma unroll
         for (int rl = 0; rl < RL; ++rl)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                settle<WF>(g[rl][j]);
-                settle<WF>(u[rl][j]);
+                settle_mask<WF>(g[rl][j], sl + LPR * j < nch);
+                settle_mask<WF>(u[rl][j], sl + LPR * j < nch);
             }
     };
-    auto compute = [&](const Chunk(&g)[RL][NJ], const Chunk(&u)[RL][NJ], const GUTask& t) {
+    auto compute = [&](Chunk(&g)[RL][NJ], Chunk(&u)[RL][NJ], const GUTask& t) {
         int i = 0;
         for (uint32_t m = t.mask; m; m &= m - 1u, ++i) {
             const int tok = __builtin_ctz(m);
+            if constexpr (WF == MOE_FMT_MXFP4) {
+                // keep the E2M1 decode inside the token loop: hoisted, the decoded rows of a task
+                // would need 160 registers
+#pragma unroll
+                for (int rl = 0; rl < RL; ++rl)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(g[rl][j].q), "+v"(u[rl][j].q));
+            }
             const LDS char* xrow = xs + (int64_t)tok * H * XB;
             float ag[RL], au[RL];
 #pragma unroll
             for (int rl = 0; rl < RL; ++rl) ag[rl] = au[rl] = 0.0f;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int c = sl + LPR * j;
-                if (c < nch) {
+                const int c = min(sl + LPR * j, nch - 1);
 #pragma unroll
-                    for (int rl = 0; rl < RL; ++rl) {
-                        ag[rl] = dot_x<AF, WF>(g[rl][j], xrow, c, ag[rl]);
-                        au[rl] = dot_x<AF, WF>(u[rl][j], xrow, c, au[rl]);
-                    }
+                for (int rl = 0; rl < RL; ++rl) {
+                    ag[rl] = dot_x<AF, WF>(g[rl][j], xrow, c, ag[rl]);
+                    au[rl] = dot_x<AF, WF>(u[rl][j], xrow, c, au[rl]);
                 }
+                if constexpr (WF == MOE_FMT_MXFP4) __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int rl = 0; rl < RL; ++rl) {
                 const float gs = group_sum<LPR>(ag[rl]);
                 const float us = group_sum<LPR>(au[rl]);
-                if (sl == LPR - 1) stage[(t.slot + gi * RL + rl) * M + i] = silu_mul(gs, us);
+                if (sl == LPR - 1) out(t.slot + gi * RL + rl, i, silu_mul(gs, us));
             }
         }
     };
@@ -727,18 +807,18 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
 
 // Down rows [0, nrows) of one unit (row 0 at wbase / sbase, in LDS when FROM_LDS) with K inputs,
 // for the unit's t tokens whose fp32 activations are at acts ([t][K], LDS).  Tasks of RT rows go
-// to the waves round robin.  `ready()` is called by every wave after its first loads are issued
+// to the waves round robin, task 0 to the wave whose slot is 0.  `ready()` is called by every wave after its first loads are issued
 // and before any compute (it may contain workgroup barriers).  out(row, i, value) receives each
 // result in the row's last lane.
 template <int WF, int NJD, bool FROM_LDS, typename Ready, typename Out>
 __device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* sbase, int K, int nrows,
-                                         const LDS float* acts, int t, Ready ready, Out out) {
+                                         const LDS float* acts, int t, int wslot, Ready ready, Out out) {
     constexpr int LPR = Geo<WF>::LPR_D, RL = Geo<WF>::RL_D, RT = rt_down<WF>();
     const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
     const int nch = K / Geo<WF>::EPC;
     const int64_t rb = row_bytes<WF>(K), sb = K / 32;
     const int ntask = (nrows + RT - 1) / RT;
-    int n = wave_id();
+    int n = wslot;
     Chunk wa[RL][NJD], wb[RL][NJD];
     auto load = [&](Chunk(&w)[RL][NJD], int task) {
 #pragma unroll
@@ -754,25 +834,24 @@ __device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* sb
             }
         }
     };
-    auto settle_all = [](Chunk(&w)[RL][NJD]) {
+    auto settle_all = [&](Chunk(&w)[RL][NJD]) {
 #pragma unroll
         for (int rl = 0; rl < RL; ++rl)
 #pragma unroll
-            for (int j = 0; j < NJD; ++j) settle<WF>(w[rl][j]);
+            for (int j = 0; j < NJD; ++j) settle_mask<WF>(w[rl][j], sl + LPR * j < nch);
     };
     auto compute = [&](const Chunk(&w)[RL][NJD], int task) {
         for (int i = 0; i < t; ++i) {
-            const LDS float* arow = acts + i * K;
+            const LDS char* arow = (const LDS char*)acts + (int64_t)i * K * 4;
             float acc[RL];
 #pragma unroll
             for (int rl = 0; rl < RL; ++rl) acc[rl] = 0.0f;
 #pragma unroll
             for (int j = 0; j < NJD; ++j) {
-                const int c = sl + LPR * j;
-                if (c < nch) {
+                const int c = min(sl + LPR * j, nch - 1);
 #pragma unroll
-                    for (int rl = 0; rl < RL; ++rl) acc[rl] = dot_a<WF>(w[rl][j], arow, c, acc[rl]);
-                }
+                for (int rl = 0; rl < RL; ++rl) acc[rl] = dot_a<WF>(w[rl][j], arow, 2 * K, c, acc[rl]);
+                if constexpr (WF == MOE_FMT_MXFP4) __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int rl = 0; rl < RL; ++rl) {
@@ -794,6 +873,97 @@ __device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* sb
         load(wa, min(n + kWaves, ntask - 1));
         settle_all(wb);
         compute(wb, n);
+        n += kWaves;
+        if (n >= ntask) break;
+    }
+}
+
+// One task of a flattened list of down rows: up to RT rows of one unit.
+struct DNTask {
+    const uint8_t* w;       // the task's first weight row (an LDS address when lds)
+    const uint8_t* s;       // MXFP4 scales of that row (global memory)
+    const LDS float* acts;  // the unit's SwiGLU rows [t][astride] in LDS
+    int lds;                // 1: the weights are in LDS
+    int nrows;              // valid rows of the task
+    int t;                  // tokens of the unit
+    int K;                  // inputs per row
+    int orow;               // index of the task's first row in the output slice
+    int prow;               // first pair row of the unit
+};
+
+// This wave's tasks n = wslot, wslot + kWaves, ... < ntask of a flattened down-row list described by
+// info(n, task); the source of each task (LDS or HBM) is its own.  Same pipelining as down_run:
+// the first task is loaded before ready(), and the next task's loads are in flight during the
+// current task's compute.  out(task, row, i, v) receives row `row` of the task for token i.
+template <int WF, int NJD, typename Info, typename Ready, typename Out>
+__device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Info info, Ready ready, Out out) {
+    constexpr int LPR = Geo<WF>::LPR_D, RL = Geo<WF>::RL_D;
+    const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
+    int n = wslot;
+    Chunk wa[RL][NJD], wb[RL][NJD];
+    DNTask ta, tb;
+    auto load = [&](Chunk(&w)[RL][NJD], const DNTask& t) {
+        const int nch = t.K / Geo<WF>::EPC;
+        const int64_t rb = row_bytes<WF>(t.K), sb = t.K / 32;
+#pragma unroll
+        for (int rl = 0; rl < RL; ++rl) {
+            const int64_t row = min(gi * RL + rl, t.nrows - 1);
+#pragma unroll
+            for (int j = 0; j < NJD; ++j) {
+                const int c = min(sl + LPR * j, nch - 1);
+                if (t.lds)
+                    ld_chunk_lds<WF>(w[rl][j], (const LDS uint8_t*)t.w + row * rb, t.s + row * sb, c);
+                else
+                    ld_chunk<WF>(w[rl][j], t.w + row * rb, t.s + row * sb, c);
+            }
+        }
+    };
+    auto settle_all = [&](Chunk(&w)[RL][NJD], const DNTask& t) {
+        const int nch = t.K / Geo<WF>::EPC;
+#pragma unroll
+        for (int rl = 0; rl < RL; ++rl)
+#pragma unroll
+            for (int j = 0; j < NJD; ++j) settle_mask<WF>(w[rl][j], sl + LPR * j < nch);
+    };
+    auto compute = [&](const Chunk(&w)[RL][NJD], const DNTask& t) {
+        const int nch = t.K / Geo<WF>::EPC;
+        for (int i = 0; i < t.t; ++i) {
+            const LDS char* arow = (const LDS char*)t.acts + (int64_t)i * astride * 4;
+            float acc[RL];
+#pragma unroll
+            for (int rl = 0; rl < RL; ++rl) acc[rl] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NJD; ++j) {
+                const int c = min(sl + LPR * j, nch - 1);
+#pragma unroll
+                for (int rl = 0; rl < RL; ++rl) acc[rl] = dot_a<WF>(w[rl][j], arow, 2 * astride, c, acc[rl]);
+                if constexpr (WF == MOE_FMT_MXFP4) __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int rl = 0; rl < RL; ++rl) {
+                const float v = group_sum<LPR>(acc[rl]);
+                const int row = gi * RL + rl;
+                if (sl == LPR - 1 && row < t.nrows) out(t, row, i, v);
+            }
+        }
+    };
+    if (n < ntask) {
+        info(n, ta);
+        load(wa, ta);
+    }
+    ready();
+    if (n >= ntask) return;
+    while (true) {
+        info(min(n + kWaves, ntask - 1), tb);
+        load(wb, tb);
+        settle_all(wa, ta);
+        compute(wa, ta);
+        n += kWaves;
+        if (n >= ntask) break;
+        info(min(n + kWaves, ntask - 1), ta);
+        load(wa, ta);
+        settle_all(wb, tb);
+        compute(wb, tb);
         n += kWaves;
         if (n >= ntask) break;
     }
@@ -825,26 +995,24 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     constexpr int RTD = rt_down<WF>();
     LDS char* lds = (LDS char*)smem;
     LDS int* tab = (LDS int*)(lds + p.lds_tab);
-    LDS char* xs = lds + p.lds_x;
+    LDS char* xs = lds + p.lds_x;        // token rows; after phase C the staged SwiGLU rows
     LDS float* cst = (LDS float*)(lds + p.lds_cst);
     LDS char* shw = lds + p.lds_sh;
     LDS float* ysh = (LDS float*)(lds + p.lds_ysh);
     LDS char* dnw = lds + p.lds_dn;
     __shared__ uint32_t s_call;
-    __shared__ int s_arrive;
     MOE_TRACE(0);
 
     // this workgroup's slice of y's columns (shared down rows, and the final combine)
     const int h0 = slice0(H, G, b), h1 = slice0(H, G, b + 1), nown = h1 - h0;
     const int64_t rbIs = row_bytes<WF>(Is);
+    const int64_t rbI = row_bytes<WF>(I);
 
     // ---- A: call index, token rows, router rows, shared-expert down rows of the slice ----
-    if (threadIdx.x == 0) {
-        s_call = ld_dev(p.ws.hdr + kHdrCall);
-        s_arrive = 0;
-    }
+    if (threadIdx.x == 0) s_call = ld_dev(p.ws.hdr + kHdrCall);
     async_to_lds((char*)xs, (const uint8_t*)p.x, M * H * XB);
     const int e0 = (int)((int64_t)E * b / G), e1 = (int)((int64_t)E * (b + 1) / G);
+    const int nrw = min(e1 - e0, kWaves);  // waves with router rows
     Chunk rfirst[NJ];
     {
         const int e = e0 + wave_id(), lane = threadIdx.x & 63, nch = H / Geo<AF>::EPC;
@@ -866,92 +1034,62 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         const int nl = kLineOwner0 + G;
         for (int l = threadIdx.x; l < nl; l += kThreads) line(nxt, l)[0] = 0u;
     }
-    // router rows; the last router wave of the workgroup arrives for it once its stores landed
-    {
-        const int nrw = min(e1 - e0, kWaves);  // waves with router rows
-        const int s = b % kRouteSubs;
-        const uint32_t members = G / kRouteSubs + (s < G % kRouteSubs ? 1 : 0);
-        if (wave_id() < nrw) {
-            router_rows<AF, NJ>(p, xs, e0, e1, rfirst);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_s_waitcnt(0);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if ((threadIdx.x & 63) == 0 && atomicAdd(&s_arrive, 1) + 1 == nrw) {
-                if (add_dev(line(set, s), 1u) + 1u == members) add_dev(line(set, kLineRouteTop), 1u);
-            }
-        } else if (nrw == 0 && threadIdx.x == 0) {
-            if (add_dev(line(set, s), 1u) + 1u == members) add_dev(line(set, kLineRouteTop), 1u);
-        }
-    }
+    // router rows (tagged logits: no arrival counter)
+    if (wave_id() < nrw) router_rows<AF, NJ>(p, xs, e0, e1, rfirst, call + 1u);
     MOE_TRACE(2);
     if (p.route_only && b != 0) return;
 
-    // ---- A': shared expert gate/up (needs no routing) ----
+    // ---- A': shared expert gate/up (needs no routing), on the waves without router rows first;
+    //      results go straight to the workspace and are counted after the routing barrier ----
+    int sh_rows = 0;
     if (has_sh && !p.route_only) {
         const int T = Is / RTG;
         const int qa = (int)((int64_t)T * b / G), qb = (int)((int64_t)T * (b + 1) / G);
-        if (qb > qa) {
-            const uint32_t all = (1u << M) - 1u;
-            gateup_run<AF, WF, NJ>(p, xs, cst, qa, qb, [&](int q, GUTask& t) {
+        sh_rows = (qb - qa) * RTG;
+        gateup_run<AF, WF, NJ>(
+            p, xs, qa, qb, kWaves - 1 - wave_id(),
+            [&](int q, GUTask& t) {
                 const int64_t r0 = (int64_t)q * RTG;
                 t.g = (const uint8_t*)p.w.sh_gate + r0 * row_bytes<WF>(H);
                 t.u = (const uint8_t*)p.w.sh_up + r0 * row_bytes<WF>(H);
                 t.gs = WF == MOE_FMT_MXFP4 ? p.w.sh_gate_s + r0 * (H / 32) : nullptr;
                 t.us = WF == MOE_FMT_MXFP4 ? p.w.sh_up_s + r0 * (H / 32) : nullptr;
-                t.mask = all;
-                t.slot = (q - qa) * RTG;
-            });
-            __syncthreads();
-            const int n = (qb - qa) * RTG * M;
-            for (int i = threadIdx.x; i < n; i += kThreads) {
-                const int r = qa * RTG + i / M, m = i - (i / M) * M;
-                st_dev(p.ws.act + (int64_t)(NP + m) * p.act_stride + r, cst[i]);
-            }
-            publish();
-            if (threadIdx.x == 0) add_dev(line(set, kLineShared), (uint32_t)((qb - qa) * RTG));
-        }
+                t.mask = (1u << M) - 1u;
+                t.slot = (int)r0;
+            },
+            [&](int r, int i, float v) { st_dev(p.ws.act + (int64_t)(NP + i) * p.act_stride + r, v); });
     }
     MOE_TRACE(3);
 
     // ---- B: routing barrier, top-k and compaction in every workgroup ----
-    wait_geq(line(set, kLineRouteTop), (uint32_t)min(G, kRouteSubs), p.ws.hdr + kHdrStatus);
-    MOE_TRACE(4);
-    const int U = route_and_compact(p, tab, (LDS char*)cst, b == 0);
+    const int U = route_and_compact(p, tab, (LDS char*)cst, b == 0, call + 1u);
     MOE_TRACE(5);
     if (b == 0 && threadIdx.x == 0)
         __hip_atomic_store(p.ws.hdr + kHdrCall, call + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (p.route_only) return;
+    if (sh_rows > 0) {  // the shared rows' stores completed long ago; this wait is short
+        publish();
+        if (threadIdx.x == 0) add_dev(line(set, kLineShared), (uint32_t)sh_rows);
+    }
     const LDS uint32_t* s_mask = (const LDS uint32_t*)tab + kTabMask;
     const LDS int* s_off = tab + kTabOff;
     const LDS int* s_exp = tab + kTabExp;
 
-    // ---- B': the shared expert's down rows of this slice (weights in LDS) -> ysh [M][nown] ----
-    if (has_sh && nown > 0) {
-        const int tb = min(M, p.dn_bytes / (Is * 4));  // tokens per pass through the staging area
-        for (int m0 = 0; m0 < M; m0 += tb) {
-            const int tc = min(tb, M - m0);
-            const uint8_t* dsb = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
-            down_run<WF, NJD, true>((const uint8_t*)shw, dsb, Is, nown, (const LDS float*)dnw, tc,
-                                    [&]() {
-                                        if (m0 == 0) wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
-                                        MOE_TRACE(6);
-                                        stage_rows((LDS float*)dnw, p.ws.act + (int64_t)(NP + m0) * p.act_stride,
-                                                   p.act_stride, tc, Is);
-                                        __syncthreads();
-                                    },
-                                    [&](int row, int i, float v) { ysh[(m0 + i) * nown + row] = v; });
-            __syncthreads();
-        }
-    }
-    MOE_TRACE(7);
-
-    // ---- start streaming this workgroup's routed down rows into LDS (as far as the window goes) ----
-    const int64_t rbI = row_bytes<WF>(I);
+    // ---- start streaming this workgroup's routed down rows into LDS (as far as the window goes):
+    //      slice mode: rows [h0, h1) of every unit; otherwise an equal share of all units' rows ----
     const int64_t dtotal = (int64_t)U * H;
     const int64_t d0 = dtotal * b / G, d1 = dtotal * (b + 1) / G;
     int pre_rows[kMaxPre];
     int pre_off[kMaxPre];
-    {
+    int nfit = 0;  // slice mode: units whose slice rows are in the window
+    if (p.slice_mode) {
+        if (nown > 0) {
+            nfit = min(U, (int)(p.dn_bytes / (nown * rbI)));
+            for (int u = 0; u < nfit; ++u)
+                async_to_lds((char*)(dnw + (int64_t)u * nown * rbI),
+                             (const uint8_t*)p.w.down + ((int64_t)s_exp[u] * H + h0) * rbI, (int)(nown * rbI));
+        }
+    } else {
         int64_t room = p.dn_bytes;
         int seg = 0;
         for (int64_t q = d0; q < d1 && seg < kMaxPre; ++seg) {
@@ -977,20 +1115,23 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         const int qa = (int)((int64_t)T * b / G), qb = (int)((int64_t)T * (b + 1) / G);
         if (qb > qa) {
             const int64_t rb = row_bytes<WF>(H);
-            gateup_run<AF, WF, NJ>(p, xs, cst, qa, qb, [&](int q, GUTask& t) {
-                const int u = q / TPU;
-                const int64_t e = uni(s_exp[u]);
-                const int64_t r0 = (int64_t)(q - u * TPU) * RTG;
-                t.g = (const uint8_t*)p.w.gate + (e * I + r0) * rb;
-                t.u = (const uint8_t*)p.w.up + (e * I + r0) * rb;
-                t.gs = WF == MOE_FMT_MXFP4 ? p.w.gate_s + (e * I + r0) * (H / 32) : nullptr;
-                t.us = WF == MOE_FMT_MXFP4 ? p.w.up_s + (e * I + r0) * (H / 32) : nullptr;
-                t.mask = uni(s_mask[u]);
-                t.slot = (q - qa) * RTG;
-            });
+            gateup_run<AF, WF, NJ>(
+                p, xs, qa, qb, wave_id(),
+                [&](int q, GUTask& t) {
+                    const int u = q / TPU;
+                    const int64_t e = uni(s_exp[u]);
+                    const int64_t r0 = (int64_t)(q - u * TPU) * RTG;
+                    t.g = (const uint8_t*)p.w.gate + (e * I + r0) * rb;
+                    t.u = (const uint8_t*)p.w.up + (e * I + r0) * rb;
+                    t.gs = WF == MOE_FMT_MXFP4 ? p.w.gate_s + (e * I + r0) * (H / 32) : nullptr;
+                    t.us = WF == MOE_FMT_MXFP4 ? p.w.up_s + (e * I + r0) * (H / 32) : nullptr;
+                    t.mask = uni(s_mask[u]);
+                    t.slot = (q - qa) * RTG;
+                },
+                [&](int r, int i, float v) { cst[r * M + i] = v; });
         }
         __syncthreads();
-        MOE_TRACE(8);
+        MOE_TRACE(6);
         // write the staged SwiGLU rows; then count them per unit once they have landed
         if (qb > qa) {
             const int n = (qb - qa) * RTG * M;
@@ -1005,7 +1146,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             }
         }
         publish();
-        MOE_TRACE(9);
+        MOE_TRACE(7);
         if (qb > qa && threadIdx.x == 0) {
             for (int u = qa / TPU; u <= (qb - 1) / TPU; ++u) {
                 const int a = max(qa, u * TPU), c = min(qb, (u + 1) * TPU);
@@ -1014,8 +1155,88 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         }
     }
 
+    // ---- B': the shared expert's down rows of this slice (weights in LDS) -> ysh [M][nown], while
+    //      the routed units' counters complete ----
+    if (has_sh && nown > 0 && !p.slice_mode) {
+        wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
+        stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
+        __syncthreads();
+        const uint8_t* dsb = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
+        down_run<WF, NJD, true>((const uint8_t*)shw, dsb, Is, nown, (const LDS float*)xs, M, wave_id(), []() {},
+                                [&](int row, int i, float v) { ysh[i * nown + row] = v; });
+        __syncthreads();
+    }
+    MOE_TRACE(8);
+
+    if (p.slice_mode) {
+        // ---- D (slice mode): rows [h0, h1) of every routed unit and of the shared expert, as one
+        //      flattened task list (units past the LDS window first, so their loads are in flight
+        //      during the waits); every pair row's SwiGLU output is staged once; partial outputs
+        //      stay in LDS: pst [NP + M][nown] ----
+        if (nown > 0) {
+            LDS float* pst = cst;
+            const int astride = p.act_stride;
+            const int nblk = (nown + RTD - 1) / RTD;
+            const int nun = U + (has_sh ? 1 : 0);
+            const int ng = U - nfit;  // routed units read from HBM in this phase
+            auto info = [&](int tt, DNTask& t) {
+                const int pidx = tt / nblk, bk = tt - pidx * nblk;
+                const int r0 = bk * RTD;
+                t.nrows = min(RTD, nown - r0);
+                t.orow = r0;
+                if (pidx < U) {
+                    const int u = pidx < ng ? nfit + pidx : pidx - ng;
+                    const int64_t e = uni(s_exp[u]);
+                    t.prow = uni(s_off[u]);
+                    t.t = __popc(uni(s_mask[u]));
+                    t.K = I;
+                    t.lds = pidx >= ng ? 1 : 0;
+                    t.w = t.lds ? (const uint8_t*)(dnw + ((int64_t)u * nown + r0) * rbI)
+                                : (const uint8_t*)p.w.down + (e * H + h0 + r0) * rbI;
+                    t.s = WF == MOE_FMT_MXFP4 ? p.w.down_s + (e * H + h0 + r0) * (I / 32) : nullptr;
+                } else {
+                    t.prow = NP;
+                    t.t = M;
+                    t.K = Is;
+                    t.lds = 1;
+                    t.w = (const uint8_t*)(shw + (int64_t)r0 * rbIs);
+                    t.s = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)(h0 + r0) * (Is / 32) : nullptr;
+                }
+                t.acts = (const LDS float*)xs + (int64_t)t.prow * astride;
+            };
+            auto ready = [&]() {
+                wait_units(set, U, (uint32_t)I, has_sh ? (uint32_t)Is : 0u, p.ws.hdr + kHdrStatus);
+                MOE_TRACE(9);
+                stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act, astride, NP + (has_sh ? M : 0), astride);
+                __syncthreads();
+                MOE_TRACE(10);
+            };
+            down_flat<WF, NJD>(nun * nblk, astride, wave_id(), info, ready,
+                               [&](const DNTask& t, int row, int i, float v) { pst[(t.prow + i) * nown + t.orow + row] = v; });
+            __syncthreads();
+            MOE_TRACE(11);
+            // ---- E (slice mode): combine from LDS ----
+            const LDS int* s_pair = tab + kTabPair;
+            const LDS float* s_roww = (const LDS float*)(tab + kTabRowW);
+            for (int i = threadIdx.x; i < M * nown; i += kThreads) {
+                const int m = i / nown, hh = i - m * nown, h = h0 + hh;
+                float acc = 0.0f;
+                for (int j = 0; j < k; ++j) {
+                    const int row = s_pair[m * k + j];
+                    acc = fmaf(s_roww[row], pst[row * nown + hh], acc);
+                }
+                if (has_sh) acc += pst[(NP + m) * nown + hh];
+                if constexpr (AF == MOE_FMT_F32)
+                    ((float*)p.y)[(int64_t)m * H + h] = acc;
+                else
+                    ((uint16_t*)p.y)[(int64_t)m * H + h] = f32_to_bf16_rne(acc);
+            }
+        }
+        MOE_TRACE(17);
+        return;
+    }
+
     // ---- D: routed down rows, unit by unit; partial outputs staged in LDS, written per pass ----
-    MOE_TRACE(10);
     {
         LDS float* pst = cst;
         const int cap = p.cst_bytes / 4;
@@ -1038,28 +1259,28 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 auto ready = [&]() {
                     if (!staged) {
                         wait_geq(line(set, kLineUnit0 + u), (uint32_t)I, p.ws.hdr + kHdrStatus);
-                        if (first) MOE_TRACE(11);
-                        stage_rows((LDS float*)xs, p.ws.act + (int64_t)row0 * p.act_stride, p.act_stride, t, I);
+                        if (first) MOE_TRACE(9);
+                        stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)row0 * p.act_stride, p.act_stride, t, I);
                         __syncthreads();
-                        if (first) MOE_TRACE(12);
+                        if (first) MOE_TRACE(10);
                         staged = true;
                         first = false;
                     }
                 };
-                auto out = [&](int row, int i, float v) { pst[(row + 0) * t + i] = v; };
+                auto out = [&](int row, int i, float v) { pst[row * t + i] = v; };
                 // part from the LDS window: rows [pa, min(pb, ha + npre))
                 const int la = pa, lb = min(pb, ha + npre);
                 if (lb > la) {
                     const uint8_t* dsb = WF == MOE_FMT_MXFP4 ? p.w.down_s + (e * H + la) * (I / 32) : nullptr;
                     down_run<WF, NJD, true>((const uint8_t*)(dnw + pre_off[seg] + (int64_t)(la - ha) * rbI), dsb, I,
-                                            lb - la, (const LDS float*)xs, t, ready,
+                                            lb - la, (const LDS float*)xs, t, wave_id(), ready,
                                             [&](int row, int i, float v) { out(row + la - pa, i, v); });
                 }
                 const int ga = max(pa, ha + npre), gb = pb;
                 if (gb > ga) {
                     const uint8_t* dsb = WF == MOE_FMT_MXFP4 ? p.w.down_s + (e * H + ga) * (I / 32) : nullptr;
                     down_run<WF, NJD, false>((const uint8_t*)p.w.down + (e * H + ga) * rbI, dsb, I, gb - ga,
-                                             (const LDS float*)xs, t, ready,
+                                             (const LDS float*)xs, t, wave_id(), ready,
                                              [&](int row, int i, float v) { out(row + ga - pa, i, v); });
                 }
                 __syncthreads();
@@ -1073,7 +1294,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         }
     }
     publish();
-    MOE_TRACE(15);
+    MOE_TRACE(11);
     // count the landed partial rows for the slices they fall in
     if (threadIdx.x == 0) {
         for (int64_t q = d0; q < d1;) {
@@ -1090,8 +1311,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
 
     // ---- E: combine this workgroup's slice of y ----
     if (nown > 0) {
-        if (U > 0) wait_geq(line(set, kLineOwner0 + b), (uint32_t)(U * nown), p.ws.hdr + kHdrStatus);
-        MOE_TRACE(16);
+        wait_geq(line(set, kLineOwner0 + b), (uint32_t)(U * nown), p.ws.hdr + kHdrStatus);
+        MOE_TRACE(12);
         const LDS int* s_pair = tab + kTabPair;
         const LDS float* s_roww = (const LDS float*)(tab + kTabRowW);
         for (int i = threadIdx.x; i < M * nown; i += kThreads) {
@@ -1123,31 +1344,30 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     constexpr int XB = AF == MOE_FMT_F32 ? 4 : 2;
     const int G = std::min(num_cus, kMaxGrid);
     const int M = p.M, H = p.H;
+    const int64_t NP = (int64_t)p.k * M;
     const int ka = std::max(p.I, p.Is);
     const int nown = (H + G - 1) / G;
-    // staging area: routing scratch; shared / routed SwiGLU results of one workgroup's tasks;
-    // down partials (any size works, larger means fewer passes)
+    // slice mode (each workgroup finishes its own y columns of every unit) while M * k is small:
+    // then every workgroup stages all pair rows' SwiGLU outputs; otherwise unit-major down rows
+    p.slice_mode = NP <= 16 ? 1 : 0;
+    // staging area: routing scratch; routed SwiGLU results of one workgroup's tasks; down partials
+    // (slice mode: [NP][nown]; unit-major: any size, larger means fewer passes)
     const int64_t tpu = p.I / rt_gate<WF>();
-    const int64_t units = std::min<int64_t>((int64_t)p.k * M, p.E);
+    const int64_t units = std::min<int64_t>(NP, p.E);
     const int64_t c_tasks = (units * tpu + G - 1) / G + 1;
-    const int64_t s_tasks = p.Is > 0 ? (p.Is / rt_gate<WF>() + G - 1) / G + 1 : 0;
-    int64_t cst = std::max<int64_t>(kSelBytes, std::max(c_tasks, s_tasks) * rt_gate<WF>() * M * 4);
-    cst = std::max<int64_t>(cst, 16 * 1024);
+    int64_t cst = std::max<int64_t>(kSelBytes, c_tasks * rt_gate<WF>() * M * 4);
+    cst = std::max<int64_t>(cst, p.slice_mode ? (NP + M) * nown * 4 : 16 * 1024);
+    int64_t xb = std::max<int64_t>((int64_t)M * H * XB, (int64_t)M * ka * 4);
+    if (p.slice_mode) xb = std::max<int64_t>(xb, (NP + M) * ka * 4);
     p.lds_tab = 0;
     p.lds_x = round16(kTabWords * 4);
-    p.lds_cst = p.lds_x + round16(std::max<int64_t>((int64_t)M * H * XB, (int64_t)M * ka * 4));
+    p.lds_cst = p.lds_x + round16(xb);
     p.cst_bytes = round16(cst);
     p.lds_sh = p.lds_cst + p.cst_bytes;
     p.lds_ysh = p.lds_sh + round16(p.Is > 0 ? nown * row_bytes<WF>(p.Is) : 0);
     p.lds_dn = p.lds_ysh + round16((int64_t)M * nown * 4);
-    const int budget = kLdsBytes - 1024;  // room for the static LDS variables
-    if (p.route_only) {
-        p.dn_bytes = 0;
-    } else {
-        p.dn_bytes = (budget - p.lds_dn) / 16 * 16;
-        if (p.Is > 0 && p.dn_bytes < p.Is * 4) return hipErrorInvalidConfiguration;  // one shared activation row
-        if (p.dn_bytes < 0) return hipErrorInvalidConfiguration;
-    }
+    const int budget = kLdsBytes - 256;  // room for the static LDS variables
+    p.dn_bytes = p.route_only ? 0 : std::max(0, (budget - p.lds_dn) / 16 * 16);
     p.lds_total = p.lds_dn + p.dn_bytes;
     if (p.lds_total > budget) return hipErrorInvalidConfiguration;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_total);
