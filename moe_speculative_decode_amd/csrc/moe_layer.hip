@@ -200,18 +200,23 @@ __device__ __forceinline__ void ld_chunk_lds(Chunk& r, const LDS uint8_t* row, c
 // lvalue directly (v.y) makes clang read the vector's first element instead.
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 
+// Independent partial sums of one dot product: a chain of dependent v_dot2 would run at the
+// instruction's latency, four interleaved chains at its issue rate.  Summed in a fixed order.
+constexpr int kAcc = 4;
+__device__ __forceinline__ float acc_sum(const float (&a)[kAcc]) { return (a[0] + a[1]) + (a[2] + a[3]); }
+
 // Dot of weight chunk c with the matching elements of a token row x (LDS; bf16, or binary32 for
-// the binary32 layer), fp32 accumulation.
+// the binary32 layer), fp32 accumulation into the partial sums acc.
 template <int AF, int WF>
-__device__ __forceinline__ float dot_x(const Chunk& r, const LDS char* xrow, int c, float acc) {
+__device__ __forceinline__ void dot_x(const Chunk& r, const LDS char* xrow, int c, float (&acc)[kAcc]) {
     if constexpr (WF == MOE_FMT_BF16) {
         const u32x4 x = *(const LDS u32x4*)(xrow + 16 * c);
         const uint32_t w0 = r.q[0], w1 = r.q[1], w2 = r.q[2], w3 = r.q[3];
         const uint32_t x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(x0), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(x1), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(x2), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(x3), acc, false);
+        acc[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(x0), acc[0], false);
+        acc[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(x1), acc[1], false);
+        acc[2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(x2), acc[2], false);
+        acc[3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(x3), acc[3], false);
     } else if constexpr (WF == MOE_FMT_MXFP4) {
         // dword d of the codes holds elements 8d .. 8d+7; byte s of it elements 8d+2s (low
         // nibble) and 8d+2s+1, which is dword s of the d-th 16 bytes of x
@@ -222,20 +227,19 @@ __device__ __forceinline__ float dot_x(const Chunk& r, const LDS char* xrow, int
             const u32x4 x = xp[d];
             const uint32_t w = r.q[d];
             const uint32_t x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0), as_bf16x2(x0), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1), as_bf16x2(x1), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2), as_bf16x2(x2), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3), as_bf16x2(x3), acc, false);
+            acc[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0), as_bf16x2(x0), acc[0], false);
+            acc[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1), as_bf16x2(x1), acc[1], false);
+            acc[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2), as_bf16x2(x2), acc[2], false);
+            acc[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3), as_bf16x2(x3), acc[3], false);
         }
     } else {
         const f32x4 x = *(const LDS f32x4*)(xrow + 16 * c);
         const uint32_t w0 = r.q[0], w1 = r.q[1], w2 = r.q[2], w3 = r.q[3];
-        acc = fmaf(__uint_as_float(w0), x[0], acc);
-        acc = fmaf(__uint_as_float(w1), x[1], acc);
-        acc = fmaf(__uint_as_float(w2), x[2], acc);
-        acc = fmaf(__uint_as_float(w3), x[3], acc);
+        acc[0] = fmaf(__uint_as_float(w0), x[0], acc[0]);
+        acc[1] = fmaf(__uint_as_float(w1), x[1], acc[1]);
+        acc[2] = fmaf(__uint_as_float(w2), x[2], acc[2]);
+        acc[3] = fmaf(__uint_as_float(w3), x[3], acc[3]);
     }
-    return acc;
 }
 
 // Dot of weight chunk c with the matching elements of a SwiGLU output row in LDS, fp32
@@ -244,21 +248,21 @@ __device__ __forceinline__ float dot_x(const Chunk& r, const LDS char* xrow, int
 // from the row), so hi + lo carries ~16 significant bits and every product pair is one
 // v_dot2_f32_bf16; for binary32 weights it is staged as fp32.
 template <int WF>
-__device__ __forceinline__ float dot_a(const Chunk& r, const LDS char* arow, int lo_off, int c, float acc) {
+__device__ __forceinline__ void dot_a(const Chunk& r, const LDS char* arow, int lo_off, int c, float (&acc)[kAcc]) {
     if constexpr (WF == MOE_FMT_BF16) {
         const u32x4 hi = *(const LDS u32x4*)(arow + 16 * c);
         const u32x4 lo = *(const LDS u32x4*)(arow + lo_off + 16 * c);
         const uint32_t w0 = r.q[0], w1 = r.q[1], w2 = r.q[2], w3 = r.q[3];
         const uint32_t h0 = hi[0], h1 = hi[1], h2 = hi[2], h3 = hi[3];
         const uint32_t l0 = lo[0], l1 = lo[1], l2 = lo[2], l3 = lo[3];
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(h0), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(h1), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(h2), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(h3), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(l0), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(l1), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(l2), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(l3), acc, false);
+        acc[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(h0), acc[0], false);
+        acc[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(h1), acc[1], false);
+        acc[2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(h2), acc[2], false);
+        acc[3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(h3), acc[3], false);
+        acc[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(l0), acc[0], false);
+        acc[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(l1), acc[1], false);
+        acc[2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(l2), acc[2], false);
+        acc[3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(l3), acc[3], false);
     } else if constexpr (WF == MOE_FMT_MXFP4) {
         const float sc = e8m0_to_f32(r.s);
 #pragma unroll
@@ -272,24 +276,23 @@ __device__ __forceinline__ float dot_a(const Chunk& r, const LDS char* arow, int
             const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
             const uint32_t h0 = hi[0], h1 = hi[1], h2 = hi[2], h3 = hi[3];
             const uint32_t l0 = lo[0], l1 = lo[1], l2 = lo[2], l3 = lo[3];
-            acc = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(h0), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(h1), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(h2), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(h3), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(l0), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(l1), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(l2), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(l3), acc, false);
+            acc[0] = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(h0), acc[0], false);
+            acc[1] = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(h1), acc[1], false);
+            acc[2] = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(h2), acc[2], false);
+            acc[3] = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(h3), acc[3], false);
+            acc[0] = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(l0), acc[0], false);
+            acc[1] = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(l1), acc[1], false);
+            acc[2] = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(l2), acc[2], false);
+            acc[3] = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(l3), acc[3], false);
         }
     } else {
         const f32x4 a = *(const LDS f32x4*)(arow + 16 * c);
         const uint32_t w0 = r.q[0], w1 = r.q[1], w2 = r.q[2], w3 = r.q[3];
-        acc = fmaf(__uint_as_float(w0), a[0], acc);
-        acc = fmaf(__uint_as_float(w1), a[1], acc);
-        acc = fmaf(__uint_as_float(w2), a[2], acc);
-        acc = fmaf(__uint_as_float(w3), a[3], acc);
+        acc[0] = fmaf(__uint_as_float(w0), a[0], acc[0]);
+        acc[1] = fmaf(__uint_as_float(w1), a[1], acc[1]);
+        acc[2] = fmaf(__uint_as_float(w2), a[2], acc[2]);
+        acc[3] = fmaf(__uint_as_float(w3), a[3], acc[3]);
     }
-    return acc;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float v) { return g / (1.0f + __expf(-g)) * v; }
@@ -308,17 +311,40 @@ constexpr int kTabWords = (kTabMisc + 8 + 3) / 4 * 4;
 constexpr int kSelBytes = (2 * kMaxExperts + 3 * kMaxTokens * kMaxTopK) * 4;
 constexpr int kMaxPre = 4;  // routed down-row segments prefetched into LDS per workgroup (unit-major)
 
+constexpr int kCostBase = 8;  // cost of one weight row's bytes in cost_split units
 constexpr int kSpinLimit = 1 << 20;  // ~1 s of polling; normal waits are microseconds
 
 // Phase timestamps for performance analysis, compiled out unless MOE_PHASE_TRACE is defined.
+// Thread 0 keeps them in LDS and writes them out when the workgroup finishes, so recording a
+// timestamp never waits on the vector-memory counter.
 #ifdef MOE_PHASE_TRACE
 __device__ uint64_t* g_moe_trace;
-#define MOE_TRACE(slot)                                                                             \
-    do {                                                                                            \
-        if (threadIdx.x == 0 && g_moe_trace) g_moe_trace[blockIdx.x * 32 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+__shared__ uint64_t s_trace[32];
+#define MOE_TRACE_INIT                                  \
+    do {                                                \
+        if (threadIdx.x < 32) s_trace[threadIdx.x] = 0; \
+    } while (0)
+#define MOE_TRACE(slot)                                                           \
+    do {                                                                          \
+        if (threadIdx.x == 0) s_trace[(slot)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+#define MOE_TRACE_FLUSH                                                                \
+    do {                                                                               \
+        if (threadIdx.x == 0) {                                                        \
+            s_trace[31] = __builtin_amdgcn_s_memrealtime();                            \
+            uint64_t* t = g_moe_trace;                                                 \
+            if (t)                                                                     \
+                for (int i_ = 0; i_ < 32; ++i_) t[blockIdx.x * 32 + i_] = s_trace[i_]; \
+        }                                                                              \
     } while (0)
 #else
+#define MOE_TRACE_INIT \
+    do {               \
+    } while (0)
 #define MOE_TRACE(slot) \
+    do {                \
+    } while (0)
+#define MOE_TRACE_FLUSH \
     do {                \
     } while (0)
 #endif
@@ -449,7 +475,9 @@ __device__ __forceinline__ void stage_rows(LDS float* dst, const float* src, int
 // ------------------------------------------------------------------------------------------
 
 // Top-k of one token's E logits with one wave, once every logit of this call has arrived (bounded
-// polling on the tags; on a timeout the status word is flagged and the selection proceeds).  Lane l
+// polling on the tags: one read in flight, since M waves of every workgroup poll at once and the
+// polls share the saturated memory path; on a timeout the status word is flagged and the selection
+// proceeds).  Lane l
 // owns experts 8l .. 8l+7, read with four 16-byte device-scope loads.  Order: larger logit first,
 // equal logits -> lower expert id first.  Every round takes the wave-wide maximum of the lanes'
 // current maxima; among equal maxima the lowest lane holds the lowest id, and inside a lane the
@@ -476,6 +504,7 @@ __device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, ui
             break;
         }
         __builtin_amdgcn_s_sleep(1);
+        asm volatile("" ::: "memory");  // the next iteration reads memory again
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -691,10 +720,10 @@ __device__ __forceinline__ void router_rows(const Params& p, const LDS char* xs,
         for (int j = 0; j < NJ; ++j) settle_mask<AF>(r[j], lane + 64 * j < nch);
         for (int m = 0; m < M; ++m) {
             const LDS char* xrow = xs + (int64_t)m * H * XB;
-            float acc = 0.0f;
+            float acc[kAcc] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) acc = dot_x<AF, AF>(r[j], xrow, min(lane + 64 * j, nch - 1), acc);
-            const float s = wave_sum_hi(acc);
+            for (int j = 0; j < NJ; ++j) dot_x<AF, AF>(r[j], xrow, min(lane + 64 * j, nch - 1), acc);
+            const float s = wave_sum_hi(acc_sum(acc));
             if (lane == 63)
                 __hip_atomic_store(p.ws.logits + (int64_t)m * logit_stride(E) + e,
                                    ((uint64_t)tag << 32) | __float_as_uint(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -766,23 +795,25 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
                     for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(g[rl][j].q), "+v"(u[rl][j].q));
             }
             const LDS char* xrow = xs + (int64_t)tok * H * XB;
-            float ag[RL], au[RL];
+            float ag[RL][kAcc], au[RL][kAcc];
 #pragma unroll
-            for (int rl = 0; rl < RL; ++rl) ag[rl] = au[rl] = 0.0f;
+            for (int rl = 0; rl < RL; ++rl)
+#pragma unroll
+                for (int q = 0; q < kAcc; ++q) ag[rl][q] = au[rl][q] = 0.0f;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int c = min(sl + LPR * j, nch - 1);
 #pragma unroll
                 for (int rl = 0; rl < RL; ++rl) {
-                    ag[rl] = dot_x<AF, WF>(g[rl][j], xrow, c, ag[rl]);
-                    au[rl] = dot_x<AF, WF>(u[rl][j], xrow, c, au[rl]);
+                    dot_x<AF, WF>(g[rl][j], xrow, c, ag[rl]);
+                    dot_x<AF, WF>(u[rl][j], xrow, c, au[rl]);
                 }
                 if constexpr (WF == MOE_FMT_MXFP4) __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int rl = 0; rl < RL; ++rl) {
-                const float gs = group_sum<LPR>(ag[rl]);
-                const float us = group_sum<LPR>(au[rl]);
+                const float gs = group_sum<LPR>(acc_sum(ag[rl]));
+                const float us = group_sum<LPR>(acc_sum(au[rl]));
                 if (sl == LPR - 1) out(t.slot + gi * RL + rl, i, silu_mul(gs, us));
             }
         }
@@ -843,19 +874,21 @@ __device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* sb
     auto compute = [&](const Chunk(&w)[RL][NJD], int task) {
         for (int i = 0; i < t; ++i) {
             const LDS char* arow = (const LDS char*)acts + (int64_t)i * K * 4;
-            float acc[RL];
+            float acc[RL][kAcc];
 #pragma unroll
-            for (int rl = 0; rl < RL; ++rl) acc[rl] = 0.0f;
+            for (int rl = 0; rl < RL; ++rl)
+#pragma unroll
+                for (int q = 0; q < kAcc; ++q) acc[rl][q] = 0.0f;
 #pragma unroll
             for (int j = 0; j < NJD; ++j) {
                 const int c = min(sl + LPR * j, nch - 1);
 #pragma unroll
-                for (int rl = 0; rl < RL; ++rl) acc[rl] = dot_a<WF>(w[rl][j], arow, 2 * K, c, acc[rl]);
+                for (int rl = 0; rl < RL; ++rl) dot_a<WF>(w[rl][j], arow, 2 * K, c, acc[rl]);
                 if constexpr (WF == MOE_FMT_MXFP4) __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int rl = 0; rl < RL; ++rl) {
-                const float s = group_sum<LPR>(acc[rl]);
+                const float s = group_sum<LPR>(acc_sum(acc[rl]));
                 const int row = task * RT + gi * RL + rl;
                 if (sl == LPR - 1 && row < nrows) out(row, i, s);
             }
@@ -929,19 +962,21 @@ __device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Inf
         const int nch = t.K / Geo<WF>::EPC;
         for (int i = 0; i < t.t; ++i) {
             const LDS char* arow = (const LDS char*)t.acts + (int64_t)i * astride * 4;
-            float acc[RL];
+            float acc[RL][kAcc];
 #pragma unroll
-            for (int rl = 0; rl < RL; ++rl) acc[rl] = 0.0f;
+            for (int rl = 0; rl < RL; ++rl)
+#pragma unroll
+                for (int q = 0; q < kAcc; ++q) acc[rl][q] = 0.0f;
 #pragma unroll
             for (int j = 0; j < NJD; ++j) {
                 const int c = min(sl + LPR * j, nch - 1);
 #pragma unroll
-                for (int rl = 0; rl < RL; ++rl) acc[rl] = dot_a<WF>(w[rl][j], arow, 2 * astride, c, acc[rl]);
+                for (int rl = 0; rl < RL; ++rl) dot_a<WF>(w[rl][j], arow, 2 * astride, c, acc[rl]);
                 if constexpr (WF == MOE_FMT_MXFP4) __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int rl = 0; rl < RL; ++rl) {
-                const float v = group_sum<LPR>(acc[rl]);
+                const float v = group_sum<LPR>(acc_sum(acc[rl]));
                 const int row = gi * RL + rl;
                 if (sl == LPR - 1 && row < t.nrows) out(t, row, i, v);
             }
@@ -967,6 +1002,30 @@ __device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Inf
         n += kWaves;
         if (n >= ntask) break;
     }
+}
+
+// Splits a list of U units of n items each (rows or tasks; item i of unit u has flat index
+// u * n + i) over G workgroups by cost, an item of unit u costing c0 + c1 * t_u where t_u is the
+// unit's token count: every workgroup gets an equal share of the total cost, so units that many
+// tokens chose (more compute per weight byte) are spread over more workgroups.  Returns the flat
+// range [lo, hi) of workgroup b; consecutive workgroups' ranges tile [0, U * n).  Every lane
+// computes the same scalar result.
+__device__ __forceinline__ void cost_split(const LDS uint32_t* s_mask, int U, int n, int c0, int c1, int G, int b,
+                                           int64_t* lo, int64_t* hi) {
+    int64_t total = 0;
+    for (int u = 0; u < U; ++u) total += (int64_t)n * (c0 + c1 * __popc(s_mask[u]));
+    auto at = [&](int64_t x) -> int64_t {  // flat index of the first item whose cost interval ends after x
+        if (x >= total) return (int64_t)U * n;
+        int64_t acc = 0;
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + c1 * __popc(s_mask[u]);
+            if (acc + n * c > x) return (int64_t)u * n + (x - acc + c - 1) / c;
+            acc += n * c;
+        }
+        return (int64_t)U * n;
+    };
+    *lo = at(total * b / G);
+    *hi = at(total * (b + 1) / G);
 }
 
 // First row of workgroup o's slice of y's columns: [slice0(o), slice0(o + 1)).
@@ -1001,6 +1060,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     LDS float* ysh = (LDS float*)(lds + p.lds_ysh);
     LDS char* dnw = lds + p.lds_dn;
     __shared__ uint32_t s_call;
+    MOE_TRACE_INIT;
     MOE_TRACE(0);
 
     // this workgroup's slice of y's columns (shared down rows, and the final combine)
@@ -1037,7 +1097,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     // router rows (tagged logits: no arrival counter)
     if (wave_id() < nrw) router_rows<AF, NJ>(p, xs, e0, e1, rfirst, call + 1u);
     MOE_TRACE(2);
-    if (p.route_only && b != 0) return;
+    if (p.route_only && b != 0) {
+        MOE_TRACE_FLUSH;
+        return;
+    }
 
     // ---- A': shared expert gate/up (needs no routing), on the waves without router rows first;
     //      results go straight to the workspace and are counted after the routing barrier ----
@@ -1066,7 +1129,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     MOE_TRACE(5);
     if (b == 0 && threadIdx.x == 0)
         __hip_atomic_store(p.ws.hdr + kHdrCall, call + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (p.route_only) return;
+    if (p.route_only) {
+        MOE_TRACE_FLUSH;
+        return;
+    }
     if (sh_rows > 0) {  // the shared rows' stores completed long ago; this wait is short
         publish();
         if (threadIdx.x == 0) add_dev(line(set, kLineShared), (uint32_t)sh_rows);
@@ -1077,8 +1143,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
 
     // ---- start streaming this workgroup's routed down rows into LDS (as far as the window goes):
     //      slice mode: rows [h0, h1) of every unit; otherwise an equal share of all units' rows ----
-    const int64_t dtotal = (int64_t)U * H;
-    const int64_t d0 = dtotal * b / G, d1 = dtotal * (b + 1) / G;
+    int64_t d0 = 0, d1 = 0;  // unit-major: this workgroup's (unit, row) range, split by cost
+    if (!p.slice_mode) cost_split(s_mask, U, H, kCostBase, p.cost_dn, G, b, &d0, &d1);
     int pre_rows[kMaxPre];
     int pre_off[kMaxPre];
     int nfit = 0;  // slice mode: units whose slice rows are in the window
@@ -1111,8 +1177,9 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     // ---- C: routed gate/up, an equal share of all routed tasks ----
     {
         const int TPU = I / RTG;
-        const int T = U * TPU;
-        const int qa = (int)((int64_t)T * b / G), qb = (int)((int64_t)T * (b + 1) / G);
+        int64_t qa64, qb64;
+        cost_split(s_mask, U, TPU, kCostBase, p.cost_gu, G, b, &qa64, &qb64);
+        const int qa = (int)qa64, qb = (int)qb64;
         if (qb > qa) {
             const int64_t rb = row_bytes<WF>(H);
             gateup_run<AF, WF, NJ>(
@@ -1232,14 +1299,26 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     ((uint16_t*)p.y)[(int64_t)m * H + h] = f32_to_bf16_rne(acc);
             }
         }
-        MOE_TRACE(17);
+        MOE_TRACE_FLUSH;
         return;
     }
 
-    // ---- D: routed down rows, unit by unit; partial outputs staged in LDS, written per pass ----
+    // ---- D: routed down rows, unit by unit.  Partial outputs are staged in LDS and written once at
+    //      the end when the whole range fits the staging area (no store in flight while the next
+    //      unit's weights stream), else per pass ----
     {
         LDS float* pst = cst;
         const int cap = p.cst_bytes / 4;
+        int64_t need = 0;
+        for (int64_t q = d0; q < d1;) {
+            const int u = (int)(q / H);
+            const int ha = (int)(q - (int64_t)u * H);
+            const int hb = (int)min<int64_t>(H, ha + (d1 - q));
+            q += hb - ha;
+            need += (int64_t)(hb - ha) * __popc(s_mask[u]);
+        }
+        const bool once = need <= cap;
+        int pbase = 0;
         int seg = 0;
         bool first = true;
         for (int64_t q = d0; q < d1; ++seg) {
@@ -1251,7 +1330,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             const int row0 = s_off[u];
             const int64_t e = s_exp[u];
             const int npre = seg < kMaxPre ? pre_rows[seg] : 0;
-            const int rows_per_pass = max(RTD, (cap / t) / RTD * RTD);
+            const int rows_per_pass = once ? hb - ha : max(RTD, (cap / t) / RTD * RTD);
             bool staged = false;
             // rows [ha, hb) in passes that fit the partial staging area
             for (int pa = ha; pa < hb; pa += rows_per_pass) {
@@ -1267,7 +1346,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                         first = false;
                     }
                 };
-                auto out = [&](int row, int i, float v) { pst[row * t + i] = v; };
+                LDS float* pout = pst + pbase;
+                auto out = [&](int row, int i, float v) { pout[row * t + i] = v; };
                 // part from the LDS window: rows [pa, min(pb, ha + npre))
                 const int la = pa, lb = min(pb, ha + npre);
                 if (lb > la) {
@@ -1284,12 +1364,33 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                                              [&](int row, int i, float v) { out(row + ga - pa, i, v); });
                 }
                 __syncthreads();
-                const int n = (pb - pa) * t;
+                if (once) {
+                    pbase += (pb - pa) * t;
+                } else {
+                    const int n = (pb - pa) * t;
+                    for (int i = threadIdx.x; i < n; i += kThreads) {
+                        const int rr = i / t, m = i - rr * t;
+                        st_dev(p.ws.part + (int64_t)(row0 + m) * H + pa + rr, pst[i]);
+                    }
+                    __syncthreads();
+                }
+            }
+        }
+        if (once) {  // every partial of the range, in the order it was staged
+            int base = 0;
+            for (int64_t q = d0; q < d1;) {
+                const int u = (int)(q / H);
+                const int ha = (int)(q - (int64_t)u * H);
+                const int hb = (int)min<int64_t>(H, ha + (d1 - q));
+                q += hb - ha;
+                const int t = __popc(s_mask[u]);
+                const int row0 = s_off[u];
+                const int n = (hb - ha) * t;
                 for (int i = threadIdx.x; i < n; i += kThreads) {
                     const int rr = i / t, m = i - rr * t;
-                    st_dev(p.ws.part + (int64_t)(row0 + m) * H + pa + rr, pst[i]);
+                    st_dev(p.ws.part + (int64_t)(row0 + m) * H + ha + rr, pst[base + i]);
                 }
-                __syncthreads();
+                base += n;
             }
         }
     }
@@ -1329,7 +1430,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 ((uint16_t*)p.y)[(int64_t)m * H + h] = f32_to_bf16_rne(acc);
         }
     }
-    MOE_TRACE(17);
+    MOE_TRACE_FLUSH;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1352,9 +1453,16 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     p.slice_mode = NP <= 16 ? 1 : 0;
     // staging area: routing scratch; routed SwiGLU results of one workgroup's tasks; down partials
     // (slice mode: [NP][nown]; unit-major: any size, larger means fewer passes)
+    // per-token cost of a gate/up task and of a down row relative to the weight bytes (kCostBase),
+    // from phase traces: bf16 down rows of 5-token units ran ~1.8x longer than 1-token ones; the
+    // decode of E2M1 codes makes MXFP4 rows four times denser in work
+    p.cost_gu = WF == MOE_FMT_MXFP4 ? 4 : 0;  // bf16 gate/up rows stay bound by their bytes
+    p.cost_dn = WF == MOE_FMT_MXFP4 ? 8 : (WF == MOE_FMT_BF16 ? 2 : 0);
     const int64_t tpu = p.I / rt_gate<WF>();
     const int64_t units = std::min<int64_t>(NP, p.E);
-    const int64_t c_tasks = (units * tpu + G - 1) / G + 1;
+    // a workgroup's gate/up share is at most (its cost share + one task) / kCostBase tasks
+    const int64_t c_tasks = (kCostBase * units * tpu + p.cost_gu * tpu * NP + (int64_t)G * kCostBase - 1) /
+                                ((int64_t)G * kCostBase) + 2;
     int64_t cst = std::max<int64_t>(kSelBytes, c_tasks * rt_gate<WF>() * M * 4);
     cst = std::max<int64_t>(cst, p.slice_mode ? (NP + M) * nown * 4 : 16 * 1024);
     int64_t xb = std::max<int64_t>((int64_t)M * H * XB, (int64_t)M * ka * 4);
@@ -1366,7 +1474,7 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     p.lds_sh = p.lds_cst + p.cst_bytes;
     p.lds_ysh = p.lds_sh + round16(p.Is > 0 ? nown * row_bytes<WF>(p.Is) : 0);
     p.lds_dn = p.lds_ysh + round16((int64_t)M * nown * 4);
-    const int budget = kLdsBytes - 256;  // room for the static LDS variables
+    const int budget = kLdsBytes - 512;  // room for the static LDS variables
     p.dn_bytes = p.route_only ? 0 : std::max(0, (budget - p.lds_dn) / 16 * 16);
     p.lds_total = p.lds_dn + p.dn_bytes;
     if (p.lds_total > budget) return hipErrorInvalidConfiguration;
