@@ -53,6 +53,8 @@ struct Params {
     int cst_bytes;    // staging area (routing scratch, SwiGLU results, down partials)
     int dn_bytes;     // routed down-row window
     int slice_mode;   // 1: every workgroup computes its y slice of every routed unit (small M*k)
+    int slice_mfma;   // 1: slice mode on the matrix cores (bfloat16 SwiGLU rows, swizzled windows)
+    int sh_mfma;      // 1: the shared expert's down rows on the matrix cores (swizzled window)
     int cost_gu;      // per-token cost of a gate/up task, and of a down row, relative to the
     int cost_dn;      // weight bytes (8 units): work is split so high-token units get more CUs
     const void* x;

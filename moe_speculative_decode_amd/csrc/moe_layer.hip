@@ -31,6 +31,7 @@
 // counter is bumped only after the stores have completed; there are no cache-wide fences.
 // Every wait is bounded: on a timeout the status word is flagged and the kernel still finishes.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -40,6 +41,7 @@ namespace {
 #define LDS __attribute__((address_space(3)))
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -426,6 +428,27 @@ __device__ __forceinline__ void async_to_lds(char* lds, const uint8_t* src, int 
     }
 }
 
+// The same for n bytes of whole rows of rb bytes, with the 16-byte chunks of each row permuted so
+// that chunk c of row r lands in slot c ^ chunk_swz(r, rb): lanes that read one chunk position of
+// 16 (rows of a multiple of 256 bytes) or 8 (of 128 bytes) consecutive rows then hit different
+// bank groups.  Each lane fetches the global chunk that belongs in its slot, so the copy stays one
+// 16-byte load per lane.
+__host__ __device__ __forceinline__ int chunk_swz(int row, int64_t rb) {
+    return (rb & 255) == 0 ? (row & 15) : ((rb & 127) == 0 ? (row & 7) : 0);
+}
+__device__ __forceinline__ void async_rows_to_lds(char* lds, const uint8_t* src, int n, int rb) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    constexpr int chunk = 64 * 16;
+    for (int base = wave * chunk; base < n; base += kWaves * chunk) {
+        const int o = base + lane * 16;
+        if (o < n) {
+            const int row = o / rb, c = (o - row * rb) >> 4;
+            auto* dst = (LDS void*)(lds + base);
+            __builtin_amdgcn_global_load_lds(src + (int64_t)row * rb + 16 * (c ^ chunk_swz(row, rb)), dst, 16, 0, 0);
+        }
+    }
+}
+
 // fp32 logits rows are padded to whole 16-byte chunks
 __host__ __device__ __forceinline__ int logit_stride(int E) { return (E + 3) / 4 * 4; }
 
@@ -465,6 +488,35 @@ __device__ __forceinline__ void stage_rows(LDS float* dst, const float* src, int
                 } else {
                     ((LDS f32x4*)dst)[i] = v[u];
                 }
+            }
+        }
+    }
+}
+
+// Stages `tcount` fp32 SwiGLU rows of K elements (global rows of `stride` floats from `src`) into
+// LDS as bfloat16 (round to nearest even), rows of `pitch` bytes, with 16-byte device-scope loads.
+__device__ __forceinline__ void stage_rows_bf16(LDS char* dst, const float* src, int stride, int tcount, int K,
+                                                int pitch) {
+    const __amdgpu_buffer_rsrc_t r = dev_rsrc(src, (uint32_t)(tcount * stride * 4));
+    const int q4 = K / 4, n = tcount * q4;
+    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * kThreads) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kThreads;
+            if (i < n) {
+                const int t = i / q4, c4 = i - t * q4;
+                v[u] = ld_dev16(r, (uint32_t)((t * stride + 4 * c4) * 4));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kThreads;
+            if (i < n) {
+                const int t = i / q4, c4 = i - t * q4;
+                const uint32_t b0 = f32_to_bf16_rne(v[u][0]), b1 = f32_to_bf16_rne(v[u][1]);
+                const uint32_t b2 = f32_to_bf16_rne(v[u][2]), b3 = f32_to_bf16_rne(v[u][3]);
+                *(LDS u32x2*)(dst + (int64_t)t * pitch + 8 * c4) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
             }
         }
     }
@@ -1004,6 +1056,149 @@ __device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Inf
     }
 }
 
+// One unit of the slice-mode down projection: its weight rows [h0, h0 + nown) (row 0 at w, an LDS
+// address when lds, stored by async_rows_to_lds), K inputs, t tokens whose bfloat16 SwiGLU rows
+// start at acts (LDS rows of the caller's pitch), and the pair row of its first token.
+struct SliceUnit {
+    const uint8_t* w;
+    const uint8_t* s;        // MXFP4 scales of row 0 (global memory)
+    const LDS char* acts;
+    int lds, K, t, prow;
+};
+
+// Slice-mode down rows on the matrix cores.  The workgroup computes y columns [h0, h0 + nown),
+// nown <= 16, of all nun units; one wave takes a whole unit (units w + 1, w + 9, ... for wave w) as a
+// chain of v_mfma_f32_16x16x32_bf16 products over the unit's 32-wide K blocks: A = its weight rows
+// (MXFP4 codes dequantised to bfloat16 on the way), B = its tokens' bfloat16 SwiGLU rows, one
+// column per token (t <= 16).  Results go to pst[(prow + token) * nown + row].  Units [0, npre) need
+// no wait and are computed before ready(); units [npre, npre + ng) read their rows from global
+// memory (a wave's first such unit is loaded before ready()), the rest from LDS.  Operand layout of the instruction (16x16x32, bf16): lane l holds A[l % 16][8 (l / 16) + 0..7],
+// B[8 (l / 16) + 0..7][l % 16] and D[4 (l / 16) + 0..3][l % 16].
+template <int WF, int KB, typename UnitOf, typename Ready>
+__device__ __forceinline__ void down_slice_mfma(int nun, int npre, int ng, int nown, int apitch, UnitOf unit_of,
+                                                Ready ready, LDS float* pst) {
+    static_assert(WF == MOE_FMT_BF16 || WF == MOE_FMT_MXFP4, "bf16 or MXFP4 weights");
+    static_assert(KB % 8 == 0, "K blocks in batches of 8");
+    constexpr int BB = 8;  // B chunks per batch
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int r = lane & 15, kq = lane >> 4;  // A row / token column; the lane's 8-wide K slice
+    const int rr = min(r, nown - 1);          // rows past nown load row nown - 1 (results dropped)
+    // A chunks: 8 bfloat16, or 8 E2M1 codes and their block's scale byte
+    struct AOpB {
+        u32x4 q;
+    };
+    struct AOpF {
+        uint32_t c, s;
+    };
+    using AOp = std::conditional_t<WF == MOE_FMT_BF16, AOpB, AOpF>;
+    AOp a[KB];
+    // Only lanes of live rows read weights and only lanes of live tokens read SwiGLU rows (the LDS
+    // port, not the matrix core, bounds this phase); other lanes keep stale operands, which reach
+    // only the rows and columns of D that are dropped.
+    auto load_a = [&](const SliceUnit& u, auto from_lds) {
+        const int64_t rb = row_bytes<WF>(u.K);
+        if (r >= nown) return;
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+            const int k0 = min(32 * i + 8 * kq, u.K - 8);  // in bounds; past K the B side is zero
+            if constexpr (decltype(from_lds)::value) {
+                const LDS uint8_t* row = (const LDS uint8_t*)u.w + rr * rb;
+                const int sw = chunk_swz(rr, rb);
+                if constexpr (WF == MOE_FMT_BF16)
+                    a[i].q = *(const LDS u32x4*)(row + 16 * ((k0 >> 3) ^ sw));
+                else
+                    a[i].c = *(const LDS uint32_t*)(row + 16 * ((k0 >> 5) ^ sw) + 4 * ((k0 >> 3) & 3));
+            } else {
+                const uint8_t* row = u.w + rr * rb;
+                if constexpr (WF == MOE_FMT_BF16)
+                    a[i].q = __builtin_nontemporal_load((const u32x4*)(row + 2 * k0));
+                else
+                    a[i].c = __builtin_nontemporal_load((const uint32_t*)(row + k0 / 2));
+            }
+            if constexpr (WF == MOE_FMT_MXFP4) a[i].s = u.s[rr * (u.K / 32) + k0 / 32];
+        }
+    };
+    auto a_operand = [&](int i) {
+        if constexpr (WF == MOE_FMT_BF16) {
+            asm volatile("" : "+v"(a[i].q));
+            return __builtin_bit_cast(bf16x8, a[i].q);
+        } else {
+            asm volatile("" : "+v"(a[i].c), "+v"(a[i].s));
+            const uint32_t c = a[i].c;
+            const float sc = e8m0_to_f32(a[i].s);
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1);
+            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 2);
+            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 3);
+            return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+    };
+    // One column per token, one B read per K block.
+    auto compute_many = [&](const SliceUnit& u) {
+        const LDS char* brow = u.acts + (int64_t)min(r, u.t - 1) * apitch;
+        auto load_b = [&](u32x4(&b)[BB], int i0) {
+            if (r >= u.t) return;
+#pragma unroll
+            for (int j = 0; j < BB; ++j) b[j] = *(const LDS u32x4*)(brow + 2 * min(32 * (i0 + j) + 8 * kq, u.K - 8));
+        };
+        f32x4 acc[4] = {};
+        u32x4 ba[BB] = {}, bb[BB] = {};
+        auto batch = [&](u32x4(&b)[BB], int i0) {
+#pragma unroll
+            for (int j = 0; j < BB; ++j) asm volatile("" : "+v"(b[j]));
+#pragma unroll
+            for (int j = 0; j < BB; ++j) {
+                const int i = i0 + j;
+                const bool kv = 32 * i + 8 * kq < u.K;
+                acc[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    a_operand(i), __builtin_bit_cast(bf16x8, kv ? b[j] : u32x4{0u, 0u, 0u, 0u}), acc[j & 3], 0, 0, 0);
+            }
+        };
+        load_b(ba, 0);
+#pragma unroll
+        for (int i0 = 0; i0 < KB; i0 += 2 * BB) {
+            if (i0 + BB < KB) load_b(bb, i0 + BB);
+            batch(ba, i0);
+            if (i0 + BB >= KB) break;
+            if (i0 + 2 * BB < KB) load_b(ba, i0 + 2 * BB);
+            batch(bb, i0 + BB);
+        }
+        const f32x4 d = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        if (r < u.t) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = 4 * kq + q;
+                if (row < nown) pst[(u.prow + r) * nown + row] = d[q];
+            }
+        }
+    };
+    auto compute = [&](const SliceUnit& u) { compute_many(u); };
+    SliceUnit u;
+    int q = (wave + 1) % kWaves;  // unit 0 to the last wave: wave 0 also polls in ready()
+    for (; q < npre; q += kWaves) {  // units that need no wait (rows in LDS, SwiGLU rows staged)
+        unit_of(q, u);
+        load_a(u, std::true_type{});
+        compute(u);
+    }
+    const int q0 = q;
+    const bool pre = q < npre + ng;
+    if (pre) {  // a unit streamed from global memory: its loads overlap the wait
+        unit_of(q, u);
+        load_a(u, std::false_type{});
+    }
+    ready();
+    for (; q < nun; q += kWaves) {
+        if (q != q0 || !pre) {
+            unit_of(q, u);
+            if (q < npre + ng)
+                load_a(u, std::false_type{});
+            else
+                load_a(u, std::true_type{});
+        }
+        compute(u);
+    }
+}
+
 // Splits a list of U units of n items each (rows or tasks; item i of unit u has flat index
 // u * n + i) over G workgroups by cost, an item of unit u costing c0 + c1 * t_u where t_u is the
 // unit's token count: every workgroup gets an equal share of the total cost, so units that many
@@ -1082,8 +1277,15 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 ld_chunk<AF>(rfirst[j], (const uint8_t*)p.wr + (int64_t)e * H * XB, nullptr, min(lane + 64 * j, nch - 1));
         }
     }
-    if (has_sh && !p.route_only && nown > 0)
-        async_to_lds((char*)shw, (const uint8_t*)p.w.sh_down + h0 * rbIs, (int)(nown * rbIs));
+    // slice mode on the matrix cores reads the LDS windows row-interleaved: store them swizzled
+    const bool mf_slice = p.slice_mfma != 0;
+    const bool mf_sh = p.sh_mfma != 0;  // shared down rows on the matrix cores (window stored swizzled)
+    if (has_sh && !p.route_only && nown > 0) {
+        if (mf_sh)
+            async_rows_to_lds((char*)shw, (const uint8_t*)p.w.sh_down + h0 * rbIs, (int)(nown * rbIs), (int)rbIs);
+        else
+            async_to_lds((char*)shw, (const uint8_t*)p.w.sh_down + h0 * rbIs, (int)(nown * rbIs));
+    }
     __builtin_amdgcn_s_waitcnt(0);  // token rows (and the slice's shared down rows) in LDS
     __syncthreads();
     MOE_TRACE(1);
@@ -1151,9 +1353,13 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     if (p.slice_mode) {
         if (nown > 0) {
             nfit = min(U, (int)(p.dn_bytes / (nown * rbI)));
-            for (int u = 0; u < nfit; ++u)
-                async_to_lds((char*)(dnw + (int64_t)u * nown * rbI),
-                             (const uint8_t*)p.w.down + ((int64_t)s_exp[u] * H + h0) * rbI, (int)(nown * rbI));
+            for (int u = 0; u < nfit; ++u) {
+                const uint8_t* src = (const uint8_t*)p.w.down + ((int64_t)s_exp[u] * H + h0) * rbI;
+                if (mf_slice)
+                    async_rows_to_lds((char*)(dnw + (int64_t)u * nown * rbI), src, (int)(nown * rbI), (int)rbI);
+                else
+                    async_to_lds((char*)(dnw + (int64_t)u * nown * rbI), src, (int)(nown * rbI));
+            }
         }
     } else {
         int64_t room = p.dn_bytes;
@@ -1224,7 +1430,27 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
 
     // ---- B': the shared expert's down rows of this slice (weights in LDS) -> ysh [M][nown], while
     //      the routed units' counters complete ----
-    if (has_sh && nown > 0 && !p.slice_mode) {
+    //      (slice mode: in its down phase, before the wait for the routed units) ----
+    if constexpr (WF != MOE_FMT_F32 && NJD <= 3) {
+        if (has_sh && nown > 0 && mf_sh && !p.slice_mode) {
+            wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
+            const int apitch = 2 * p.act_stride;
+            stage_rows_bf16((LDS char*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is, apitch);
+            __syncthreads();
+            auto unit_of = [&](int, SliceUnit& t) {
+                t.prow = 0;
+                t.t = M;
+                t.K = Is;
+                t.lds = 1;
+                t.w = (const uint8_t*)shw;
+                t.s = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
+                t.acts = (const LDS char*)xs;
+            };
+            down_slice_mfma<WF, 8 * NJD>(1, 1, 0, nown, apitch, unit_of, []() {}, ysh);
+            __syncthreads();
+        }
+    }
+    if (has_sh && nown > 0 && !p.slice_mode && !mf_sh) {
         wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
         stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
         __syncthreads();
@@ -1278,6 +1504,65 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 __syncthreads();
                 MOE_TRACE(10);
             };
+            if constexpr (WF != MOE_FMT_F32 && NJD <= 3) {
+                if (mf_slice) {
+                    // matrix-core path: SwiGLU rows staged as bfloat16, one wave per unit
+                    const int apitch = 2 * astride;
+                    const int nsh = has_sh ? 1 : 0;  // the shared unit first: it needs no wait
+                    if (has_sh) {
+                        wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
+                        stage_rows_bf16((LDS char*)xs + (int64_t)NP * apitch, p.ws.act + (int64_t)NP * astride, astride,
+                                        M, Is, apitch);
+                        __syncthreads();
+                    }
+                    auto unit_of = [&](int q0, SliceUnit& t) {
+                        const int q = q0 - nsh;
+                        if (q >= 0) {
+                            const int u = q < ng ? nfit + q : q - ng;
+                            const int64_t e = uni(s_exp[u]);
+                            t.prow = uni(s_off[u]);
+                            t.t = __popc(uni(s_mask[u]));
+                            t.K = I;
+                            t.lds = q >= ng ? 1 : 0;
+                            t.w = t.lds ? (const uint8_t*)(dnw + (int64_t)u * nown * rbI)
+                                        : (const uint8_t*)p.w.down + (e * H + h0) * rbI;
+                            t.s = WF == MOE_FMT_MXFP4 ? p.w.down_s + (e * H + h0) * (I / 32) : nullptr;
+                        } else {
+                            t.prow = NP;
+                            t.t = M;
+                            t.K = Is;
+                            t.lds = 1;
+                            t.w = (const uint8_t*)shw;
+                            t.s = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
+                        }
+                        t.acts = (const LDS char*)xs + (int64_t)t.prow * apitch;
+                    };
+                    auto ready_bf16 = [&]() {  // the shared expert's rows were staged above
+                        wait_units(set, U, (uint32_t)I, 0u, p.ws.hdr + kHdrStatus);
+                        MOE_TRACE(9);
+                        stage_rows_bf16((LDS char*)xs, p.ws.act, astride, NP, astride, apitch);
+                        __syncthreads();
+                        MOE_TRACE(10);
+                    };
+                    down_slice_mfma<WF, 8 * NJD>(U + nsh, nsh, ng, nown, apitch, unit_of, ready_bf16, pst);
+                    __syncthreads();
+                    MOE_TRACE(11);
+                    const LDS int* s_pair = tab + kTabPair;
+                    const LDS float* s_roww = (const LDS float*)(tab + kTabRowW);
+                    for (int i = threadIdx.x; i < M * nown; i += kThreads) {
+                        const int m = i / nown, hh = i - m * nown, h = h0 + hh;
+                        float acc = 0.0f;
+                        for (int j = 0; j < k; ++j) {
+                            const int row = s_pair[m * k + j];
+                            acc = fmaf(s_roww[row], pst[row * nown + hh], acc);
+                        }
+                        if (has_sh) acc += pst[(NP + m) * nown + hh];
+                        ((uint16_t*)p.y)[(int64_t)m * H + h] = f32_to_bf16_rne(acc);
+                    }
+                    MOE_TRACE_FLUSH;
+                    return;
+                }
+            }
             down_flat<WF, NJD>(nun * nblk, astride, wave_id(), info, ready,
                                [&](const DNTask& t, int row, int i, float v) { pst[(t.prow + i) * nown + t.orow + row] = v; });
             __syncthreads();
@@ -1451,6 +1736,10 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     // slice mode (each workgroup finishes its own y columns of every unit) while M * k is small:
     // then every workgroup stages all pair rows' SwiGLU outputs; otherwise unit-major down rows
     p.slice_mode = NP <= 16 ? 1 : 0;
+    // slice mode on the matrix cores (bf16 and MXFP4 weights, up to 16 rows per workgroup, K <= 768):
+    // bfloat16 SwiGLU rows, swizzled weight windows
+    p.sh_mfma = (WF != MOE_FMT_F32 && NJD <= 3 && nown <= 16) ? 1 : 0;
+    p.slice_mfma = (p.slice_mode && p.sh_mfma) ? 1 : 0;
     // staging area: routing scratch; routed SwiGLU results of one workgroup's tasks; down partials
     // (slice mode: [NP][nown]; unit-major: any size, larger means fewer passes)
     // per-token cost of a gate/up task and of a down row relative to the weight bytes (kCostBase),
@@ -1466,7 +1755,7 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     int64_t cst = std::max<int64_t>(kSelBytes, c_tasks * rt_gate<WF>() * M * 4);
     cst = std::max<int64_t>(cst, p.slice_mode ? (NP + M) * nown * 4 : 16 * 1024);
     int64_t xb = std::max<int64_t>((int64_t)M * H * XB, (int64_t)M * ka * 4);
-    if (p.slice_mode) xb = std::max<int64_t>(xb, (NP + M) * ka * 4);
+    if (p.slice_mode) xb = std::max<int64_t>(xb, (NP + M) * ka * (p.slice_mfma ? 2 : 4));
     p.lds_tab = 0;
     p.lds_x = round16(kTabWords * 4);
     p.lds_cst = p.lds_x + round16(xb);

@@ -37,6 +37,11 @@ SMALL = [
     small("bf16_k_eq_E", E=8, k=8, lens=(3,)),
     small("bf16_k16", E=128, k=16, lens=(16,)),
     small("bf16_E512", E=512, k=8, lens=(8,)),
+    # top-k split over several waves per token (parts of 64 * L experts, then a merge pass)
+    small("bf16_E512_m2", E=512, k=8, lens=(2,)),
+    small("bf16_E384_m3", E=384, k=6, lens=(3,)),
+    small("bf16_E512_k16_m1", E=512, k=16, lens=(1,), recipe="iid"),
+    small("bf16_E200_m1", E=200, k=8, lens=(1,), recipe="iid"),
 ]
 
 
