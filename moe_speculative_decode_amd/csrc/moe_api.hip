@@ -18,7 +18,7 @@ bool is_aligned(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 // byte offsets of the workspace regions for a description (validated by the caller)
 struct Layout {
-    size_t hdr, ctr, logits, act, part, total;
+    size_t hdr, ctr, logits, route, act, part, total;
 };
 
 Layout layout(const moe_desc_t& d) {
@@ -33,6 +33,8 @@ Layout layout(const moe_desc_t& d) {
     o = up(o + 2 * sizeof(uint32_t) * (size_t)moe::kSetWords);
     L.logits = o;
     o = up(o + 8 * Mx * ((E + 3) / 4 * 4));
+    L.route = o;
+    o = up(o + 16 * Mx * k);
     L.act = o;
     o = up(o + 4 * rows * ka);
     L.part = o;
@@ -85,6 +87,7 @@ int fill_common(Params& p, const moe_desc_t* d, int32_t M, const void* x, const 
     W.hdr = (uint32_t*)(b + L.hdr);
     W.ctr = (uint32_t*)(b + L.ctr);
     W.logits = (uint64_t*)(b + L.logits);
+    W.route = (uint64_t*)(b + L.route);
     W.act = (float*)(b + L.act);
     W.part = (float*)(b + L.part);
     return MOE_OK;

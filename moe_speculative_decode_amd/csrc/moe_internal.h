@@ -21,8 +21,8 @@ constexpr int kLdsBytes = 160 * 1024;     // LDS of one CU (gfx950)
 // (c + 1) & 1, which the previous call used and the next call will use.
 constexpr int kLineWords = 64;
 constexpr int kLineShared = 0;                            // shared-expert SwiGLU rows finished
-constexpr int kLineUnit0 = 1;                             // [kMaxExperts] routed SwiGLU rows finished
-constexpr int kLineOwner0 = kLineUnit0 + kMaxExperts;     // [kMaxGrid] partial rows landed per y slice
+constexpr int kLineRouted = 1;                            // routed SwiGLU rows finished (all units)
+constexpr int kLineOwner0 = 2;                            // [kMaxGrid] partial rows landed per y slice
 constexpr int kSetLines = kLineOwner0 + kMaxGrid;
 constexpr int kSetWords = kSetLines * kLineWords;
 
@@ -39,6 +39,7 @@ struct Workspace {
     uint32_t* hdr;    // [kHdrBytes / 4]
     uint32_t* ctr;    // [2][kSetWords]
     uint64_t* logits; // [max_tokens][E] (rows padded to 4): fp32 logit bits | (call index + 1) << 32
+    uint64_t* route;  // [max_tokens * k][2]: expert id, fp32 weight bits, each | (call index + 1) << 32
     float* act;       // [max_tokens * (k + 1)][act_stride]  SwiGLU output per pair row
     float* part;      // [max_tokens * (k + 1)][H]           down projection per pair row
 };
@@ -48,6 +49,7 @@ struct Params {
     int act_fmt, w_fmt;
     int act_stride;   // row stride (elements) of Workspace::act = max(I, Is)
     int route_only;   // 1: routing outputs only (moe_route)
+    int route_delegate;  // 1: workgroup m selects token m's experts and publishes them
     // LDS layout, byte offsets from the dynamic LDS base (filled by launch_layer)
     int lds_tab, lds_x, lds_cst, lds_sh, lds_ysh, lds_dn, lds_total;
     int cst_bytes;    // staging area (routing scratch, SwiGLU results, down partials)
@@ -55,8 +57,10 @@ struct Params {
     int slice_mode;   // 1: every workgroup computes its y slice of every routed unit (small M*k)
     int slice_mfma;   // 1: slice mode on the matrix cores (bfloat16 SwiGLU rows, swizzled windows)
     int sh_mfma;      // 1: the shared expert's down rows on the matrix cores (swizzled window)
-    int cost_gu;      // per-token cost of a gate/up task, and of a down row, relative to the
-    int cost_dn;      // weight bytes (8 units): work is split so high-token units get more CUs
+    int gu_mfma;      // 1: routed gate/up rows on the matrix cores (MXFP4 weights)
+    int xpitch;       // bytes between consecutive token rows staged in LDS (padded)
+    int cost_dn;      // per-token cost of a down row relative to its weight bytes (8 units): work
+                      // is split so that high-token units get more CUs
     const void* x;
     const void* wr;
     moe_weights_t w;

@@ -112,6 +112,10 @@ __device__ __forceinline__ float wave_max_bcast(float v) {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+// Number of the tasks b, b + G, b + 2G, ... below T: tasks are dealt to the G workgroups round
+// robin, so at any moment the whole grid streams one contiguous window of the weights (every HBM
+// channel busy, every workgroup with the same bytes to move).
+__device__ __forceinline__ int n_strided(int T, int b, int G) { return b < T ? (T - 1 - b) / G + 1 : 0; }
 
 
 // ------------------------------------------------------------------------------------------
@@ -394,14 +398,15 @@ __device__ __forceinline__ void wait_geq(const uint32_t* c, uint32_t target, uin
 }
 __device__ __forceinline__ uint32_t* line(uint32_t* set, int l) { return set + (int64_t)l * kLineWords; }
 
-// Every wave of the workgroup continues once the first U unit counters have reached `target` and
-// the shared expert's counter `sh_target` (bounded).
-__device__ __forceinline__ void wait_units(uint32_t* set, int U, uint32_t target, uint32_t sh_target, uint32_t* status) {
+// Every wave of the workgroup continues once the routed SwiGLU row counter has reached `target`
+// and the shared expert's counter `sh_target` (bounded).
+__device__ __forceinline__ void wait_units(uint32_t* set, uint32_t target, uint32_t sh_target, uint32_t* status) {
     if (wave_id() == 0) {
         const int lane = threadIdx.x & 63;
         for (int it = 0;; ++it) {
-            bool ok = lane != 0 || ld_dev(line(set, kLineShared)) >= sh_target;
-            for (int u = lane; u < U; u += 64) ok = ok && ld_dev(line(set, kLineUnit0 + u)) >= target;
+            bool ok = true;
+            if (lane == 0) ok = ld_dev(line(set, kLineShared)) >= sh_target;
+            if (lane == 1) ok = ld_dev(line(set, kLineRouted)) >= target;
             if (__ballot(!ok) == 0ull) break;
             if (it >= kSpinLimit) {
                 if (lane == 0) atomicOr(status, kStatusTimeout);
@@ -424,6 +429,20 @@ __device__ __forceinline__ void async_to_lds(char* lds, const uint8_t* src, int 
         if (base + lane * 16 < n) {
             auto* dst = (LDS void*)(lds + base);
             __builtin_amdgcn_global_load_lds(src + base + lane * 16, dst, 16, 0, 0);
+        }
+    }
+}
+
+// The same for nrows rows of rb bytes (a multiple of 16) that land `pitch` bytes apart in LDS.
+__device__ __forceinline__ void async_rows_pitch(char* lds, const uint8_t* src, int nrows, int rb, int pitch) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    constexpr int chunk = 64 * 16;
+    const int cpr = (rb + chunk - 1) / chunk;  // instructions per row
+    for (int c = wave; c < nrows * cpr; c += kWaves) {
+        const int row = c / cpr, o = (c - row * cpr) * chunk;
+        if (o + lane * 16 < rb) {
+            auto* dst = (LDS void*)(lds + (int64_t)row * pitch + o);
+            __builtin_amdgcn_global_load_lds(src + (int64_t)row * rb + o + lane * 16, dst, 16, 0, 0);
         }
     }
 }
@@ -633,9 +652,58 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
     LDS int* s_pair = tab + kTabPair;
     LDS float* s_roww = (LDS float*)(tab + kTabRowW);
 
-    for (int m = wave; m < M; m += kWaves)
-        wave_topk(p.ws.logits + (int64_t)m * logit_stride(E), E, k, tag, p.ws.hdr + kHdrStatus, sid + m * k,
-                  sw + m * k, sv + m * k);
+    if (!p.route_delegate) {
+        for (int m = wave; m < M; m += kWaves)
+            wave_topk(p.ws.logits + (int64_t)m * logit_stride(E), E, k, tag, p.ws.hdr + kHdrStatus, sid + m * k,
+                      sw + m * k, sv + m * k);
+    } else {
+        // workgroup m < M selects token m's experts and publishes them as tagged words; every
+        // workgroup then reads the M * k published (id, weight) pairs instead of M * E logits
+        const int b = blockIdx.x;
+        if (b < M && wave == 0) {
+            wave_topk(p.ws.logits + (int64_t)b * logit_stride(E), E, k, tag, p.ws.hdr + kHdrStatus, sid + b * k,
+                      sw + b * k, sv + b * k);
+            if (lane < k) {
+                uint64_t* dst = p.ws.route + 2 * (int64_t)(b * k + lane);
+                const uint64_t hi = (uint64_t)tag << 32;
+                __hip_atomic_store(dst, hi | (uint32_t)sid[b * k + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + 1, hi | __float_as_uint(sw[b * k + lane]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        if (wave == kWaves - 1) {  // pairs q = lane + 64 i, i < 4 (M * k <= 256), written once all are current
+            const __amdgpu_buffer_rsrc_t rs = dev_rsrc(p.ws.route, (uint32_t)NP * 16);
+            u32x4 v[kMaxTokens * kMaxTopK / 64];
+            for (int it = 0;; ++it) {
+                bool ok = true;
+#pragma unroll
+                for (int i = 0; i < kMaxTokens * kMaxTopK / 64; ++i) {
+                    const int q = lane + 64 * i;
+                    if (q < NP) {
+                        v[i] = __builtin_bit_cast(u32x4, ld_dev16(rs, (uint32_t)q * 16));
+                        ok = ok && v[i][1] == tag && v[i][3] == tag;
+                    }
+                }
+                if (__ballot(!ok) == 0ull) {
+#pragma unroll
+                    for (int i = 0; i < kMaxTokens * kMaxTopK / 64; ++i) {
+                        const int q = lane + 64 * i;
+                        if (q < NP) {
+                            sid[q] = min((int)v[i][0], E - 1);
+                            sw[q] = __uint_as_float(v[i][2]);
+                        }
+                    }
+                    break;
+                }
+                if (it >= kSpinLimit) {
+                    if (lane == 0) atomicOr(p.ws.hdr + kHdrStatus, kStatusTimeout);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                asm volatile("" ::: "memory");  // the next iteration reads memory again
+            }
+        }
+    }
     __syncthreads();
     MOE_TRACE(13);
     if (wave == 0) {
@@ -771,7 +839,7 @@ __device__ __forceinline__ void router_rows(const Params& p, const LDS char* xs,
 #pragma unroll
         for (int j = 0; j < NJ; ++j) settle_mask<AF>(r[j], lane + 64 * j < nch);
         for (int m = 0; m < M; ++m) {
-            const LDS char* xrow = xs + (int64_t)m * H * XB;
+            const LDS char* xrow = xs + (int64_t)m * p.xpitch;
             float acc[kAcc] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int j = 0; j < NJ; ++j) dot_x<AF, AF>(r[j], xrow, min(lane + 64 * j, nch - 1), acc);
@@ -794,23 +862,21 @@ struct GUTask {
     int slot;           // staging row of the task's first row
 };
 
-// This wave's gate/up tasks q = qa + wslot, qa + wslot + kWaves, ... < qb.  info(q, task) describes
-// task q.  out(s, i, v) receives silu(g) * v of the task's row s - t.slot and the unit's i-th token
-// (in the row's last lane).  Each
+// This wave's gate/up tasks, local indices i = wslot, wslot + kWaves, ... < n.  info(i, task)
+// describes local task i.  out(s, i, v) receives silu(g) * v of the task's row s - t.slot and the
+// unit's i-th token (in the row's last lane).  Each
 // wave keeps the next task's loads in flight while it computes the current one; the prefetch is
 // unconditional (the last task re-reads itself) so the number of loads in flight is static and
 // the compiler waits for exactly the task it needs.
 template <int AF, int WF, int NJ, typename Info, typename Out>
-__device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, int qa, int qb, int wslot, Info info,
-                                           Out out) {
+__device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, int n, int wslot, Info info, Out out) {
     constexpr int LPR = Geo<WF>::LPR_G, RL = Geo<WF>::RL_G;
-    constexpr int XB = AF == MOE_FMT_F32 ? 4 : 2;
     const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
     const int H = p.H;
     const int nch = H / Geo<WF>::EPC;
     const int64_t rb = row_bytes<WF>(H), sb = H / 32;
-    int q = qa + wslot;
-    if (q >= qb) return;
+    int q = wslot;
+    if (q >= n) return;
     Chunk ga[RL][NJ], ua[RL][NJ], gb[RL][NJ], ub[RL][NJ];
     GUTask ta, tb;
     auto load = [&](Chunk(&g)[RL][NJ], Chunk(&u)[RL][NJ], const GUTask& t) {
@@ -846,7 +912,7 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
 #pragma unroll
                     for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(g[rl][j].q), "+v"(u[rl][j].q));
             }
-            const LDS char* xrow = xs + (int64_t)tok * H * XB;
+            const LDS char* xrow = xs + (int64_t)tok * p.xpitch;
             float ag[RL][kAcc], au[RL][kAcc];
 #pragma unroll
             for (int rl = 0; rl < RL; ++rl)
@@ -873,18 +939,124 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
     info(q, ta);
     load(ga, ua, ta);
     while (true) {
-        info(min(q + kWaves, qb - 1), tb);
+        info(min(q + kWaves, n - 1), tb);
         load(gb, ub, tb);
         settle_all(ga, ua);
         compute(ga, ua, ta);
         q += kWaves;
-        if (q >= qb) break;
-        info(min(q + kWaves, qb - 1), ta);
+        if (q >= n) break;
+        info(min(q + kWaves, n - 1), ta);
         load(ga, ua, ta);
         settle_all(gb, ub);
         compute(gb, ub, tb);
         q += kWaves;
-        if (q >= qb) break;
+        if (q >= n) break;
+    }
+}
+
+// Routed gate/up rows on the matrix cores, for MXFP4 weights.  The workgroup's tasks are nloc
+// tiles of 8 consecutive rows of the flattened (unit, row) list (local tile i = rows 8 (b + i G) ..
+// + 7), dealt to its waves round robin.  A tile is one 16-row A operand: the 8 gate rows (A rows
+// 0..7) and the same 8 up rows (A rows 8..15).
+// B holds the rows x of all M tokens (column n = token n, whichever unit the row belongs to), so a
+// chain of v_mfma_f32_16x16x32_bf16 gives g and v of the 8 rows for every token and each E2M1 code
+// is decoded once, not once per token.  Operand layout of the instruction: lane l holds A[l % 16][8
+// (l / 16) + 0..7], B[8 (l / 16) + 0..7][l % 16] and D[4 (l / 16) + 0..3][l % 16].  Lane (r, kq) =
+// (l % 16, l / 16) owns whole MX blocks 4q + kq of its row (16 bytes of codes and the block's scale
+// byte) and feeds elements 8m .. 8m + 7 of the block to the m-th product of block group q; B lane
+// (n, kq) holds the same elements of token n's row.  Stages of NQ block groups are double-buffered
+// (the last one re-read, so the number of loads in flight is static).  Blocks past H are zeroed.
+// silu(g) * v of row 8 (b + i G) + s of local tile i and the unit's n-th token goes to
+// cst[(8 i + s) * M + n].
+template <int NQ>
+__device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* xs, int nloc,
+                                               const LDS uint32_t* s_mask, const LDS int* s_exp, LDS float* cst) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int r = lane & 15, kq = lane >> 4;
+    const int H = p.H, I = p.I, M = p.M, G = gridDim.x, b = blockIdx.x;
+    const int nblk = H / 32, nquad = (nblk + 3) / 4, nstage = (nquad + NQ - 1) / NQ;
+    const int64_t rb = H / 2, sb = H / 32;
+    const int nmine = n_strided(nloc, wave, kWaves);  // local tiles wave, wave + kWaves, ...
+    if (nmine == 0) return;
+    const int nsteps = nmine * nstage;
+    const uint8_t* mat = r < 8 ? (const uint8_t*)p.w.gate : (const uint8_t*)p.w.up;
+    const uint8_t* mats = r < 8 ? p.w.gate_s : p.w.up_s;
+    const LDS char* xrow = xs + (int64_t)min(r, M - 1) * p.xpitch;  // columns past M are dropped
+    // first flat row of this wave's j-th tile, and its staging slot
+    auto tile_row = [&](int j) { return (int64_t)(b + (wave + kWaves * j) * G) * 8; };
+    auto tile_slot = [&](int j) { return (wave + kWaves * j) * 8; };
+    struct Stage {
+        u32x4 c[NQ];
+        uint32_t s[NQ];
+    };
+    auto load = [&](Stage& st, int t) {
+        const int j = t / nstage, sg = t - j * nstage;
+        const int64_t f = tile_row(j) + (r & 7);
+        const int u = (int)(f / I);
+        const int64_t row = (int64_t)s_exp[u] * I + (f - (int64_t)u * I);
+        const uint8_t* w = mat + row * rb;
+        const uint8_t* sc = mats + row * sb;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int bc = min(4 * (NQ * sg + q) + kq, nblk - 1);
+            st.c[q] = __builtin_nontemporal_load((const u32x4*)(w + 16 * bc));
+            st.s[q] = __builtin_nontemporal_load(sc + bc);
+        }
+    };
+    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+    auto compute = [&](Stage& st, int t) {
+        const int j = t / nstage, sg = t - j * nstage;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) asm volatile("" : "+v"(st.c[q]), "+v"(st.s[q]));
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int blk = 4 * (NQ * sg + q) + kq;
+            const bool valid = blk < nblk;
+            const float sc = e8m0_to_f32(valid ? st.s[q] : 127u);
+            const u32x4 c = valid ? st.c[q] : u32x4{0u, 0u, 0u, 0u};
+            const LDS char* xp = xrow + 64 * min(blk, nblk - 1);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const bf16x8 bop = *(const LDS bf16x8*)(xp + 16 * m);
+                const uint32_t wd = c[m];
+                const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 0);
+                const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 1);
+                const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 2);
+                const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 3);
+                const bf16x8 aop = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                if (m & 1)
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc1, 0, 0, 0);
+                else
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc0, 0, 0, 0);
+            }
+        }
+        if (sg == nstage - 1) {  // tile j done: lanes kq < 2 hold g of rows 4 kq + i, lanes kq + 2 their v
+            const f32x4 d = acc0 + acc1;
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = __shfl_xor(d[i], 32);
+            if (kq < 2 && r < M) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t mk = s_mask[(int)((tile_row(j) + 4 * kq + i) / I)];
+                    if ((mk >> r) & 1u)
+                        cst[(tile_slot(j) + 4 * kq + i) * M + __popc(mk & ((1u << r) - 1u))] = silu_mul(d[i], v[i]);
+                }
+            }
+            acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            acc1 = acc0;
+        }
+    };
+    Stage sa, sb2;
+    load(sa, 0);
+    int t = 0;
+    while (true) {
+        load(sb2, min(t + 1, nsteps - 1));
+        compute(sa, t);
+        if (++t >= nsteps) break;
+        load(sa, min(t + 1, nsteps - 1));
+        compute(sb2, t);
+        if (++t >= nsteps) break;
     }
 }
 
@@ -1265,7 +1437,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
 
     // ---- A: call index, token rows, router rows, shared-expert down rows of the slice ----
     if (threadIdx.x == 0) s_call = ld_dev(p.ws.hdr + kHdrCall);
-    async_to_lds((char*)xs, (const uint8_t*)p.x, M * H * XB);
+    async_rows_pitch((char*)xs, (const uint8_t*)p.x, M, H * XB, p.xpitch);
     const int e0 = (int)((int64_t)E * b / G), e1 = (int)((int64_t)E * (b + 1) / G);
     const int nrw = min(e1 - e0, kWaves);  // waves with router rows
     Chunk rfirst[NJ];
@@ -1308,13 +1480,12 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     //      results go straight to the workspace and are counted after the routing barrier ----
     int sh_rows = 0;
     if (has_sh && !p.route_only) {
-        const int T = Is / RTG;
-        const int qa = (int)((int64_t)T * b / G), qb = (int)((int64_t)T * (b + 1) / G);
-        sh_rows = (qb - qa) * RTG;
+        const int nsh = n_strided(Is / RTG, b, G);  // tasks b, b + G, b + 2G, ...
+        sh_rows = nsh * RTG;
         gateup_run<AF, WF, NJ>(
-            p, xs, qa, qb, kWaves - 1 - wave_id(),
-            [&](int q, GUTask& t) {
-                const int64_t r0 = (int64_t)q * RTG;
+            p, xs, nsh, kWaves - 1 - wave_id(),
+            [&](int i, GUTask& t) {
+                const int64_t r0 = (int64_t)(b + i * G) * RTG;
                 t.g = (const uint8_t*)p.w.sh_gate + r0 * row_bytes<WF>(H);
                 t.u = (const uint8_t*)p.w.sh_up + r0 * row_bytes<WF>(H);
                 t.gs = WF == MOE_FMT_MXFP4 ? p.w.sh_gate_s + r0 * (H / 32) : nullptr;
@@ -1380,52 +1551,57 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         for (; seg < kMaxPre; ++seg) pre_rows[seg] = pre_off[seg] = 0;
     }
 
-    // ---- C: routed gate/up, an equal share of all routed tasks ----
+    // ---- C: routed gate/up.  Tasks of rt consecutive rows of the flattened (unit, row) list are
+    //      dealt to the workgroups round robin; each workgroup stages its results in LDS, writes
+    //      them at the end and counts its rows on one counter ----
     {
-        const int TPU = I / RTG;
-        int64_t qa64, qb64;
-        cost_split(s_mask, U, TPU, kCostBase, p.cost_gu, G, b, &qa64, &qb64);
-        const int qa = (int)qa64, qb = (int)qb64;
-        if (qb > qa) {
-            const int64_t rb = row_bytes<WF>(H);
-            gateup_run<AF, WF, NJ>(
-                p, xs, qa, qb, wave_id(),
-                [&](int q, GUTask& t) {
-                    const int u = q / TPU;
-                    const int64_t e = uni(s_exp[u]);
-                    const int64_t r0 = (int64_t)(q - u * TPU) * RTG;
-                    t.g = (const uint8_t*)p.w.gate + (e * I + r0) * rb;
-                    t.u = (const uint8_t*)p.w.up + (e * I + r0) * rb;
-                    t.gs = WF == MOE_FMT_MXFP4 ? p.w.gate_s + (e * I + r0) * (H / 32) : nullptr;
-                    t.us = WF == MOE_FMT_MXFP4 ? p.w.up_s + (e * I + r0) * (H / 32) : nullptr;
-                    t.mask = uni(s_mask[u]);
-                    t.slot = (q - qa) * RTG;
-                },
-                [&](int r, int i, float v) { cst[r * M + i] = v; });
+        const int rt = p.gu_mfma ? 8 : RTG;  // rows per task (whole tasks: I is a multiple of rt)
+        const int64_t nrows = (int64_t)U * I;
+        const int nloc = n_strided((int)(nrows / rt), b, G);
+        if (nloc > 0) {
+            bool done = false;
+            if constexpr (WF == MOE_FMT_MXFP4) {
+                if (p.gu_mfma) {
+                    gateup_mfma_mx<10>(p, xs, nloc, s_mask, s_exp, cst);
+                    done = true;
+                }
+            }
+            if (!done) {
+                const int64_t rb = row_bytes<WF>(H);
+                gateup_run<AF, WF, NJ>(
+                    p, xs, nloc, wave_id(),
+                    [&](int i, GUTask& t) {
+                        const int64_t f = (int64_t)(b + i * G) * RTG;  // the task's first flat row
+                        const int u = uni((int)(f / I));
+                        const int64_t e = uni(s_exp[u]);
+                        const int64_t r0 = f - (int64_t)u * I;
+                        t.g = (const uint8_t*)p.w.gate + (e * I + r0) * rb;
+                        t.u = (const uint8_t*)p.w.up + (e * I + r0) * rb;
+                        t.gs = WF == MOE_FMT_MXFP4 ? p.w.gate_s + (e * I + r0) * (H / 32) : nullptr;
+                        t.us = WF == MOE_FMT_MXFP4 ? p.w.up_s + (e * I + r0) * (H / 32) : nullptr;
+                        t.mask = uni(s_mask[u]);
+                        t.slot = i * RTG;
+                    },
+                    [&](int r, int i, float v) { cst[r * M + i] = v; });
+            }
         }
         __syncthreads();
         MOE_TRACE(6);
-        // write the staged SwiGLU rows; then count them per unit once they have landed
-        if (qb > qa) {
-            const int n = (qb - qa) * RTG * M;
+        // write the staged SwiGLU rows (slot s: row s % rt of local task s / rt); then count them
+        // once they have landed
+        {
+            const int n = nloc * rt * M;
             for (int i = threadIdx.x; i < n; i += kThreads) {
                 const int s = i / M, m = i - s * M;
-                const int q = qa + s / RTG;
-                const int u = q / TPU;
-                if (m < __popc(s_mask[u])) {
-                    const int r = (q - u * TPU) * RTG + s % RTG;
-                    st_dev(p.ws.act + (int64_t)(s_off[u] + m) * p.act_stride + r, cst[i]);
-                }
+                const int64_t f = (int64_t)(b + (s / rt) * G) * rt + s % rt;
+                const int u = (int)(f / I);
+                if (m < __popc(s_mask[u]))
+                    st_dev(p.ws.act + (int64_t)(s_off[u] + m) * p.act_stride + (f - (int64_t)u * I), cst[i]);
             }
         }
         publish();
         MOE_TRACE(7);
-        if (qb > qa && threadIdx.x == 0) {
-            for (int u = qa / TPU; u <= (qb - 1) / TPU; ++u) {
-                const int a = max(qa, u * TPU), c = min(qb, (u + 1) * TPU);
-                add_dev(line(set, kLineUnit0 + u), (uint32_t)((c - a) * RTG));
-            }
-        }
+        if (nloc > 0 && threadIdx.x == 0) add_dev(line(set, kLineRouted), (uint32_t)(nloc * rt));
     }
 
     // ---- B': the shared expert's down rows of this slice (weights in LDS) -> ysh [M][nown], while
@@ -1498,7 +1674,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 t.acts = (const LDS float*)xs + (int64_t)t.prow * astride;
             };
             auto ready = [&]() {
-                wait_units(set, U, (uint32_t)I, has_sh ? (uint32_t)Is : 0u, p.ws.hdr + kHdrStatus);
+                wait_units(set, (uint32_t)(U * I), has_sh ? (uint32_t)Is : 0u, p.ws.hdr + kHdrStatus);
                 MOE_TRACE(9);
                 stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act, astride, NP + (has_sh ? M : 0), astride);
                 __syncthreads();
@@ -1538,7 +1714,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                         t.acts = (const LDS char*)xs + (int64_t)t.prow * apitch;
                     };
                     auto ready_bf16 = [&]() {  // the shared expert's rows were staged above
-                        wait_units(set, U, (uint32_t)I, 0u, p.ws.hdr + kHdrStatus);
+                        wait_units(set, (uint32_t)(U * I), 0u, p.ws.hdr + kHdrStatus);
                         MOE_TRACE(9);
                         stage_rows_bf16((LDS char*)xs, p.ws.act, astride, NP, astride, apitch);
                         __syncthreads();
@@ -1622,7 +1798,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 const int pb = min(hb, pa + rows_per_pass);
                 auto ready = [&]() {
                     if (!staged) {
-                        wait_geq(line(set, kLineUnit0 + u), (uint32_t)I, p.ws.hdr + kHdrStatus);
+                        wait_geq(line(set, kLineRouted), (uint32_t)(U * I), p.ws.hdr + kHdrStatus);
                         if (first) MOE_TRACE(9);
                         stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)row0 * p.act_stride, p.act_stride, t, I);
                         __syncthreads();
@@ -1736,6 +1912,9 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     // slice mode (each workgroup finishes its own y columns of every unit) while M * k is small:
     // then every workgroup stages all pair rows' SwiGLU outputs; otherwise unit-major down rows
     p.slice_mode = NP <= 16 ? 1 : 0;
+    // from three tokens on, the M * E logits that every workgroup would read are more polling traffic
+    // than one extra hand-off costs: workgroup m selects token m's experts and publishes them
+    p.route_delegate = (!p.route_only && M >= 3 && M <= G) ? 1 : 0;
     // slice mode on the matrix cores (bf16 and MXFP4 weights, up to 16 rows per workgroup, K <= 768):
     // bfloat16 SwiGLU rows, swizzled weight windows
     p.sh_mfma = (WF != MOE_FMT_F32 && NJD <= 3 && nown <= 16) ? 1 : 0;
@@ -1745,16 +1924,20 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     // per-token cost of a gate/up task and of a down row relative to the weight bytes (kCostBase),
     // from phase traces: bf16 down rows of 5-token units ran ~1.8x longer than 1-token ones; the
     // decode of E2M1 codes makes MXFP4 rows four times denser in work
-    p.cost_gu = WF == MOE_FMT_MXFP4 ? 4 : 0;  // bf16 gate/up rows stay bound by their bytes
+    // MXFP4 gate/up rows on the matrix cores: each code is decoded once for all tokens, so the
+    // work per weight byte no longer grows with the unit's token count
+    p.gu_mfma = WF == MOE_FMT_MXFP4 ? 1 : 0;
     p.cost_dn = WF == MOE_FMT_MXFP4 ? 8 : (WF == MOE_FMT_BF16 ? 2 : 0);
-    const int64_t tpu = p.I / rt_gate<WF>();
+    // gate/up tasks of rtg rows are dealt round robin: a workgroup stages at most ceil(T / G) tasks
+    const int64_t rtg = p.gu_mfma ? 8 : rt_gate<WF>();
     const int64_t units = std::min<int64_t>(NP, p.E);
-    // a workgroup's gate/up share is at most (its cost share + one task) / kCostBase tasks
-    const int64_t c_tasks = (kCostBase * units * tpu + p.cost_gu * tpu * NP + (int64_t)G * kCostBase - 1) /
-                                ((int64_t)G * kCostBase) + 2;
-    int64_t cst = std::max<int64_t>(kSelBytes, c_tasks * rt_gate<WF>() * M * 4);
+    const int64_t c_tasks = (units * p.I / rtg + G - 1) / G;
+    int64_t cst = std::max<int64_t>(kSelBytes, c_tasks * rtg * M * 4);
     cst = std::max<int64_t>(cst, p.slice_mode ? (NP + M) * nown * 4 : 16 * 1024);
-    int64_t xb = std::max<int64_t>((int64_t)M * H * XB, (int64_t)M * ka * 4);
+    // token rows 16 bytes further apart than their size: the 16 token columns of a matrix-core B
+    // operand then start in 16 different bank groups
+    p.xpitch = H * XB + 16;
+    int64_t xb = std::max<int64_t>((int64_t)M * p.xpitch, (int64_t)M * ka * 4);
     if (p.slice_mode) xb = std::max<int64_t>(xb, (NP + M) * ka * (p.slice_mfma ? 2 : 4));
     p.lds_tab = 0;
     p.lds_x = round16(kTabWords * 4);
