@@ -22,8 +22,11 @@ constexpr int kLdsBytes = 160 * 1024;     // LDS of one CU (gfx950)
 constexpr int kLineWords = 64;
 constexpr int kLineShared = 0;                            // shared-expert SwiGLU rows finished
 constexpr int kLineRouted = 1;                            // routed SwiGLU rows finished (all units)
-constexpr int kLineOwner0 = 2;                            // [kMaxGrid] partial rows landed per y slice
-constexpr int kSetLines = kLineOwner0 + kMaxGrid;
+constexpr int kMaxPools = kMaxGrid / 8;                   // work pools: one per 8 workgroups
+constexpr int kLinePoolC0 = 2;                            // [kMaxPools] gate/up chunks handed out
+constexpr int kLinePoolD0 = kLinePoolC0 + kMaxPools;      // [kMaxPools] down chunks handed out
+constexpr int kLineDownDone = kLinePoolD0 + kMaxPools;    // workgroups whose down partials have landed
+constexpr int kSetLines = kLineDownDone + 1;
 constexpr int kSetWords = kSetLines * kLineWords;
 
 // workspace header words
@@ -58,6 +61,7 @@ struct Params {
     int slice_mfma;   // 1: slice mode on the matrix cores (bfloat16 SwiGLU rows, swizzled windows)
     int sh_mfma;      // 1: the shared expert's down rows on the matrix cores (swizzled window)
     int gu_mfma;      // 1: routed gate/up rows on the matrix cores (MXFP4 weights)
+    int gu_cap;       // gate/up tasks one wave may stage (static share plus the chunks it takes)
     int xpitch;       // bytes between consecutive token rows staged in LDS (padded)
     int cost_dn;      // per-token cost of a down row relative to its weight bytes (8 units): work
                       // is split so that high-token units get more CUs

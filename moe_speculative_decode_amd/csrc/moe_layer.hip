@@ -862,21 +862,22 @@ struct GUTask {
     int slot;           // staging row of the task's first row
 };
 
-// This wave's gate/up tasks, local indices i = wslot, wslot + kWaves, ... < n.  info(i, task)
-// describes local task i.  out(s, i, v) receives silu(g) * v of the task's row s - t.slot and the
-// unit's i-th token (in the row's last lane).  Each
-// wave keeps the next task's loads in flight while it computes the current one; the prefetch is
-// unconditional (the last task re-reads itself) so the number of loads in flight is static and
-// the compiler waits for exactly the task it needs.
-template <int AF, int WF, int NJ, typename Info, typename Out>
-__device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, int n, int wslot, Info info, Out out) {
+// This wave's gate/up tasks, in the order next(0), next(1), ... until next returns -1 (called once
+// per position, in order, one position ahead of the compute).  info(q, s, task) describes task q
+// at position s.  out(r, i, v) receives silu(g) * v of the task's row r - t.slot and the unit's
+// i-th token (in the row's last lane).  Each wave keeps the next task's loads in flight while it
+// computes the current one; the prefetch is unconditional (the last task re-reads itself) so the
+// number of loads in flight is static and the compiler waits for exactly the task it needs.
+// Returns the number of tasks computed.
+template <int AF, int WF, int NJ, typename Next, typename Info, typename Out>
+__device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, Next next, Info info, Out out) {
     constexpr int LPR = Geo<WF>::LPR_G, RL = Geo<WF>::RL_G;
     const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
     const int H = p.H;
     const int nch = H / Geo<WF>::EPC;
     const int64_t rb = row_bytes<WF>(H), sb = H / 32;
-    int q = wslot;
-    if (q >= n) return;
+    int q = next(0);
+    if (q < 0) return 0;
     Chunk ga[RL][NJ], ua[RL][NJ], gb[RL][NJ], ub[RL][NJ];
     GUTask ta, tb;
     auto load = [&](Chunk(&g)[RL][NJ], Chunk(&u)[RL][NJ], const GUTask& t) {
@@ -936,22 +937,35 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
             }
         }
     };
-    info(q, ta);
+    int s = 0;
+    info(q, 0, ta);
     load(ga, ua, ta);
     while (true) {
-        info(min(q + kWaves, n - 1), tb);
+        const int qb = next(s + 1);
+        info(qb >= 0 ? qb : q, s + 1, tb);
         load(gb, ub, tb);
         settle_all(ga, ua);
         compute(ga, ua, ta);
-        q += kWaves;
-        if (q >= n) break;
-        info(min(q + kWaves, n - 1), ta);
+        ++s;
+        if (qb < 0) break;
+        const int qa = next(s + 1);
+        info(qa >= 0 ? qa : qb, s + 1, ta);
         load(ga, ua, ta);
         settle_all(gb, ub);
         compute(gb, ub, tb);
-        q += kWaves;
-        if (q >= n) break;
+        ++s;
+        if (qa < 0) break;
+        q = qa;
     }
+    return s;
+}
+
+// The static form: local tasks i = wslot, wslot + kWaves, ... < n; info(i, task) describes task i.
+template <int AF, int WF, int NJ, typename Info, typename Out>
+__device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, int n, int wslot, Info info, Out out) {
+    gateup_seq<AF, WF, NJ>(
+        p, xs, [&](int s) { return wslot + kWaves * s < n ? wslot + kWaves * s : -1; },
+        [&](int i, int, GUTask& t) { info(i, t); }, out);
 }
 
 // Routed gate/up rows on the matrix cores, for MXFP4 weights.  The workgroup's tasks are nloc
@@ -968,7 +982,7 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
 // (the last one re-read, so the number of loads in flight is static).  Blocks past H are zeroed.
 // silu(g) * v of row 8 (b + i G) + s of local tile i and the unit's n-th token goes to
 // cst[(8 i + s) * M + n].
-template <int NQ>
+template <int NQ, bool WIDE>
 __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* xs, int nloc,
                                                const LDS uint32_t* s_mask, const LDS int* s_exp, LDS float* cst) {
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -985,9 +999,14 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
     // first flat row of this wave's j-th tile, and its staging slot
     auto tile_row = [&](int j) { return (int64_t)(b + (wave + kWaves * j) * G) * 8; };
     auto tile_slot = [&](int j) { return (wave + kWaves * j) * 8; };
+    // A stage's scale bytes: blocks 4 NQ sg .. 4 NQ sg + 4 NQ - 1 of the row.  When the rows' scale
+    // bytes are 16-byte aligned (H a multiple of 512) they come as NS 16-byte loads from the
+    // aligned dword (NQ sg) & ~3 on, and block 4 (NQ sg + q) + kq is byte kq of dword
+    // ((NQ sg) & 3) + q; otherwise one byte load per block.
+    constexpr int NS = (NQ + 3 + 3) / 4;
     struct Stage {
         u32x4 c[NQ];
-        uint32_t s[NQ];
+        uint32_t s[WIDE ? 4 * NS : NQ];
     };
     auto load = [&](Stage& st, int t) {
         const int j = t / nstage, sg = t - j * nstage;
@@ -1000,19 +1019,46 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
         for (int q = 0; q < NQ; ++q) {
             const int bc = min(4 * (NQ * sg + q) + kq, nblk - 1);
             st.c[q] = __builtin_nontemporal_load((const u32x4*)(w + 16 * bc));
-            st.s[q] = __builtin_nontemporal_load(sc + bc);
+        }
+        if constexpr (WIDE) {
+            const int d0 = (NQ * sg) & ~3;  // first dword of the stage's scales, 16-byte aligned
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const int o = min(4 * d0 + 16 * i, (int)sb - 16);  // in the row (a clamped load is never used)
+                const u32x4 v = __builtin_nontemporal_load((const u32x4*)(sc + o));
+                st.s[4 * i] = v[0];
+                st.s[4 * i + 1] = v[1];
+                st.s[4 * i + 2] = v[2];
+                st.s[4 * i + 3] = v[3];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int bc = min(4 * (NQ * sg + q) + kq, nblk - 1);
+                st.s[q] = __builtin_nontemporal_load(sc + bc);
+            }
         }
     };
     f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
     auto compute = [&](Stage& st, int t) {
         const int j = t / nstage, sg = t - j * nstage;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) asm volatile("" : "+v"(st.c[q]), "+v"(st.s[q]));
+        for (int q = 0; q < NQ; ++q) asm volatile("" : "+v"(st.c[q]));
+#pragma unroll
+        for (int i = 0; i < (WIDE ? 4 * NS : NQ); ++i) asm volatile("" : "+v"(st.s[i]));
+        const int sh = (NQ * sg) & 3;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int blk = 4 * (NQ * sg + q) + kq;
             const bool valid = blk < nblk;
-            const float sc = e8m0_to_f32(valid ? st.s[q] : 127u);
+            uint32_t sbyte;
+            if constexpr (WIDE) {
+                const uint32_t dw = sh == 0 ? st.s[q] : (sh == 1 ? st.s[q + 1] : (sh == 2 ? st.s[q + 2] : st.s[q + 3]));
+                sbyte = (dw >> (8 * kq)) & 0xFFu;
+            } else {
+                sbyte = st.s[q];
+            }
+            const float sc = e8m0_to_f32(valid ? sbyte : 127u);
             const u32x4 c = valid ? st.c[q] : u32x4{0u, 0u, 0u, 0u};
             const LDS char* xp = xrow + 64 * min(blk, nblk - 1);
 #pragma unroll
@@ -1397,13 +1443,6 @@ __device__ __forceinline__ void cost_split(const LDS uint32_t* s_mask, int U, in
 
 // First row of workgroup o's slice of y's columns: [slice0(o), slice0(o + 1)).
 __device__ __forceinline__ int slice0(int H, int G, int o) { return (int)((int64_t)H * o / G); }
-// The workgroup whose slice holds column h.
-__device__ __forceinline__ int slice_of(int H, int G, int h) {
-    int o = (int)(((int64_t)h * G) / H);
-    while (o + 1 < G && slice0(H, G, o + 1) <= h) ++o;
-    while (o > 0 && slice0(H, G, o) > h) --o;
-    return o;
-}
 
 // ------------------------------------------------------------------------------------------
 // the layer kernel
@@ -1465,8 +1504,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     uint32_t* set = p.ws.ctr + (int64_t)(call & 1u) * kSetWords;
     if (b == 0) {
         uint32_t* nxt = p.ws.ctr + (int64_t)((call + 1u) & 1u) * kSetWords;
-        const int nl = kLineOwner0 + G;
-        for (int l = threadIdx.x; l < nl; l += kThreads) line(nxt, l)[0] = 0u;
+        for (int l = threadIdx.x; l < kSetLines; l += kThreads) line(nxt, l)[0] = 0u;
     }
     // router rows (tagged logits: no arrival counter)
     if (wave_id() < nrw) router_rows<AF, NJ>(p, xs, e0, e1, rfirst, call + 1u);
@@ -1540,7 +1578,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             const int ha = (int)(q - (int64_t)u * H);
             const int hb = (int)min<int64_t>(H, ha + (d1 - q));
             q += hb - ha;
-            const int n = (int)min<int64_t>(hb - ha, room / rbI);
+            int n = (int)min<int64_t>(hb - ha, room / rbI);
+            if (n < hb - ha) n = n / RTD * RTD;  // whole down tasks only
             pre_rows[seg] = n;
             pre_off[seg] = (int)(p.dn_bytes - room);
             if (n > 0)
@@ -1551,90 +1590,157 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         for (; seg < kMaxPre; ++seg) pre_rows[seg] = pre_off[seg] = 0;
     }
 
-    // ---- C: routed gate/up.  Tasks of rt consecutive rows of the flattened (unit, row) list are
-    //      dealt to the workgroups round robin; each workgroup stages its results in LDS, writes
-    //      them at the end and counts its rows on one counter ----
+    // ---- C: routed gate/up over the flattened (unit, row) list.  Results are staged in LDS,
+    //      written at the end, and counted on one counter ----
     {
-        const int rt = p.gu_mfma ? 8 : RTG;  // rows per task (whole tasks: I is a multiple of rt)
         const int64_t nrows = (int64_t)U * I;
-        const int nloc = n_strided((int)(nrows / rt), b, G);
-        if (nloc > 0) {
-            bool done = false;
-            if constexpr (WF == MOE_FMT_MXFP4) {
-                if (p.gu_mfma) {
-                    gateup_mfma_mx<10>(p, xs, nloc, s_mask, s_exp, cst);
-                    done = true;
+        int my_rows = 0;
+        if (p.gu_mfma) {
+            // tiles of 8 rows dealt to the workgroups round robin
+            const int nloc = n_strided((int)(nrows / 8), b, G);
+            if constexpr (WF == MOE_FMT_MXFP4)
+                if (nloc > 0) {
+                    if ((H / 32) % 16 == 0)
+                        gateup_mfma_mx<10, true>(p, xs, nloc, s_mask, s_exp, cst);
+                    else
+                        gateup_mfma_mx<10, false>(p, xs, nloc, s_mask, s_exp, cst);
                 }
-            }
-            if (!done) {
-                const int64_t rb = row_bytes<WF>(H);
-                gateup_run<AF, WF, NJ>(
-                    p, xs, nloc, wave_id(),
-                    [&](int i, GUTask& t) {
-                        const int64_t f = (int64_t)(b + i * G) * RTG;  // the task's first flat row
-                        const int u = uni((int)(f / I));
-                        const int64_t e = uni(s_exp[u]);
-                        const int64_t r0 = f - (int64_t)u * I;
-                        t.g = (const uint8_t*)p.w.gate + (e * I + r0) * rb;
-                        t.u = (const uint8_t*)p.w.up + (e * I + r0) * rb;
-                        t.gs = WF == MOE_FMT_MXFP4 ? p.w.gate_s + (e * I + r0) * (H / 32) : nullptr;
-                        t.us = WF == MOE_FMT_MXFP4 ? p.w.up_s + (e * I + r0) * (H / 32) : nullptr;
-                        t.mask = uni(s_mask[u]);
-                        t.slot = i * RTG;
-                    },
-                    [&](int r, int i, float v) { cst[r * M + i] = v; });
-            }
-        }
-        __syncthreads();
-        MOE_TRACE(6);
-        // write the staged SwiGLU rows (slot s: row s % rt of local task s / rt); then count them
-        // once they have landed
-        {
-            const int n = nloc * rt * M;
+            __syncthreads();
+            MOE_TRACE(6);
+            const int n = nloc * 8 * M;
             for (int i = threadIdx.x; i < n; i += kThreads) {
-                const int s = i / M, m = i - s * M;
-                const int64_t f = (int64_t)(b + (s / rt) * G) * rt + s % rt;
+                const int sl = i / M, m = i - sl * M;
+                const int64_t f = (int64_t)(b + (sl / 8) * G) * 8 + sl % 8;
                 const int u = (int)(f / I);
                 if (m < __popc(s_mask[u]))
                     st_dev(p.ws.act + (int64_t)(s_off[u] + m) * p.act_stride + (f - (int64_t)u * I), cst[i]);
             }
+            my_rows = nloc * 8;
+        } else {
+            // Tasks of RTG rows.  Each wave first takes a static share, round robin over the grid
+            // (task b + (w + kWaves s) G at position s < Rs, about 70% of the work); the rest
+            // is handed out in chunks of ch tasks from npool pools of eight workgroups each: some
+            // CUs stream persistently faster than others, and the fast ones take more chunks.  A wave claims its next chunk one chunk ahead, so the atomic's
+            // round trip overlaps the current chunk, and claims only what its staging room holds
+            // (room for twice the average dynamic share, so the pools always drain).  Each wave
+            // logs the task at every position for the write-out.
+            const int T = (int)(nrows / RTG), cap = p.gu_cap, lane = threadIdx.x & 63, w = wave_id();
+            LDS int* qlog = (LDS int*)(cst + (int64_t)kWaves * cap * RTG * M);  // [kWaves][cap]
+            LDS int* nwv = qlog + kWaves * cap;                                 // [kWaves]
+            // below six tasks per wave the chunks' granularity costs more than the balance gains
+            const bool dyn = T >= 6 * kWaves * G;
+            const int Rs = dyn ? (int)(7 * (int64_t)T / (80 * (int64_t)G)) : (T + kWaves * G - 1) / (kWaves * G);
+            const int P0 = dyn ? kWaves * G * Rs : T;
+            // consecutive workgroups sit on different XCDs (round robin), so pool b mod npool
+            // gathers workgroups of one XCD (measured: stealing across XCDs costs more than it
+            // evens out)
+            const int npool = max(1, G / 8), pool = b % npool;
+            const int pa = P0 + (int)((int64_t)(T - P0) * pool / npool);
+            const int pb = P0 + (int)((int64_t)(T - P0) * (pool + 1) / npool);
+            const int64_t rb = row_bytes<WF>(H);
+            const int ch = max(1, (int)(20480 / (2 * RTG * rb)));
+            const int nch = (pb - pa + ch - 1) / ch;
+            uint32_t* pctr = line(set, kLinePoolC0 + pool);
+            bool has_pend = dyn && Rs + ch <= cap;
+            uint32_t pend = 0;
+            if (has_pend && lane == 0) pend = add_dev(pctr, 1u);
+            int cstart = 0;
+            const int n = gateup_seq<AF, WF, NJ>(
+                p, xs,
+                [&](int s) -> int {
+                    int q;
+                    if (s < Rs) {
+                        q = b + (w + kWaves * s) * G;
+                        if (q >= T) return -1;
+                    } else {
+                        const int o = (s - Rs) % ch;
+                        if (o == 0) {
+                            if (!has_pend) return -1;
+                            const int c = __builtin_amdgcn_readlane((int)pend, 0);
+                            has_pend = false;
+                            if (c >= nch) return -1;
+                            cstart = pa + c * ch;
+                            if (s + 2 * ch <= cap) {
+                                has_pend = true;
+                                if (lane == 0) pend = add_dev(pctr, 1u);
+                            }
+                        }
+                        q = cstart + o;
+                        if (q >= pb) return -1;
+                    }
+                    if (lane == 0) qlog[w * cap + s] = q;
+                    return q;
+                },
+                [&](int q, int s, GUTask& t) {
+                    const int64_t f = (int64_t)q * RTG;  // the task's first flat row
+                    const int u = uni((int)(f / I));
+                    const int64_t e = uni(s_exp[u]);
+                    const int64_t r0 = f - (int64_t)u * I;
+                    t.g = (const uint8_t*)p.w.gate + (e * I + r0) * rb;
+                    t.u = (const uint8_t*)p.w.up + (e * I + r0) * rb;
+                    t.gs = WF == MOE_FMT_MXFP4 ? p.w.gate_s + (e * I + r0) * (H / 32) : nullptr;
+                    t.us = WF == MOE_FMT_MXFP4 ? p.w.up_s + (e * I + r0) * (H / 32) : nullptr;
+                    t.mask = uni(s_mask[u]);
+                    t.slot = (w * cap + s) * RTG;
+                },
+                [&](int r, int i, float v) { cst[r * M + i] = v; });
+            if (lane == 0) nwv[w] = n;
+            __syncthreads();
+            MOE_TRACE(6);
+            const int per = cap * RTG * M;  // staged values of one wave
+            for (int i = threadIdx.x; i < kWaves * per; i += kThreads) {
+                const int wv = i / per, rem = i - wv * per;
+                const int sl = rem / M, m = rem - sl * M;
+                const int sp = sl / RTG;
+                if (sp < nwv[wv]) {
+                    const int64_t f = (int64_t)qlog[wv * cap + sp] * RTG + sl % RTG;
+                    const int u = (int)(f / I);
+                    if (m < __popc(s_mask[u]))
+                        st_dev(p.ws.act + (int64_t)(s_off[u] + m) * p.act_stride + (f - (int64_t)u * I), cst[i]);
+                }
+            }
+            for (int wv = 0; wv < kWaves; ++wv) my_rows += nwv[wv] * RTG;
         }
         publish();
         MOE_TRACE(7);
-        if (nloc > 0 && threadIdx.x == 0) add_dev(line(set, kLineRouted), (uint32_t)(nloc * rt));
+        if (my_rows > 0 && threadIdx.x == 0) add_dev(line(set, kLineRouted), (uint32_t)my_rows);
     }
 
     // ---- B': the shared expert's down rows of this slice (weights in LDS) -> ysh [M][nown], while
-    //      the routed units' counters complete ----
+    //      the routed units' counters complete (measured: doing it after the down rows instead,
+    //      on the workgroups that finish gate/up last, is slower) ----
     //      (slice mode: in its down phase, before the wait for the routed units) ----
-    if constexpr (WF != MOE_FMT_F32 && NJD <= 3) {
-        if (has_sh && nown > 0 && mf_sh && !p.slice_mode) {
+    auto shared_down = [&]() {
+        if constexpr (WF != MOE_FMT_F32 && NJD <= 3) {
+            if (has_sh && nown > 0 && mf_sh && !p.slice_mode) {
+                wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
+                const int apitch = 2 * p.act_stride;
+                stage_rows_bf16((LDS char*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is, apitch);
+                __syncthreads();
+                auto unit_of = [&](int, SliceUnit& t) {
+                    t.prow = 0;
+                    t.t = M;
+                    t.K = Is;
+                    t.lds = 1;
+                    t.w = (const uint8_t*)shw;
+                    t.s = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
+                    t.acts = (const LDS char*)xs;
+                };
+                down_slice_mfma<WF, 8 * NJD>(1, 1, 0, nown, apitch, unit_of, []() {}, ysh);
+                __syncthreads();
+            }
+        }
+        if (has_sh && nown > 0 && !p.slice_mode && !mf_sh) {
             wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
-            const int apitch = 2 * p.act_stride;
-            stage_rows_bf16((LDS char*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is, apitch);
+            stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
             __syncthreads();
-            auto unit_of = [&](int, SliceUnit& t) {
-                t.prow = 0;
-                t.t = M;
-                t.K = Is;
-                t.lds = 1;
-                t.w = (const uint8_t*)shw;
-                t.s = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
-                t.acts = (const LDS char*)xs;
-            };
-            down_slice_mfma<WF, 8 * NJD>(1, 1, 0, nown, apitch, unit_of, []() {}, ysh);
+            const uint8_t* dsb = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
+            down_run<WF, NJD, true>((const uint8_t*)shw, dsb, Is, nown, (const LDS float*)xs, M, wave_id(), []() {},
+                                    [&](int row, int i, float v) { ysh[i * nown + row] = v; });
             __syncthreads();
         }
-    }
-    if (has_sh && nown > 0 && !p.slice_mode && !mf_sh) {
-        wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
-        stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
-        __syncthreads();
-        const uint8_t* dsb = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
-        down_run<WF, NJD, true>((const uint8_t*)shw, dsb, Is, nown, (const LDS float*)xs, M, wave_id(), []() {},
-                                [&](int row, int i, float v) { ysh[i * nown + row] = v; });
-        __syncthreads();
-    }
+    };
+    if (has_sh && nown > 0 && !p.slice_mode) shared_down();
     MOE_TRACE(8);
 
     if (p.slice_mode) {
@@ -1779,10 +1885,80 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             need += (int64_t)(hb - ha) * __popc(s_mask[u]);
         }
         const bool once = need <= cap;
+        // The range's segments (one per unit).  When every segment's SwiGLU rows fit the staging
+        // area together and the partials fit at once, the whole range is one task list: one wait,
+        // one staging pass, and the next task's loads stay in flight across segment boundaries.
+        int nseg = 0;
+        int sg_u[kMaxPre], sg_ha[kMaxPre], sg_hb[kMaxPre];
+        bool flat = once;
+        {
+            int64_t abytes = 0;
+            for (int64_t q = d0; q < d1;) {
+                const int u = (int)(q / H);
+                const int ha = (int)(q - (int64_t)u * H);
+                const int hb = (int)min<int64_t>(H, ha + (d1 - q));
+                q += hb - ha;
+                if (nseg == kMaxPre) {
+                    flat = false;
+                    break;
+                }
+                sg_u[nseg] = u;
+                sg_ha[nseg] = ha;
+                sg_hb[nseg] = hb;
+                ++nseg;
+                abytes += (int64_t)__popc(s_mask[u]) * I * 4;
+            }
+            if (abytes > p.lds_cst - p.lds_x) flat = false;
+        }
+        if (flat && nseg > 0) {
+            int toff[kMaxPre + 1], aoff[kMaxPre], poff[kMaxPre];
+            toff[0] = 0;
+            int ao = 0, po = 0;
+            for (int sg = 0; sg < nseg; ++sg) {
+                const int t = __popc(s_mask[sg_u[sg]]);
+                toff[sg + 1] = toff[sg] + (sg_hb[sg] - sg_ha[sg] + RTD - 1) / RTD;
+                aoff[sg] = ao;
+                poff[sg] = po;
+                ao += t * I;  // floats
+                po += (sg_hb[sg] - sg_ha[sg]) * t;
+            }
+            auto info = [&](int n, DNTask& t) {
+                int sg = 0;
+                while (sg + 1 < nseg && n >= toff[sg + 1]) ++sg;
+                const int u = sg_u[sg], ha = sg_ha[sg];
+                const int r0 = ha + (n - toff[sg]) * RTD;
+                const int64_t e = uni(s_exp[u]);
+                t.nrows = min(RTD, sg_hb[sg] - r0);
+                t.t = __popc(uni(s_mask[u]));
+                t.K = I;
+                t.orow = r0 - ha;
+                t.prow = poff[sg];
+                t.lds = r0 - ha < pre_rows[sg] ? 1 : 0;
+                t.w = t.lds ? (const uint8_t*)(dnw + pre_off[sg] + (int64_t)(r0 - ha) * rbI)
+                            : (const uint8_t*)p.w.down + (e * H + r0) * rbI;
+                t.s = WF == MOE_FMT_MXFP4 ? p.w.down_s + (e * H + r0) * (I / 32) : nullptr;
+                t.acts = (const LDS float*)xs + aoff[sg];
+            };
+            auto ready = [&]() {
+                wait_geq(line(set, kLineRouted), (uint32_t)(U * I), p.ws.hdr + kHdrStatus);
+                MOE_TRACE(9);
+                for (int sg = 0; sg < nseg; ++sg) {
+                    const int u = sg_u[sg];
+                    stage_rows<WF != MOE_FMT_F32>((LDS float*)xs + aoff[sg], p.ws.act + (int64_t)s_off[u] * p.act_stride,
+                                                  p.act_stride, __popc(s_mask[u]), I);
+                }
+                __syncthreads();
+                MOE_TRACE(10);
+            };
+            down_flat<WF, NJD>(toff[nseg], I, wave_id(), info, ready, [&](const DNTask& t, int row, int i, float v) {
+                pst[t.prow + (t.orow + row) * t.t + i] = v;
+            });
+            __syncthreads();
+        }
         int pbase = 0;
         int seg = 0;
         bool first = true;
-        for (int64_t q = d0; q < d1; ++seg) {
+        for (int64_t q = flat ? d1 : d0; q < d1; ++seg) {
             const int u = (int)(q / H);
             const int ha = (int)(q - (int64_t)u * H);
             const int hb = (int)min<int64_t>(H, ha + (d1 - q));
@@ -1828,10 +2004,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 if (once) {
                     pbase += (pb - pa) * t;
                 } else {
-                    const int n = (pb - pa) * t;
+                    const int nr = pb - pa, n = nr * t;
                     for (int i = threadIdx.x; i < n; i += kThreads) {
-                        const int rr = i / t, m = i - rr * t;
-                        st_dev(p.ws.part + (int64_t)(row0 + m) * H + pa + rr, pst[i]);
+                        const int m = i / nr, rr = i - m * nr;
+                        st_dev(p.ws.part + (int64_t)(row0 + m) * H + pa + rr, pst[rr * t + m]);
                     }
                     __syncthreads();
                 }
@@ -1846,34 +2022,24 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 q += hb - ha;
                 const int t = __popc(s_mask[u]);
                 const int row0 = s_off[u];
-                const int n = (hb - ha) * t;
-                for (int i = threadIdx.x; i < n; i += kThreads) {
-                    const int rr = i / t, m = i - rr * t;
-                    st_dev(p.ws.part + (int64_t)(row0 + m) * H + ha + rr, pst[base + i]);
+                const int nr = hb - ha, n = nr * t;
+                for (int i = threadIdx.x; i < n; i += kThreads) {  // token-major: contiguous runs of y
+                    const int m = i / nr, rr = i - m * nr;
+                    st_dev(p.ws.part + (int64_t)(row0 + m) * H + ha + rr, pst[base + rr * t + m]);
                 }
                 base += n;
             }
         }
     }
+    MOE_TRACE(15);
     publish();
     MOE_TRACE(11);
-    // count the landed partial rows for the slices they fall in
-    if (threadIdx.x == 0) {
-        for (int64_t q = d0; q < d1;) {
-            const int u = (int)(q / H);
-            const int ha = (int)(q - (int64_t)u * H);
-            const int hb = (int)min<int64_t>(H, ha + (d1 - q));
-            q += hb - ha;
-            for (int o = slice_of(H, G, ha); o < G && slice0(H, G, o) < hb; ++o) {
-                const int a = max(ha, slice0(H, G, o)), c = min(hb, slice0(H, G, o + 1));
-                if (c > a) add_dev(line(set, kLineOwner0 + o), (uint32_t)(c - a));
-            }
-        }
-    }
+    // every slice of y takes partials from most workgroups: one counter of finished workgroups
+    if (threadIdx.x == 0) add_dev(line(set, kLineDownDone), 1u);
 
     // ---- E: combine this workgroup's slice of y ----
     if (nown > 0) {
-        wait_geq(line(set, kLineOwner0 + b), (uint32_t)(U * nown), p.ws.hdr + kHdrStatus);
+        wait_geq(line(set, kLineDownDone), (uint32_t)G, p.ws.hdr + kHdrStatus);
         MOE_TRACE(12);
         const LDS int* s_pair = tab + kTabPair;
         const LDS float* s_roww = (const LDS float*)(tab + kTabRowW);
@@ -1927,12 +2093,26 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     // MXFP4 gate/up rows on the matrix cores: each code is decoded once for all tokens, so the
     // work per weight byte no longer grows with the unit's token count
     p.gu_mfma = WF == MOE_FMT_MXFP4 ? 1 : 0;
-    p.cost_dn = WF == MOE_FMT_MXFP4 ? 8 : (WF == MOE_FMT_BF16 ? 2 : 0);
-    // gate/up tasks of rtg rows are dealt round robin: a workgroup stages at most ceil(T / G) tasks
-    const int64_t rtg = p.gu_mfma ? 8 : rt_gate<WF>();
+    // per-token cost of a down row, from per-workgroup phase timings against each workgroup's rows
+    // and row-tokens: bf16 rows of 5-token units take ~1.6x the time per byte of 1-token rows (the
+    // split-bf16 SwiGLU rows double the dot products), MXFP4 rows are bound by their loads
+    p.cost_dn = WF == MOE_FMT_MXFP4 ? 1 : (WF == MOE_FMT_BF16 ? 4 : 0);
+    // gate/up staging: MXFP4 tiles of 8 rows dealt round robin (at most ceil(T / G) per workgroup);
+    // otherwise per wave the static share plus up to twice the average dynamic share (the split
+    // the kernel makes from the actual number of units, bounded here by its maximum)
     const int64_t units = std::min<int64_t>(NP, p.E);
-    const int64_t c_tasks = (units * p.I / rtg + G - 1) / G;
-    int64_t cst = std::max<int64_t>(kSelBytes, c_tasks * rtg * M * 4);
+    int64_t cst;
+    if (p.gu_mfma) {
+        cst = std::max<int64_t>(kSelBytes, (units * p.I / 8 + G - 1) / G * 8 * M * 4);
+        p.gu_cap = 0;
+    } else {
+        const int64_t rtg = rt_gate<WF>();
+        const int64_t T = units * p.I / rtg;
+        const int64_t Rs = 7 * T / (80 * (int64_t)G), dyn = T - (int64_t)kWaves * G * Rs;
+        const int64_t ch = std::max<int64_t>(1, 20480 / (2 * rtg * row_bytes<WF>(H)));
+        p.gu_cap = (int)(Rs + 2 * ((dyn + kWaves * G - 1) / (kWaves * G)) + 2 * ch + 5);
+        cst = std::max<int64_t>(kSelBytes, (int64_t)kWaves * p.gu_cap * (rtg * M * 4 + 4) + kWaves * 4);
+    }
     cst = std::max<int64_t>(cst, p.slice_mode ? (NP + M) * nown * 4 : 16 * 1024);
     // token rows 16 bytes further apart than their size: the 16 token columns of a matrix-core B
     // operand then start in 16 different bank groups
