@@ -1617,8 +1617,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             }
             my_rows = nloc * 8;
         } else {
-            // Tasks of RTG rows.  Each wave first takes a static share, round robin over the grid
-            // (task b + (w + kWaves s) G at position s < Rs, about 70% of the work); the rest
+            // Tasks of RTG rows.  Each wave first takes a static share (about 70% of the work); the rest
             // is handed out in chunks of ch tasks from npool pools of eight workgroups each: some
             // CUs stream persistently faster than others, and the fast ones take more chunks.  A wave claims its next chunk one chunk ahead, so the atomic's
             // round trip overlaps the current chunk, and claims only what its staging room holds
@@ -1631,6 +1630,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             const bool dyn = T >= 6 * kWaves * G;
             const int Rs = dyn ? (int)(7 * (int64_t)T / (80 * (int64_t)G)) : (T + kWaves * G - 1) / (kWaves * G);
             const int P0 = dyn ? kWaves * G * Rs : T;
+            // this workgroup's static tasks: a contiguous range of the static part, dealt to its
+            // waves round robin (consecutive rows: whole DRAM pages, contiguous write-out)
+            const int sa = (int)((int64_t)P0 * b / G), sbnd = (int)((int64_t)P0 * (b + 1) / G);
+            const int ns = n_strided(sbnd - sa, w, kWaves);  // static positions of this wave
             // consecutive workgroups sit on different XCDs (round robin), so pool b mod npool
             // gathers workgroups of one XCD (measured: stealing across XCDs costs more than it
             // evens out)
@@ -1641,7 +1644,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             const int ch = max(1, (int)(20480 / (2 * RTG * rb)));
             const int nch = (pb - pa + ch - 1) / ch;
             uint32_t* pctr = line(set, kLinePoolC0 + pool);
-            bool has_pend = dyn && Rs + ch <= cap;
+            bool has_pend = dyn && ns + ch <= cap;
             uint32_t pend = 0;
             if (has_pend && lane == 0) pend = add_dev(pctr, 1u);
             int cstart = 0;
@@ -1649,11 +1652,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 p, xs,
                 [&](int s) -> int {
                     int q;
-                    if (s < Rs) {
-                        q = b + (w + kWaves * s) * G;
-                        if (q >= T) return -1;
+                    if (s < ns) {
+                        q = sa + w + kWaves * s;
                     } else {
-                        const int o = (s - Rs) % ch;
+                        const int o = (s - ns) % ch;
                         if (o == 0) {
                             if (!has_pend) return -1;
                             const int c = __builtin_amdgcn_readlane((int)pend, 0);
@@ -2075,9 +2077,12 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     const int64_t NP = (int64_t)p.k * M;
     const int ka = std::max(p.I, p.Is);
     const int nown = (H + G - 1) / G;
-    // slice mode (each workgroup finishes its own y columns of every unit) while M * k is small:
+    // slice mode (each workgroup finishes its own y columns of every unit) while M * k is small,
+    // and for MXFP4 weights while all pair rows' SwiGLU outputs fit in LDS as bfloat16 (the slices'
+    // 4-bit down rows mostly fit the LDS window; no partial write-out, no down barrier):
     // then every workgroup stages all pair rows' SwiGLU outputs; otherwise unit-major down rows
-    p.slice_mode = NP <= 16 ? 1 : 0;
+    const bool mx_slice = WF == MOE_FMT_MXFP4 && NJD <= 3 && nown <= 16 && (NP + M) * ka * 2 <= 96 * 1024;
+    p.slice_mode = (NP <= 16 || mx_slice) ? 1 : 0;
     // from three tokens on, the M * E logits that every workgroup would read are more polling traffic
     // than one extra hand-off costs: workgroup m selects token m's experts and publishes them
     p.route_delegate = (!p.route_only && M >= 3 && M <= G) ? 1 : 0;
