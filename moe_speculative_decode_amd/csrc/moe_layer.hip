@@ -1448,8 +1448,11 @@ __device__ __forceinline__ int slice0(int H, int G, int o) { return (int)((int64
 // the layer kernel
 // ------------------------------------------------------------------------------------------
 
-template <int AF, int WF, int NJ, int NJD>
+// SL: 1 for slice mode (the down rows of each workgroup's own y columns), 0 for unit-major down
+// rows; one instance per mode keeps each kernel's code to the path it runs.
+template <int AF, int WF, int NJ, int NJD, int SL>
 __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
+    constexpr bool SLICE = SL != 0;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int G = gridDim.x, b = blockIdx.x;
     const int H = p.H, E = p.E, M = p.M, k = p.k, I = p.I, Is = p.Is;
@@ -1555,11 +1558,11 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     // ---- start streaming this workgroup's routed down rows into LDS (as far as the window goes):
     //      slice mode: rows [h0, h1) of every unit; otherwise an equal share of all units' rows ----
     int64_t d0 = 0, d1 = 0;  // unit-major: this workgroup's (unit, row) range, split by cost
-    if (!p.slice_mode) cost_split(s_mask, U, H, kCostBase, p.cost_dn, G, b, &d0, &d1);
+    if constexpr (!SLICE) cost_split(s_mask, U, H, kCostBase, p.cost_dn, G, b, &d0, &d1);
     int pre_rows[kMaxPre];
     int pre_off[kMaxPre];
     int nfit = 0;  // slice mode: units whose slice rows are in the window
-    if (p.slice_mode) {
+    if constexpr (SLICE) {
         if (nown > 0) {
             nfit = min(U, (int)(p.dn_bytes / (nown * rbI)));
             for (int u = 0; u < nfit; ++u) {
@@ -1714,7 +1717,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     //      (slice mode: in its down phase, before the wait for the routed units) ----
     auto shared_down = [&]() {
         if constexpr (WF != MOE_FMT_F32 && NJD <= 3) {
-            if (has_sh && nown > 0 && mf_sh && !p.slice_mode) {
+            if (has_sh && nown > 0 && mf_sh && !SLICE) {
                 wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
                 const int apitch = 2 * p.act_stride;
                 stage_rows_bf16((LDS char*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is, apitch);
@@ -1732,7 +1735,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 __syncthreads();
             }
         }
-        if (has_sh && nown > 0 && !p.slice_mode && !mf_sh) {
+        if (has_sh && nown > 0 && !SLICE && !mf_sh) {
             wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
             stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
             __syncthreads();
@@ -1742,10 +1745,11 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             __syncthreads();
         }
     };
-    if (has_sh && nown > 0 && !p.slice_mode) shared_down();
+    if constexpr (!SLICE)
+        if (has_sh && nown > 0) shared_down();
     MOE_TRACE(8);
 
-    if (p.slice_mode) {
+    if constexpr (SLICE) {
         // ---- D (slice mode): rows [h0, h1) of every routed unit and of the shared expert, as one
         //      flattened task list (units past the LDS window first, so their loads are in flight
         //      during the waits); every pair row's SwiGLU output is staged once; partial outputs
@@ -2070,7 +2074,6 @@ int round16(int64_t v) { return (int)((v + 15) / 16 * 16); }
 
 template <int AF, int WF, int NJ, int NJD>
 hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
-    auto kern = k_layer<AF, WF, NJ, NJD>;
     constexpr int XB = AF == MOE_FMT_F32 ? 4 : 2;
     const int G = std::min(num_cus, kMaxGrid);
     const int M = p.M, H = p.H;
@@ -2135,13 +2138,16 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     p.dn_bytes = p.route_only ? 0 : std::max(0, (budget - p.lds_dn) / 16 * 16);
     p.lds_total = p.lds_dn + p.dn_bytes;
     if (p.lds_total > budget) return hipErrorInvalidConfiguration;
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_total);
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, kThreads, p.lds_total) != hipSuccess)
-        return hipErrorInvalidValue;
-    if (occ < 1) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), p.lds_total, s, p);
-    return hipGetLastError();
+    auto go = [&](auto kern) -> hipError_t {
+        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_total);
+        int occ = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, kThreads, p.lds_total) != hipSuccess)
+            return hipErrorInvalidValue;
+        if (occ < 1) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), p.lds_total, s, p);
+        return hipGetLastError();
+    };
+    return p.slice_mode ? go(k_layer<AF, WF, NJ, NJD, 1>) : go(k_layer<AF, WF, NJ, NJD, 0>);
 }
 
 // chunks per lane: NJ for the router and gate/up rows (K = H), NJD for the down rows (K = I, Is)
