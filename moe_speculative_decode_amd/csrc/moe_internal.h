@@ -21,9 +21,10 @@ constexpr int kLdsBytes = 160 * 1024;     // LDS of one CU (gfx950)
 // (c + 1) & 1, which the previous call used and the next call will use.
 constexpr int kLineWords = 64;
 constexpr int kLineShared = 0;                            // shared-expert SwiGLU rows finished
-constexpr int kLineRouted = 1;                            // routed SwiGLU rows finished (all units)
+constexpr int kRoutedStripes = 8;                         // routed-row counter lines (atomics spread)
+constexpr int kLineRouted = 1;                            // [kRoutedStripes] routed SwiGLU rows finished
 constexpr int kMaxPools = kMaxGrid / 8;                   // work pools: one per 8 workgroups
-constexpr int kLinePoolC0 = 2;                            // [kMaxPools] gate/up chunks handed out
+constexpr int kLinePoolC0 = kLineRouted + kRoutedStripes; // [kMaxPools] gate/up chunks handed out
 constexpr int kLinePoolD0 = kLinePoolC0 + kMaxPools;      // [kMaxPools] down chunks handed out
 constexpr int kLineDownDone = kLinePoolD0 + kMaxPools;    // workgroups whose down partials have landed
 constexpr int kSetLines = kLineDownDone + 1;

@@ -398,15 +398,25 @@ __device__ __forceinline__ void wait_geq(const uint32_t* c, uint32_t target, uin
 }
 __device__ __forceinline__ uint32_t* line(uint32_t* set, int l) { return set + (int64_t)l * kLineWords; }
 
-// Every wave of the workgroup continues once the routed SwiGLU row counter has reached `target`
-// and the shared expert's counter `sh_target` (bounded).
+// Routed SwiGLU rows landed so far: the sum of the counter's stripes (each workgroup adds to
+// stripe b mod kRoutedStripes, so 256 atomics do not queue on one address).  Uniform in the wave.
+__device__ __forceinline__ uint32_t routed_rows(uint32_t* set) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t v = lane < kRoutedStripes ? ld_dev(line(set, kLineRouted + lane)) : 0u;
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < kRoutedStripes; ++i) sum += (uint32_t)__builtin_amdgcn_readlane((int)v, i);
+    return sum;
+}
+// Every wave of the workgroup continues once the routed SwiGLU rows have reached `target` and the
+// shared expert's counter `sh_target` (bounded).
 __device__ __forceinline__ void wait_units(uint32_t* set, uint32_t target, uint32_t sh_target, uint32_t* status) {
     if (wave_id() == 0) {
         const int lane = threadIdx.x & 63;
         for (int it = 0;; ++it) {
-            bool ok = true;
-            if (lane == 0) ok = ld_dev(line(set, kLineShared)) >= sh_target;
-            if (lane == 1) ok = ld_dev(line(set, kLineRouted)) >= target;
+            const uint32_t rr = routed_rows(set);  // every lane takes part
+            bool ok = rr >= target;
+            if (lane == 0) ok = ok && ld_dev(line(set, kLineShared)) >= sh_target;
             if (__ballot(!ok) == 0ull) break;
             if (it >= kSpinLimit) {
                 if (lane == 0) atomicOr(status, kStatusTimeout);
@@ -1521,12 +1531,13 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     //      results go straight to the workspace and are counted after the routing barrier ----
     int sh_rows = 0;
     if (has_sh && !p.route_only) {
-        const int nsh = n_strided(Is / RTG, b, G);  // tasks b, b + G, b + 2G, ...
-        sh_rows = nsh * RTG;
+        const int T = Is / RTG;  // a contiguous range of tasks per workgroup
+        const int qa = (int)((int64_t)T * b / G), qb = (int)((int64_t)T * (b + 1) / G);
+        sh_rows = (qb - qa) * RTG;
         gateup_run<AF, WF, NJ>(
-            p, xs, nsh, kWaves - 1 - wave_id(),
+            p, xs, qb - qa, kWaves - 1 - wave_id(),
             [&](int i, GUTask& t) {
-                const int64_t r0 = (int64_t)(b + i * G) * RTG;
+                const int64_t r0 = (int64_t)(qa + i) * RTG;
                 t.g = (const uint8_t*)p.w.sh_gate + r0 * row_bytes<WF>(H);
                 t.u = (const uint8_t*)p.w.sh_up + r0 * row_bytes<WF>(H);
                 t.gs = WF == MOE_FMT_MXFP4 ? p.w.sh_gate_s + r0 * (H / 32) : nullptr;
@@ -1708,7 +1719,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         }
         publish();
         MOE_TRACE(7);
-        if (my_rows > 0 && threadIdx.x == 0) add_dev(line(set, kLineRouted), (uint32_t)my_rows);
+        if (my_rows > 0 && threadIdx.x == 0) add_dev(line(set, kLineRouted + b % kRoutedStripes), (uint32_t)my_rows);
     }
 
     // ---- B': the shared expert's down rows of this slice (weights in LDS) -> ysh [M][nown], while
@@ -1946,7 +1957,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 t.acts = (const LDS float*)xs + aoff[sg];
             };
             auto ready = [&]() {
-                wait_geq(line(set, kLineRouted), (uint32_t)(U * I), p.ws.hdr + kHdrStatus);
+                wait_units(set, (uint32_t)(U * I), 0u, p.ws.hdr + kHdrStatus);
                 MOE_TRACE(9);
                 for (int sg = 0; sg < nseg; ++sg) {
                     const int u = sg_u[sg];
@@ -1980,7 +1991,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 const int pb = min(hb, pa + rows_per_pass);
                 auto ready = [&]() {
                     if (!staged) {
-                        wait_geq(line(set, kLineRouted), (uint32_t)(U * I), p.ws.hdr + kHdrStatus);
+                        wait_units(set, (uint32_t)(U * I), 0u, p.ws.hdr + kHdrStatus);
                         if (first) MOE_TRACE(9);
                         stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)row0 * p.act_stride, p.act_stride, t, I);
                         __syncthreads();
