@@ -2112,10 +2112,10 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     // MXFP4 gate/up rows on the matrix cores: each code is decoded once for all tokens, so the
     // work per weight byte no longer grows with the unit's token count
     p.gu_mfma = WF == MOE_FMT_MXFP4 ? 1 : 0;
-    // per-token cost of a down row, from per-workgroup phase timings against each workgroup's rows
-    // and row-tokens: bf16 rows of 5-token units take ~1.6x the time per byte of 1-token rows (the
-    // split-bf16 SwiGLU rows double the dot products), MXFP4 rows are bound by their loads
-    p.cost_dn = WF == MOE_FMT_MXFP4 ? 1 : (WF == MOE_FMT_BF16 ? 4 : 0);
+    // per-token cost of a down row (a row's bytes cost kCostBase = 8): bf16 from a sweep of the
+    // whole-layer time over 0, 1, 2, 4 and 6 at 6 and 16 tokens (2 is fastest at both); MXFP4 rows
+    // are bound by their loads
+    p.cost_dn = WF == MOE_FMT_MXFP4 ? 1 : (WF == MOE_FMT_BF16 ? 2 : 0);
     // gate/up staging: MXFP4 tiles of 8 rows dealt round robin (at most ceil(T / G) per workgroup);
     // otherwise per wave the static share plus up to twice the average dynamic share (the split
     // the kernel makes from the actual number of units, bounded here by its maximum)
