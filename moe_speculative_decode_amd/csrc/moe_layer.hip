@@ -870,6 +870,7 @@ struct GUTask {
     const uint8_t* us;
     uint32_t mask;      // the unit's tokens
     int slot;           // staging row of the task's first row
+    int dummy;          // 1: a stand-in for the prefetch after the last task (one chunk, every lane)
 };
 
 // This wave's gate/up tasks, in the order next(0), next(1), ... until next returns -1 (called once
@@ -893,10 +894,10 @@ __device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, N
     auto load = [&](Chunk(&g)[RL][NJ], Chunk(&u)[RL][NJ], const GUTask& t) {
 #pragma unroll
         for (int rl = 0; rl < RL; ++rl) {
-            const int64_t ro = gi * RL + rl;
+            const int64_t ro = t.dummy ? 0 : gi * RL + rl;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int c = min(sl + LPR * j, nch - 1);
+                const int c = t.dummy ? 0 : min(sl + LPR * j, nch - 1);
                 ld_chunk<WF>(g[rl][j], t.g + ro * rb, t.gs + ro * sb, c);
                 ld_chunk<WF>(u[rl][j], t.u + ro * rb, t.us + ro * sb, c);
             }
@@ -947,12 +948,16 @@ __device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, N
             }
         }
     };
+    // the prefetch after the last task stays unconditional (a static number of loads in flight) but
+    // reads one chunk of the current task's first row in every lane: one cache line, not a task
     int s = 0;
     info(q, 0, ta);
+    ta.dummy = 0;
     load(ga, ua, ta);
     while (true) {
         const int qb = next(s + 1);
         info(qb >= 0 ? qb : q, s + 1, tb);
+        tb.dummy = qb < 0;
         load(gb, ub, tb);
         settle_all(ga, ua);
         compute(ga, ua, ta);
@@ -960,6 +965,7 @@ __device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, N
         if (qb < 0) break;
         const int qa = next(s + 1);
         info(qa >= 0 ? qa : qb, s + 1, ta);
+        ta.dummy = qa < 0;
         load(ga, ua, ta);
         settle_all(gb, ub);
         compute(gb, ub, tb);
@@ -1018,23 +1024,27 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
         u32x4 c[NQ];
         uint32_t s[WIDE ? 4 * NS : NQ];
     };
+    // t == nsteps: the stand-in prefetch after the last stage (static loads in flight): every lane
+    // reads the first block of the last tile's first row, one cache line
     auto load = [&](Stage& st, int t) {
+        const bool dummy = t >= nsteps;
+        t = min(t, nsteps - 1);
         const int j = t / nstage, sg = t - j * nstage;
-        const int64_t f = tile_row(j) + (r & 7);
+        const int64_t f = tile_row(j) + (dummy ? 0 : (r & 7));
         const int u = (int)(f / I);
         const int64_t row = (int64_t)s_exp[u] * I + (f - (int64_t)u * I);
-        const uint8_t* w = mat + row * rb;
-        const uint8_t* sc = mats + row * sb;
+        const uint8_t* w = (dummy ? (const uint8_t*)p.w.gate : mat) + row * rb;
+        const uint8_t* sc = (dummy ? p.w.gate_s : mats) + row * sb;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const int bc = min(4 * (NQ * sg + q) + kq, nblk - 1);
+            const int bc = dummy ? 0 : min(4 * (NQ * sg + q) + kq, nblk - 1);
             st.c[q] = __builtin_nontemporal_load((const u32x4*)(w + 16 * bc));
         }
         if constexpr (WIDE) {
             const int d0 = (NQ * sg) & ~3;  // first dword of the stage's scales, 16-byte aligned
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
-                const int o = min(4 * d0 + 16 * i, (int)sb - 16);  // in the row (a clamped load is never used)
+                const int o = dummy ? 0 : min(4 * d0 + 16 * i, (int)sb - 16);  // in the row (a clamped load is never used)
                 const u32x4 v = __builtin_nontemporal_load((const u32x4*)(sc + o));
                 st.s[4 * i] = v[0];
                 st.s[4 * i + 1] = v[1];
@@ -1107,10 +1117,10 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
     load(sa, 0);
     int t = 0;
     while (true) {
-        load(sb2, min(t + 1, nsteps - 1));
+        load(sb2, t + 1);
         compute(sa, t);
         if (++t >= nsteps) break;
-        load(sa, min(t + 1, nsteps - 1));
+        load(sa, t + 1);
         compute(sb2, t);
         if (++t >= nsteps) break;
     }
