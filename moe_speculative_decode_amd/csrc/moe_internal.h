@@ -76,6 +76,8 @@ struct Params {
     float* topk_w;
     moe_dispatch_t disp;
     Workspace ws;
+    int lds_scl;         // MXFP4: LDS scale windows (shared expert, then routed units) at this offset,
+    int scl_sh, scl_rt;  // of these sizes in bytes (0: none)
 };
 
 // Enqueues one call.

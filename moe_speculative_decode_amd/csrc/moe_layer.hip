@@ -443,6 +443,18 @@ __device__ __forceinline__ void async_to_lds(char* lds, const uint8_t* src, int 
     }
 }
 
+// The same with 4-byte pieces, for n bytes (a multiple of 4) from a 4-byte aligned source.
+__device__ __forceinline__ void async_dwords_to_lds(char* lds, const uint8_t* src, int n) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    constexpr int chunk = 64 * 4;
+    for (int base = wave * chunk; base < n; base += kWaves * chunk) {
+        if (base + lane * 4 < n) {
+            auto* dst = (LDS void*)(lds + base);
+            __builtin_amdgcn_global_load_lds(src + base + lane * 4, dst, 4, 0, 0);
+        }
+    }
+}
+
 // The same for nrows rows of rb bytes (a multiple of 16) that land `pitch` bytes apart in LDS.
 __device__ __forceinline__ void async_rows_pitch(char* lds, const uint8_t* src, int nrows, int rb, int pitch) {
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -1300,6 +1312,7 @@ __device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Inf
 struct SliceUnit {
     const uint8_t* w;
     const uint8_t* s;        // MXFP4 scales of row 0 (global memory)
+    const LDS uint8_t* sl;   // the same scales copied into LDS, or null
     const LDS char* acts;
     int lds, K, t, prow;
 };
@@ -1353,7 +1366,16 @@ __device__ __forceinline__ void down_slice_mfma(int nun, int npre, int ng, int n
                 else
                     a[i].c = __builtin_nontemporal_load((const uint32_t*)(row + k0 / 2));
             }
-            if constexpr (WF == MOE_FMT_MXFP4) a[i].s = u.s[rr * (u.K / 32) + k0 / 32];
+        }
+        if constexpr (WF == MOE_FMT_MXFP4) {
+            // scale bytes: from the LDS copy when there is one (no global round trip per unit)
+            if (u.sl) {
+#pragma unroll
+                for (int i = 0; i < KB; ++i) a[i].s = u.sl[rr * (u.K / 32) + min(32 * i + 8 * kq, u.K - 8) / 32];
+            } else {
+#pragma unroll
+                for (int i = 0; i < KB; ++i) a[i].s = u.s[rr * (u.K / 32) + min(32 * i + 8 * kq, u.K - 8) / 32];
+            }
         }
     };
     auto a_operand = [&](int i) {
@@ -1488,6 +1510,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     LDS char* shw = lds + p.lds_sh;
     LDS float* ysh = (LDS float*)(lds + p.lds_ysh);
     LDS char* dnw = lds + p.lds_dn;
+    // MXFP4 scales of the slice rows in LDS (the shared expert's, and the routed units' in slice
+    // mode), or null
+    const LDS uint8_t* sclw_sh = WF == MOE_FMT_MXFP4 && p.scl_sh ? (const LDS uint8_t*)(lds + p.lds_scl) : nullptr;
+    const LDS uint8_t* sclw = WF == MOE_FMT_MXFP4 && p.scl_rt ? (const LDS uint8_t*)(lds + p.lds_scl) + p.scl_sh : nullptr;
     __shared__ uint32_t s_call;
     MOE_TRACE_INIT;
     MOE_TRACE(0);
@@ -1519,6 +1545,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             async_rows_to_lds((char*)shw, (const uint8_t*)p.w.sh_down + h0 * rbIs, (int)(nown * rbIs), (int)rbIs);
         else
             async_to_lds((char*)shw, (const uint8_t*)p.w.sh_down + h0 * rbIs, (int)(nown * rbIs));
+        if (sclw_sh)
+            async_dwords_to_lds((char*)sclw_sh, p.w.sh_down_s + (int64_t)h0 * (Is / 32), nown * (Is / 32));
     }
     __builtin_amdgcn_s_waitcnt(0);  // token rows (and the slice's shared down rows) in LDS
     __syncthreads();
@@ -1593,6 +1621,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 else
                     async_to_lds((char*)(dnw + (int64_t)u * nown * rbI), src, (int)(nown * rbI));
             }
+            if (sclw)
+                for (int u = 0; u < U; ++u)
+                    async_dwords_to_lds((char*)(sclw + (int64_t)u * nown * (I / 32)),
+                                        p.w.down_s + ((int64_t)s_exp[u] * H + h0) * (I / 32), nown * (I / 32));
         }
     } else {
         int64_t room = p.dn_bytes;
@@ -1740,7 +1772,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         if constexpr (WF != MOE_FMT_F32 && NJD <= 3) {
             if (has_sh && nown > 0 && mf_sh && !SLICE) {
                 wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
-                const int apitch = 2 * p.act_stride;
+                const int apitch = 2 * p.act_stride + 16;  // rows 4 banks apart: no conflicts among the B columns
                 stage_rows_bf16((LDS char*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is, apitch);
                 __syncthreads();
                 auto unit_of = [&](int, SliceUnit& t) {
@@ -1750,6 +1782,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     t.lds = 1;
                     t.w = (const uint8_t*)shw;
                     t.s = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
+                    if constexpr (WF == MOE_FMT_MXFP4) t.sl = sclw_sh;
                     t.acts = (const LDS char*)xs;
                 };
                 down_slice_mfma<WF, 8 * NJD>(1, 1, 0, nown, apitch, unit_of, []() {}, ysh);
@@ -1816,7 +1849,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             if constexpr (WF != MOE_FMT_F32 && NJD <= 3) {
                 if (mf_slice) {
                     // matrix-core path: SwiGLU rows staged as bfloat16, one wave per unit
-                    const int apitch = 2 * astride;
+                    const int apitch = 2 * astride + 16;  // rows 4 banks apart: no conflicts among the B columns
                     const int nsh = has_sh ? 1 : 0;  // the shared unit first: it needs no wait
                     if (has_sh) {
                         wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
@@ -1836,6 +1869,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                             t.w = t.lds ? (const uint8_t*)(dnw + (int64_t)u * nown * rbI)
                                         : (const uint8_t*)p.w.down + (e * H + h0) * rbI;
                             t.s = WF == MOE_FMT_MXFP4 ? p.w.down_s + (e * H + h0) * (I / 32) : nullptr;
+                            if constexpr (WF == MOE_FMT_MXFP4) t.sl = sclw ? sclw + (int64_t)u * nown * (I / 32) : nullptr;
                         } else {
                             t.prow = NP;
                             t.t = M;
@@ -1843,6 +1877,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                             t.lds = 1;
                             t.w = (const uint8_t*)shw;
                             t.s = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
+                            if constexpr (WF == MOE_FMT_MXFP4) t.sl = sclw_sh;
                         }
                         t.acts = (const LDS char*)xs + (int64_t)t.prow * apitch;
                     };
@@ -2105,7 +2140,7 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     // and for MXFP4 weights while all pair rows' SwiGLU outputs fit in LDS as bfloat16 (the slices'
     // 4-bit down rows mostly fit the LDS window; no partial write-out, no down barrier):
     // then every workgroup stages all pair rows' SwiGLU outputs; otherwise unit-major down rows
-    const bool mx_slice = WF == MOE_FMT_MXFP4 && NJD <= 3 && nown <= 16 && (NP + M) * ka * 2 <= 96 * 1024;
+    const bool mx_slice = WF == MOE_FMT_MXFP4 && NJD <= 3 && nown <= 16 && (NP + M) * (ka * 2 + 16) <= 96 * 1024;
     p.slice_mode = (NP <= 16 || mx_slice) ? 1 : 0;
     // from three tokens on, the M * E logits that every workgroup would read are more polling traffic
     // than one extra hand-off costs: workgroup m selects token m's experts and publishes them
@@ -2147,14 +2182,22 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     // operand then start in 16 different bank groups
     p.xpitch = H * XB + 16;
     int64_t xb = std::max<int64_t>((int64_t)M * p.xpitch, (int64_t)M * ka * 4);
-    if (p.slice_mode) xb = std::max<int64_t>(xb, (NP + M) * ka * (p.slice_mfma ? 2 : 4));
+    if (p.slice_mode) xb = std::max<int64_t>(xb, (NP + M) * (p.slice_mfma ? 2 * ka + 16 : 4 * ka));
     p.lds_tab = 0;
     p.lds_x = round16(kTabWords * 4);
     p.lds_cst = p.lds_x + round16(xb);
     p.cst_bytes = round16(cst);
     p.lds_sh = p.lds_cst + p.cst_bytes;
     p.lds_ysh = p.lds_sh + round16(p.Is > 0 ? nown * row_bytes<WF>(p.Is) : 0);
-    p.lds_dn = p.lds_ysh + round16((int64_t)M * nown * 4);
+    p.lds_scl = p.lds_ysh + round16((int64_t)M * nown * 4);
+    // MXFP4 scales of the slice rows in LDS (copied in 4-byte pieces: whole dwords per row block):
+    // the shared expert's when its down rows run on the matrix cores, the routed units' in slice mode
+    p.scl_sh = p.scl_rt = 0;
+    if constexpr (WF == MOE_FMT_MXFP4) if (!p.route_only) {
+        if (p.sh_mfma && p.Is > 0 && (p.Is / 32) % 4 == 0) p.scl_sh = (int)round16((int64_t)nown * (p.Is / 32));
+        if (p.slice_mfma && (p.I / 32) % 4 == 0) p.scl_rt = (int)round16(units * nown * (p.I / 32));
+    }
+    p.lds_dn = p.lds_scl + p.scl_sh + p.scl_rt;
     const int budget = kLdsBytes - 512;  // room for the static LDS variables
     p.dn_bytes = p.route_only ? 0 : std::max(0, (budget - p.lds_dn) / 16 * 16);
     p.lds_total = p.lds_dn + p.dn_bytes;
