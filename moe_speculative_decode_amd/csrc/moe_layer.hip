@@ -9,20 +9,23 @@
 // result runs before the routing barrier:
 //
 //   A  stage the token rows in LDS and copy this workgroup's slice of the shared expert's down
-//      rows into LDS; compute this workgroup's router rows (fp32 logits) and arrive at the
-//      routing barrier; compute a share of the shared expert's gate/up rows.
-//   B  wait for the routing barrier; every workgroup redoes the per-token top-k and the batch
-//      compaction (distinct experts ascending, token bitmask and pair rows per unit) in its own
-//      LDS, so no second hand-off is needed; workgroup 0 writes the caller-visible outputs.
-//      Then the shared expert's down rows of this workgroup's y slice, from LDS.
-//   C  an equal share of all routed units' gate/up rows: each weight row is read once and
-//      applied to every token of its unit, silu(g) * v in fp32.  Meanwhile as many of this
-//      workgroup's routed down rows as fit stream into LDS.
-//   D  an equal share of all routed units' down rows, writing fp32 partial outputs per pair row
-//      once the unit's SwiGLU rows are complete.
-//   E  every workgroup owns a fixed slice of y's columns: once all routed partials of the slice
-//      have landed it sums each token's partials in slot order, adds the shared expert and
-//      casts once.
+//      rows into LDS; compute this workgroup's router rows (tagged fp32 logits); compute a share
+//      of the shared expert's gate/up rows.
+//   B  routing: below three tokens every workgroup redoes the per-token top-k from the tagged
+//      logits; from three tokens on workgroup m selects token m's experts and publishes them as
+//      tagged words that every workgroup reads.  Each workgroup builds the batch compaction
+//      (distinct experts ascending, token bitmask and pair rows per unit) in its own LDS;
+//      workgroup 0 writes the caller-visible outputs.
+//   C  all routed units' gate/up rows: each weight row is read once and applied to every token of
+//      its unit, silu(g) * v in fp32 (bf16 weights on the vector ALU, a static share and then
+//      chunks from per-XCD pools; MXFP4 weights on the matrix cores).  Meanwhile as many of this
+//      workgroup's down rows as fit stream into LDS.
+//   D  slice mode (few pair rows, or MXFP4 rows that fit): every workgroup computes its own y
+//      columns of every unit on the matrix cores from LDS; otherwise a cost-weighted share of
+//      all units' down rows as one task list, fp32 partial outputs per pair row.
+//   E  every workgroup owns a fixed slice of y's columns: it sums each token's partials in slot
+//      order (slice mode: from LDS; otherwise once every workgroup's partials have landed),
+//      adds the shared expert and casts once.
 //
 // The streaming loops never store to global memory: vector memory operations retire in order
 // on gfx9, so a store in the loop would make the next wait for prefetched weights also wait
