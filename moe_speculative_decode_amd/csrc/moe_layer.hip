@@ -1614,9 +1614,14 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     int pre_rows[kMaxPre];
     int pre_off[kMaxPre];
     int nfit = 0;  // slice mode: units whose slice rows are in the window
-    if constexpr (SLICE) {
+    // slice mode on the matrix cores: the window streams in after this workgroup's gate/up rows
+    // have been published (during the wait for the other workgroups): issued before them, it would
+    // sit ahead of the gate/up loads in every wave's in-order memory counter and delay the whole
+    // phase (bf16: -0.8 us at one token; the 4-bit MXFP4 window is small and gains nothing).  The
+    // vector slice path loads its first window task before its wait, so its window is issued here,
+    // before C.
+    auto slice_window = [&]() {
         if (nown > 0) {
-            nfit = min(U, (int)(p.dn_bytes / (nown * rbI)));
             for (int u = 0; u < nfit; ++u) {
                 const uint8_t* src = (const uint8_t*)p.w.down + ((int64_t)s_exp[u] * H + h0) * rbI;
                 if (mf_slice)
@@ -1629,6 +1634,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     async_dwords_to_lds((char*)(sclw + (int64_t)u * nown * (I / 32)),
                                         p.w.down_s + ((int64_t)s_exp[u] * H + h0) * (I / 32), nown * (I / 32));
         }
+    };
+    if constexpr (SLICE) {
+        if (nown > 0) nfit = min(U, (int)(p.dn_bytes / (nown * rbI)));
+        if (!mf_slice || WF != MOE_FMT_BF16) slice_window();
     } else {
         int64_t room = p.dn_bytes;
         int seg = 0;
@@ -1766,6 +1775,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         MOE_TRACE(7);
         if (my_rows > 0 && threadIdx.x == 0) add_dev(line(set, kLineRouted + b % kRoutedStripes), (uint32_t)my_rows);
     }
+    if constexpr (SLICE)
+        if (mf_slice && WF == MOE_FMT_BF16) slice_window();
 
     // ---- B': the shared expert's down rows of this slice (weights in LDS) -> ysh [M][nown], while
     //      the routed units' counters complete (measured: doing it after the down rows instead,
@@ -1888,6 +1899,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                         wait_units(set, (uint32_t)(U * I), 0u, p.ws.hdr + kHdrStatus);
                         MOE_TRACE(9);
                         stage_rows_bf16((LDS char*)xs, p.ws.act, astride, NP, astride, apitch);
+                        if constexpr (WF == MOE_FMT_BF16)
+                            __builtin_amdgcn_s_waitcnt(0);  // this wave's share of the late window has landed
                         __syncthreads();
                         MOE_TRACE(10);
                     };
