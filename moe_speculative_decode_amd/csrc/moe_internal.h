@@ -78,6 +78,8 @@ struct Params {
     Workspace ws;
     int lds_scl;         // MXFP4: LDS scale windows (shared expert, then routed units) at this offset,
     int scl_sh, scl_rt;  // of these sizes in bytes (0: none)
+    int gu_ksplit;       // MXFP4 gate/up: (tile, stage) items, partials in the staging area at
+    int gu_part;         // this float offset
 };
 
 // Enqueues one call.

@@ -1013,23 +1013,40 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
 // (the last one re-read, so the number of loads in flight is static).  Blocks past H are zeroed.
 // silu(g) * v of row 8 (b + i G) + s of local tile i and the unit's n-th token goes to
 // cst[(8 i + s) * M + n].
+// With `part` (LDS, nloc * nstage * 16 * M floats) the work items are (tile, stage) pairs instead of
+// tiles, dealt to the waves round robin: every wave carries about the same bytes even when a
+// workgroup has few tiles (9 tiles of 2 stages on 8 waves: 3 stages at most per wave, not 4).  Each
+// item's partial g and v go to `part`; after a barrier the stages of a tile are summed in stage
+// order and silu(g) * v is staged as above.  Every wave of the workgroup must call this.
 template <int NQ, bool WIDE>
 __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* xs, int nloc,
-                                               const LDS uint32_t* s_mask, const LDS int* s_exp, LDS float* cst) {
+                                               const LDS uint32_t* s_mask, const LDS int* s_exp, LDS float* cst,
+                                               LDS float* part) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r = lane & 15, kq = lane >> 4;
     const int H = p.H, I = p.I, M = p.M, G = gridDim.x, b = blockIdx.x;
     const int nblk = H / 32, nquad = (nblk + 3) / 4, nstage = (nquad + NQ - 1) / NQ;
     const int64_t rb = H / 2, sb = H / 32;
-    const int nmine = n_strided(nloc, wave, kWaves);  // local tiles wave, wave + kWaves, ...
-    if (nmine == 0) return;
-    const int nsteps = nmine * nstage;
+    const bool ks = part != nullptr;
+    // this wave's steps: items wave, wave + kWaves, ... (split), or all stages of tiles wave,
+    // wave + kWaves, ...
+    const int nsteps = ks ? n_strided(nloc * nstage, wave, kWaves) : n_strided(nloc, wave, kWaves) * nstage;
     const uint8_t* mat = r < 8 ? (const uint8_t*)p.w.gate : (const uint8_t*)p.w.up;
     const uint8_t* mats = r < 8 ? p.w.gate_s : p.w.up_s;
     const LDS char* xrow = xs + (int64_t)min(r, M - 1) * p.xpitch;  // columns past M are dropped
-    // first flat row of this wave's j-th tile, and its staging slot
-    auto tile_row = [&](int j) { return (int64_t)(b + (wave + kWaves * j) * G) * 8; };
-    auto tile_slot = [&](int j) { return (wave + kWaves * j) * 8; };
+    // local tile and stage of this wave's step t; a local tile's first flat row and staging slot
+    auto tile_of = [&](int t, int& i, int& sg) {
+        if (ks) {
+            const int k = wave + kWaves * t;
+            i = k / nstage;
+            sg = k - i * nstage;
+        } else {
+            i = wave + kWaves * (t / nstage);
+            sg = t - (t / nstage) * nstage;
+        }
+    };
+    auto tile_row = [&](int i) { return (int64_t)(b + i * G) * 8; };
+    auto tile_slot = [&](int i) { return i * 8; };
     // A stage's scale bytes: blocks 4 NQ sg .. 4 NQ sg + 4 NQ - 1 of the row.  When the rows' scale
     // bytes are 16-byte aligned (H a multiple of 512) they come as NS 16-byte loads from the
     // aligned dword (NQ sg) & ~3 on, and block 4 (NQ sg + q) + kq is byte kq of dword
@@ -1044,7 +1061,8 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
     auto load = [&](Stage& st, int t) {
         const bool dummy = t >= nsteps;
         t = min(t, nsteps - 1);
-        const int j = t / nstage, sg = t - j * nstage;
+        int j, sg;
+        tile_of(t, j, sg);
         const int64_t f = tile_row(j) + (dummy ? 0 : (r & 7));
         const int u = (int)(f / I);
         const int64_t row = (int64_t)s_exp[u] * I + (f - (int64_t)u * I);
@@ -1076,7 +1094,8 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
     };
     f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
     auto compute = [&](Stage& st, int t) {
-        const int j = t / nstage, sg = t - j * nstage;
+        int j, sg;
+        tile_of(t, j, sg);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) asm volatile("" : "+v"(st.c[q]));
 #pragma unroll
@@ -1111,7 +1130,11 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
                     acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc0, 0, 0, 0);
             }
         }
-        if (sg == nstage - 1) {  // tile j done: lanes kq < 2 hold g of rows 4 kq + i, lanes kq + 2 their v
+        if (ks) {  // item done: its partial g (rows 0..7) and v (rows 8..15) of the M tokens to part
+            if (r < M) *(LDS f32x4*)(part + (((int64_t)(j * nstage + sg) * 4 + kq) * M + r) * 4) = acc0 + acc1;
+            acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            acc1 = acc0;
+        } else if (sg == nstage - 1) {  // tile j done: lanes kq < 2 hold g of rows 4 kq + i, lanes kq + 2 their v
             const f32x4 d = acc0 + acc1;
             f32x4 v;
 #pragma unroll
@@ -1128,16 +1151,33 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
             acc1 = acc0;
         }
     };
-    Stage sa, sb2;
-    load(sa, 0);
-    int t = 0;
-    while (true) {
-        load(sb2, t + 1);
-        compute(sa, t);
-        if (++t >= nsteps) break;
-        load(sa, t + 1);
-        compute(sb2, t);
-        if (++t >= nsteps) break;
+    if (nsteps > 0) {
+        Stage sa, sb2;
+        load(sa, 0);
+        int t = 0;
+        while (true) {
+            load(sb2, t + 1);
+            compute(sa, t);
+            if (++t >= nsteps) break;
+            load(sa, t + 1);
+            compute(sb2, t);
+            if (++t >= nsteps) break;
+        }
+    }
+    if (ks) {  // sum each tile's stages in stage order, then silu(g) * v for the unit's tokens
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < nloc * 8 * M; idx += kThreads) {
+            const int i = idx / (8 * M), rem = idx - i * 8 * M;
+            const int jr = rem / M, n = rem - jr * M;
+            float g = 0.0f, v = 0.0f;
+            for (int sg = 0; sg < nstage; ++sg) {
+                const LDS float* pp = part + (int64_t)(i * nstage + sg) * 4 * M * 4;
+                g += pp[((jr >> 2) * M + n) * 4 + (jr & 3)];
+                v += pp[((2 + (jr >> 2)) * M + n) * 4 + (jr & 3)];
+            }
+            const uint32_t mk = s_mask[(int)((tile_row(i) + jr) / I)];
+            if ((mk >> n) & 1u) cst[(tile_slot(i) + jr) * M + __popc(mk & ((1u << n) - 1u))] = silu_mul(g, v);
+        }
     }
 }
 
@@ -1668,10 +1708,11 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             const int nloc = n_strided((int)(nrows / 8), b, G);
             if constexpr (WF == MOE_FMT_MXFP4)
                 if (nloc > 0) {
+                    LDS float* part = p.gu_ksplit ? cst + p.gu_part : nullptr;
                     if ((H / 32) % 16 == 0)
-                        gateup_mfma_mx<10, true>(p, xs, nloc, s_mask, s_exp, cst);
+                        gateup_mfma_mx<10, true>(p, xs, nloc, s_mask, s_exp, cst, part);
                     else
-                        gateup_mfma_mx<10, false>(p, xs, nloc, s_mask, s_exp, cst);
+                        gateup_mfma_mx<10, false>(p, xs, nloc, s_mask, s_exp, cst, part);
                 }
             __syncthreads();
             MOE_TRACE(6);
@@ -2183,7 +2224,13 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     const int64_t units = std::min<int64_t>(NP, p.E);
     int64_t cst;
     if (p.gu_mfma) {
-        cst = std::max<int64_t>(kSelBytes, (units * p.I / 8 + G - 1) / G * 8 * M * 4);
+        // tiles of 8 rows per workgroup; (tile, stage) items with partials in LDS while they fit
+        const int64_t tiles = (units * p.I / 8 + G - 1) / G;
+        const int64_t nstage = ((H / 32 + 3) / 4 + 9) / 10;  // stages of 10 block groups
+        const int64_t pbytes = tiles * nstage * 16 * M * 4;
+        p.gu_ksplit = pbytes <= 16 * 1024 ? 1 : 0;
+        p.gu_part = (int)(tiles * 8 * M);
+        cst = std::max<int64_t>(kSelBytes, tiles * 8 * M * 4 + (p.gu_ksplit ? pbytes : 0));
         p.gu_cap = 0;
     } else {
         const int64_t rtg = rt_gate<WF>();
