@@ -537,6 +537,38 @@ __device__ __forceinline__ void stage_rows(LDS float* dst, const float* src, int
     }
 }
 
+// Device-scope (sc1) store of v rounded to bfloat16 (nearest even) at byte byte_off of r.
+__device__ __forceinline__ void st_dev_bf16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), r, (int)byte_off, 0, 16 /* sc1 */);
+}
+
+// Stages `tcount` bfloat16 SwiGLU rows of K elements (global rows of `stride` elements from `src`)
+// into LDS rows of `pitch` bytes with 16-byte device-scope loads.
+__device__ __forceinline__ void stage_rows_b16(LDS char* dst, const uint16_t* src, int stride, int tcount, int K,
+                                               int pitch) {
+    const __amdgpu_buffer_rsrc_t r = dev_rsrc(src, (uint32_t)(tcount * stride * 2));
+    const int q8 = K / 8, n = tcount * q8;
+    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * kThreads) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kThreads;
+            if (i < n) {
+                const int t = i / q8, c8 = i - t * q8;
+                v[u] = ld_dev16(r, (uint32_t)((t * stride + 8 * c8) * 2));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kThreads;
+            if (i < n) {
+                const int t = i / q8, c8 = i - t * q8;
+                *(LDS f32x4*)(dst + (int64_t)t * pitch + 16 * c8) = v[u];
+            }
+        }
+    }
+}
+
 // Stages `tcount` fp32 SwiGLU rows of K elements (global rows of `stride` floats from `src`) into
 // LDS as bfloat16 (round to nearest even), rows of `pitch` bytes, with 16-byte device-scope loads.
 __device__ __forceinline__ void stage_rows_bf16(LDS char* dst, const float* src, int stride, int tcount, int K,
@@ -1583,6 +1615,12 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     // slice mode on the matrix cores reads the LDS windows row-interleaved: store them swizzled
     const bool mf_slice = p.slice_mfma != 0;
     const bool mf_sh = p.sh_mfma != 0;  // shared down rows on the matrix cores (window stored swizzled)
+    // slice mode on the matrix cores rounds the SwiGLU rows to bfloat16 for its B operands: the
+    // producers write them as bfloat16 (the same rounding, half the bytes every workgroup stages)
+    const bool bf_act = SLICE && mf_slice;
+    const uint16_t* act16 = (const uint16_t*)p.ws.act;
+    const __amdgpu_buffer_rsrc_t act_rs =
+        dev_rsrc(p.ws.act, (uint32_t)((int64_t)(NP + M) * p.act_stride * 4));
     if (has_sh && !p.route_only && nown > 0) {
         if (mf_sh)
             async_rows_to_lds((char*)shw, (const uint8_t*)p.w.sh_down + h0 * rbIs, (int)(nown * rbIs), (int)rbIs);
@@ -1626,7 +1664,12 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 t.mask = (1u << M) - 1u;
                 t.slot = (int)r0;
             },
-            [&](int r, int i, float v) { st_dev(p.ws.act + (int64_t)(NP + i) * p.act_stride + r, v); });
+            [&](int r, int i, float v) {
+                if (bf_act)
+                    st_dev_bf16(act_rs, (uint32_t)(((int64_t)(NP + i) * p.act_stride + r) * 2), v);
+                else
+                    st_dev(p.ws.act + (int64_t)(NP + i) * p.act_stride + r, v);
+            });
     }
     MOE_TRACE(3);
 
@@ -1722,7 +1765,13 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 const int64_t f = (int64_t)(b + (sl / 8) * G) * 8 + sl % 8;
                 const int u = (int)(f / I);
                 if (m < __popc(s_mask[u]))
-                    st_dev(p.ws.act + (int64_t)(s_off[u] + m) * p.act_stride + (f - (int64_t)u * I), cst[i]);
+                {
+                    const int64_t o = (int64_t)(s_off[u] + m) * p.act_stride + (f - (int64_t)u * I);
+                    if (bf_act)
+                        st_dev_bf16(act_rs, (uint32_t)(o * 2), cst[i]);
+                    else
+                        st_dev(p.ws.act + o, cst[i]);
+                }
             }
             my_rows = nloc * 8;
         } else {
@@ -1807,7 +1856,13 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     const int64_t f = (int64_t)qlog[wv * cap + sp] * RTG + sl % RTG;
                     const int u = (int)(f / I);
                     if (m < __popc(s_mask[u]))
-                        st_dev(p.ws.act + (int64_t)(s_off[u] + m) * p.act_stride + (f - (int64_t)u * I), cst[i]);
+                    {
+                    const int64_t o = (int64_t)(s_off[u] + m) * p.act_stride + (f - (int64_t)u * I);
+                    if (bf_act)
+                        st_dev_bf16(act_rs, (uint32_t)(o * 2), cst[i]);
+                    else
+                        st_dev(p.ws.act + o, cst[i]);
+                }
                 }
             }
             for (int wv = 0; wv < kWaves; ++wv) my_rows += nwv[wv] * RTG;
@@ -1908,7 +1963,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     const int nsh = has_sh ? 1 : 0;  // the shared unit first: it needs no wait
                     if (has_sh) {
                         wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
-                        stage_rows_bf16((LDS char*)xs + (int64_t)NP * apitch, p.ws.act + (int64_t)NP * astride, astride,
+                        stage_rows_b16((LDS char*)xs + (int64_t)NP * apitch, act16 + (int64_t)NP * astride, astride,
                                         M, Is, apitch);
                         __syncthreads();
                     }
@@ -1939,7 +1994,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     auto ready_bf16 = [&]() {  // the shared expert's rows were staged above
                         wait_units(set, (uint32_t)(U * I), 0u, p.ws.hdr + kHdrStatus);
                         MOE_TRACE(9);
-                        stage_rows_bf16((LDS char*)xs, p.ws.act, astride, NP, astride, apitch);
+                        stage_rows_b16((LDS char*)xs, act16, astride, NP, astride, apitch);
                         if constexpr (WF == MOE_FMT_BF16)
                             __builtin_amdgcn_s_waitcnt(0);  // this wave's share of the late window has landed
                         __syncthreads();
