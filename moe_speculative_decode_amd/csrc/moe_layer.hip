@@ -1534,6 +1534,137 @@ __device__ __forceinline__ void down_slice_mfma(int nun, int npre, int ng, int n
     }
 }
 
+// The MXFP4 form of down_slice_mfma (same units, order, waits and outputs).  K is permuted alike
+// for A and B: lane (r, kq) owns whole MX blocks 4j + kq of its row (16 bytes of codes, one scale
+// byte), and product 4j + m takes sub-chunk m of those blocks, so B lane (n, kq) of that product
+// holds elements 32 (4j + kq) + 8m .. + 7 of token n's row.  A unit's A operand is then KB / 4
+// 16-byte reads and KB / 4 scale bytes per lane instead of KB 4-byte reads and KB scale bytes:
+// small enough for a wave to hold two units, so the next unit's reads are in flight while the
+// current one is computed (units past the LDS window stream their rows from global memory, and a
+// wait per unit would serialise their latencies).  Rows of the LDS window are in place before the
+// call, so any unit's reads may start before ready().
+template <int KB, typename UnitOf, typename Ready>
+__device__ __forceinline__ void down_slice_mfma_mx(int nun, int npre, int nown, int apitch, UnitOf unit_of,
+                                                   Ready ready, LDS float* pst) {
+    static_assert(KB % 8 == 0, "K blocks in batches of 8");
+    constexpr int NB = KB / 4;  // MX blocks per lane
+    constexpr int BB = 8;       // B chunks per batch
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int r = lane & 15, kq = lane >> 4;
+    const int rr = min(r, nown - 1);
+    struct AOp {
+        u32x4 q[NB];
+        uint32_t s[NB];
+    };
+    // lanes of rows past nown keep stale operands, which reach only dropped rows of D
+    auto load_a = [&](AOp& a, const SliceUnit& u) {
+        if (r >= nown) return;
+        const int nblk = u.K / 32;
+        const int64_t rb = u.K / 2;
+        if (u.lds) {
+            const LDS uint8_t* row = (const LDS uint8_t*)u.w + rr * rb;
+            const int sw = chunk_swz(rr, rb);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) a.q[j] = *(const LDS u32x4*)(row + 16 * (min(4 * j + kq, nblk - 1) ^ sw));
+        } else {
+            const uint8_t* row = u.w + rr * rb;
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                a.q[j] = __builtin_nontemporal_load((const u32x4*)(row + 16 * min(4 * j + kq, nblk - 1)));
+        }
+        if (u.sl) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) a.s[j] = u.sl[rr * nblk + min(4 * j + kq, nblk - 1)];
+        } else {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) a.s[j] = u.s[rr * nblk + min(4 * j + kq, nblk - 1)];
+        }
+    };
+    auto compute = [&](AOp& a, const SliceUnit& u) {
+        const int nblk = u.K / 32;
+        const LDS char* brow = u.acts + (int64_t)min(r, u.t - 1) * apitch;
+        auto boff = [&](int i) {  // byte offset of product i's 8 elements, 0 past K
+            return 4 * (i >> 2) + kq < nblk ? 2 * (128 * (i >> 2) + 32 * kq + 8 * (i & 3)) : 0;
+        };
+        auto load_b = [&](u32x4(&b)[BB], int i0) {
+            if (r >= u.t) return;
+#pragma unroll
+            for (int j = 0; j < BB; ++j) b[j] = *(const LDS u32x4*)(brow + boff(i0 + j));
+        };
+        f32x4 acc[4] = {};
+        u32x4 ba[BB] = {}, bb[BB] = {};
+        auto batch = [&](u32x4(&b)[BB], int i0) {
+#pragma unroll
+            for (int j = 0; j < BB; ++j) asm volatile("" : "+v"(b[j]));
+#pragma unroll
+            for (int j = 0; j < BB; ++j) {
+                const int i = i0 + j, jb = i >> 2;
+                const bool kv = 4 * jb + kq < nblk;
+                asm volatile("" : "+v"(a.q[jb]), "+v"(a.s[jb]));
+                const uint32_t c = a.q[jb][i & 3];
+                const float sc = e8m0_to_f32(a.s[jb]);
+                const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0);
+                const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1);
+                const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 2);
+                const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 3);
+                const bf16x8 av = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                acc[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    av, __builtin_bit_cast(bf16x8, kv ? b[j] : u32x4{0u, 0u, 0u, 0u}), acc[j & 3], 0, 0, 0);
+            }
+        };
+        load_b(ba, 0);
+#pragma unroll
+        for (int i0 = 0; i0 < KB; i0 += 2 * BB) {
+            if (i0 + BB < KB) load_b(bb, i0 + BB);
+            batch(ba, i0);
+            if (i0 + BB >= KB) break;
+            if (i0 + 2 * BB < KB) load_b(ba, i0 + 2 * BB);
+            batch(bb, i0 + BB);
+        }
+        const f32x4 d = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        if (r < u.t) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = 4 * kq + q;
+                if (row < nown) pst[(u.prow + r) * nown + row] = d[q];
+            }
+        }
+    };
+    SliceUnit u0, u1;
+    AOp a0, a1;
+    int q = (wave + 1) % kWaves;  // unit 0 to the last wave: wave 0 also polls in ready()
+    for (; q < npre; q += kWaves) {  // units that need no wait (rows in LDS, SwiGLU rows staged)
+        unit_of(q, u0);
+        load_a(a0, u0);
+        compute(a0, u0);
+    }
+    // two units in flight from here on; both reads are issued before the wait
+    if (q < nun) {
+        unit_of(q, u0);
+        load_a(a0, u0);
+    }
+    if (q + kWaves < nun) {
+        unit_of(q + kWaves, u1);
+        load_a(a1, u1);
+    }
+    ready();
+    while (q < nun) {
+        compute(a0, u0);
+        if (q + 2 * kWaves < nun) {
+            unit_of(q + 2 * kWaves, u0);
+            load_a(a0, u0);
+        }
+        q += kWaves;
+        if (q >= nun) break;
+        compute(a1, u1);
+        if (q + 2 * kWaves < nun) {
+            unit_of(q + 2 * kWaves, u1);
+            load_a(a1, u1);
+        }
+        q += kWaves;
+    }
+}
+
 // Splits a list of U units of n items each (rows or tasks; item i of unit u has flat index
 // u * n + i) over G workgroups by cost, an item of unit u costing c0 + c1 * t_u where t_u is the
 // unit's token count: every workgroup gets an equal share of the total cost, so units that many
@@ -2000,7 +2131,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                         __syncthreads();
                         MOE_TRACE(10);
                     };
-                    down_slice_mfma<WF, 8 * NJD>(U + nsh, nsh, ng, nown, apitch, unit_of, ready_bf16, pst);
+                    if constexpr (WF == MOE_FMT_MXFP4)
+                        down_slice_mfma_mx<8 * NJD>(U + nsh, nsh, nown, apitch, unit_of, ready_bf16, pst);
+                    else
+                        down_slice_mfma<WF, 8 * NJD>(U + nsh, nsh, ng, nown, apitch, unit_of, ready_bf16, pst);
                     __syncthreads();
                     MOE_TRACE(11);
                     const LDS int* s_pair = tab + kTabPair;
