@@ -86,6 +86,10 @@ CONFIGS: Dict[str, LayerConfig] = {
                                   "Ling shapes, bf16, M=16 ragged verify, requests {2,6,3,5}"),
     "ling_mxfp4_m6": _ling("ling_mxfp4_m6", MXFP4, (6,), "shared_base",
                            "Ling shapes, MXFP4 expert weights, bf16 router/activations, M=6"),
+    "ling_mxfp4_m1": _ling("ling_mxfp4_m1", MXFP4, (1,), "iid",
+                           "Ling shapes, MXFP4 expert weights, bf16 router/activations, M=1"),
+    "ling_mxfp4_m16_ragged": _ling("ling_mxfp4_m16_ragged", MXFP4, (2, 6, 3, 5), "shared_base",
+                                   "Ling shapes, MXFP4 expert weights, M=16 ragged verify, requests {2,6,3,5}"),
 }
 
 

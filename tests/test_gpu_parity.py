@@ -78,7 +78,8 @@ def test_tiny_f32_config():
     _check_case(case, disp)
 
 
-@pytest.mark.parametrize("name", ["ling_bf16_m1", "ling_bf16_m6", "ling_bf16_m16_ragged", "ling_mxfp4_m6"])
+@pytest.mark.parametrize("name", ["ling_bf16_m1", "ling_bf16_m6", "ling_bf16_m16_ragged", "ling_mxfp4_m1",
+                                  "ling_mxfp4_m6", "ling_mxfp4_m16_ragged"])
 def test_ling_configs(name):
     cfg = synth.CONFIGS[name]
     G.log("ling", name, "generating layer")
