@@ -694,7 +694,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // and the batch compaction into this workgroup's LDS tables.  Workgroup 0 (`publish_outputs`)
 // also writes the caller-visible routing outputs.  Returns U.
 __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, LDS char* sel, bool publish_outputs,
-                                                 uint32_t tag) {
+                                                 uint32_t tag, int poll_wave) {
     const int E = p.E, M = p.M, k = p.k, NP = M * k;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const bool has_sh = p.Is > 0;
@@ -728,7 +728,7 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        if (wave == kWaves - 1) {  // pairs q = lane + 64 i, i < 4 (M * k <= 256), written once all are current
+        if (wave == poll_wave) {  // pairs q = lane + 64 i, i < 4 (M * k <= 256), written once all are current
             const __amdgpu_buffer_rsrc_t rs = dev_rsrc(p.ws.route, (uint32_t)NP * 16);
             u32x4 v[kMaxTokens * kMaxTopK / 64];
             for (int it = 0;; ++it) {
@@ -1780,10 +1780,12 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     // ---- A': shared expert gate/up (needs no routing), on the waves without router rows first;
     //      results go straight to the workspace and are counted after the routing barrier ----
     int sh_rows = 0;
+    int sh_waves = 0;  // waves kWaves - sh_waves .. kWaves - 1 have shared gate/up tasks
     if (has_sh && !p.route_only) {
         const int T = Is / RTG;  // a contiguous range of tasks per workgroup
         const int qa = (int)((int64_t)T * b / G), qb = (int)((int64_t)T * (b + 1) / G);
         sh_rows = (qb - qa) * RTG;
+        sh_waves = min(qb - qa, kWaves);
         gateup_run<AF, WF, NJ>(
             p, xs, qb - qa, kWaves - 1 - wave_id(),
             [&](int i, GUTask& t) {
@@ -1805,7 +1807,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     MOE_TRACE(3);
 
     // ---- B: routing barrier, top-k and compaction in every workgroup ----
-    const int U = route_and_compact(p, tab, (LDS char*)cst, b == 0, call + 1u);
+    // the published expert pairs are polled by the highest wave without shared gate/up tasks (those
+    // run on the vector ALU and, at 16 tokens with E2M1 decode, would hold the poll back by µs)
+    const int U = route_and_compact(p, tab, (LDS char*)cst, b == 0, call + 1u,
+                                    sh_waves >= kWaves ? kWaves - 1 : kWaves - 1 - sh_waves);
     MOE_TRACE(5);
     if (b == 0 && threadIdx.x == 0)
         __hip_atomic_store(p.ws.hdr + kHdrCall, call + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2403,10 +2408,11 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     // MXFP4 gate/up rows on the matrix cores: each code is decoded once for all tokens, so the
     // work per weight byte no longer grows with the unit's token count
     p.gu_mfma = WF == MOE_FMT_MXFP4 ? 1 : 0;
-    // per-token cost of a down row (a row's bytes cost kCostBase = 8): bf16 from a sweep of the
-    // whole-layer time over 0, 1, 2, 4 and 6 at 6 and 16 tokens (2 is fastest at both); MXFP4 rows
-    // are bound by their loads
-    p.cost_dn = WF == MOE_FMT_MXFP4 ? 1 : (WF == MOE_FMT_BF16 ? 2 : 0);
+    // per-token cost of a down row (a row's bytes cost kCostBase = 8), from sweeps of the
+    // whole-layer time: bf16 over 0, 1, 2, 4 and 6 at 6 and 16 tokens (2 is fastest at both);
+    // MXFP4 over 1, 3, 6, 9 and 14 at 16 tokens (6 is fastest: the vector path decodes every
+    // code once per token)
+    p.cost_dn = WF == MOE_FMT_MXFP4 ? 6 : (WF == MOE_FMT_BF16 ? 2 : 0);
     // gate/up staging: MXFP4 tiles of 8 rows dealt round robin (at most ceil(T / G) per workgroup);
     // otherwise per wave the static share plus up to twice the average dynamic share (the split
     // the kernel makes from the actual number of units, bounded here by its maximum)
