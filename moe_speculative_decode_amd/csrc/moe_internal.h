@@ -80,6 +80,7 @@ struct Params {
     int scl_sh, scl_rt;  // of these sizes in bytes (0: none)
     int gu_ksplit;       // MXFP4 gate/up: (tile, stage) items, partials in the staging area at
     int gu_part;         // this float offset
+    int sh_gu_mfma;      // MXFP4: the shared expert's gate/up rows on the matrix cores too
 };
 
 // Enqueues one call.

@@ -1050,7 +1050,7 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
 // workgroup has few tiles (9 tiles of 2 stages on 8 waves: 3 stages at most per wave, not 4).  Each
 // item's partial g and v go to `part`; after a barrier the stages of a tile are summed in stage
 // order and silu(g) * v is staged as above.  Every wave of the workgroup must call this.
-template <int NQ, bool WIDE>
+template <int NQ, bool WIDE, bool SH = false>
 __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* xs, int nloc,
                                                const LDS uint32_t* s_mask, const LDS int* s_exp, LDS float* cst,
                                                LDS float* part) {
@@ -1063,8 +1063,11 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
     // this wave's steps: items wave, wave + kWaves, ... (split), or all stages of tiles wave,
     // wave + kWaves, ...
     const int nsteps = ks ? n_strided(nloc * nstage, wave, kWaves) : n_strided(nloc, wave, kWaves) * nstage;
-    const uint8_t* mat = r < 8 ? (const uint8_t*)p.w.gate : (const uint8_t*)p.w.up;
-    const uint8_t* mats = r < 8 ? p.w.gate_s : p.w.up_s;
+    const uint8_t* mat = SH ? (r < 8 ? (const uint8_t*)p.w.sh_gate : (const uint8_t*)p.w.sh_up)
+                            : (r < 8 ? (const uint8_t*)p.w.gate : (const uint8_t*)p.w.up);
+    const uint8_t* mats = SH ? (r < 8 ? p.w.sh_gate_s : p.w.sh_up_s) : (r < 8 ? p.w.gate_s : p.w.up_s);
+    // the token mask of a flat row: the unit's, or every token for the shared expert
+    auto row_mask = [&](int64_t f) -> uint32_t { return SH ? (1u << M) - 1u : s_mask[(int)(f / I)]; };
     const LDS char* xrow = xs + (int64_t)min(r, M - 1) * p.xpitch;  // columns past M are dropped
     // local tile and stage of this wave's step t; a local tile's first flat row and staging slot
     auto tile_of = [&](int t, int& i, int& sg) {
@@ -1096,8 +1099,11 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
         int j, sg;
         tile_of(t, j, sg);
         const int64_t f = tile_row(j) + (dummy ? 0 : (r & 7));
-        const int u = (int)(f / I);
-        const int64_t row = (int64_t)s_exp[u] * I + (f - (int64_t)u * I);
+        int64_t row = f;  // the shared expert's rows are the flat rows
+        if constexpr (!SH) {
+            const int u = (int)(f / I);
+            row = (int64_t)s_exp[u] * I + (f - (int64_t)u * I);
+        }
         const uint8_t* w = (dummy ? (const uint8_t*)p.w.gate : mat) + row * rb;
         const uint8_t* sc = (dummy ? p.w.gate_s : mats) + row * sb;
 #pragma unroll
@@ -1174,7 +1180,7 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
             if (kq < 2 && r < M) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint32_t mk = s_mask[(int)((tile_row(j) + 4 * kq + i) / I)];
+                    const uint32_t mk = row_mask(tile_row(j) + 4 * kq + i);
                     if ((mk >> r) & 1u)
                         cst[(tile_slot(j) + 4 * kq + i) * M + __popc(mk & ((1u << r) - 1u))] = silu_mul(d[i], v[i]);
                 }
@@ -1207,7 +1213,7 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
                 g += pp[((jr >> 2) * M + n) * 4 + (jr & 3)];
                 v += pp[((2 + (jr >> 2)) * M + n) * 4 + (jr & 3)];
             }
-            const uint32_t mk = s_mask[(int)((tile_row(i) + jr) / I)];
+            const uint32_t mk = row_mask(tile_row(i) + jr);
             if ((mk >> n) & 1u) cst[(tile_slot(i) + jr) * M + __popc(mk & ((1u << n) - 1u))] = silu_mul(g, v);
         }
     }
@@ -1781,7 +1787,33 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     //      results go straight to the workspace and are counted after the routing barrier ----
     int sh_rows = 0;
     int sh_waves = 0;  // waves kWaves - sh_waves .. kWaves - 1 have shared gate/up tasks
-    if (has_sh && !p.route_only) {
+    bool sh_done = false;
+    if constexpr (WF == MOE_FMT_MXFP4) {
+        // MXFP4 from 8 tokens on: tiles of 8 shared rows on the matrix cores (on the vector ALU every
+        // code would be decoded once per token, and at 16 tokens one 4-row task outlasts the routing)
+        if (has_sh && !p.route_only && p.sh_gu_mfma) {
+            const int nloc = n_strided(Is / 8, b, G);
+            if (nloc > 0) {
+                if ((H / 32) % 16 == 0)
+                    gateup_mfma_mx<10, true, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
+                else
+                    gateup_mfma_mx<10, false, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
+            }
+            __syncthreads();
+            for (int i = threadIdx.x; i < nloc * 8 * M; i += kThreads) {
+                const int sl = i / M, m = i - sl * M;
+                const int64_t o = (int64_t)(NP + m) * p.act_stride + (int64_t)(b + (sl / 8) * G) * 8 + sl % 8;
+                if (bf_act)
+                    st_dev_bf16(act_rs, (uint32_t)(o * 2), cst[i]);
+                else
+                    st_dev(p.ws.act + o, cst[i]);
+            }
+            __syncthreads();  // the staging area is the routing scratch next
+            sh_rows = nloc * 8;
+            sh_done = true;
+        }
+    }
+    if (has_sh && !p.route_only && !sh_done) {
         const int T = Is / RTG;  // a contiguous range of tasks per workgroup
         const int qa = (int)((int64_t)T * b / G), qb = (int)((int64_t)T * (b + 1) / G);
         sh_rows = (qb - qa) * RTG;
@@ -2408,6 +2440,7 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     // MXFP4 gate/up rows on the matrix cores: each code is decoded once for all tokens, so the
     // work per weight byte no longer grows with the unit's token count
     p.gu_mfma = WF == MOE_FMT_MXFP4 ? 1 : 0;
+    p.sh_gu_mfma = WF == MOE_FMT_MXFP4 && M >= 8 && p.Is % 8 == 0 ? 1 : 0;  // the shared expert's too
     // per-token cost of a down row (a row's bytes cost kCostBase = 8), from sweeps of the
     // whole-layer time: bf16 over 0, 1, 2, 4 and 6 at 6 and 16 tokens (2 is fastest at both);
     // MXFP4 over 1, 3, 6, 9 and 14 at 16 tokens (6 is fastest: the vector path decodes every
