@@ -2442,10 +2442,10 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     p.gu_mfma = WF == MOE_FMT_MXFP4 ? 1 : 0;
     p.sh_gu_mfma = WF == MOE_FMT_MXFP4 && M >= 8 && p.Is % 8 == 0 ? 1 : 0;  // the shared expert's too
     // per-token cost of a down row (a row's bytes cost kCostBase = 8), from sweeps of the
-    // whole-layer time: bf16 over 0, 1, 2, 4 and 6 at 6 and 16 tokens (2 is fastest at both);
+    // whole-layer time: bf16 over 0, 1, 2, 3, 4 and 6 at 6 and 16 tokens (3 is fastest at both);
     // MXFP4 over 1, 3, 6, 9 and 14 at 16 tokens (6 is fastest: the vector path decodes every
     // code once per token)
-    p.cost_dn = WF == MOE_FMT_MXFP4 ? 6 : (WF == MOE_FMT_BF16 ? 2 : 0);
+    p.cost_dn = WF == MOE_FMT_MXFP4 ? 6 : (WF == MOE_FMT_BF16 ? 3 : 0);
     // gate/up staging: MXFP4 tiles of 8 rows dealt round robin (at most ceil(T / G) per workgroup);
     // otherwise per wave the static share plus up to twice the average dynamic share (the split
     // the kernel makes from the actual number of units, bounded here by its maximum)
