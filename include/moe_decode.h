@@ -32,9 +32,17 @@
  *     negative status has enqueued nothing.  MOE_ERR_HIP reports a failed launch.  Faults inside
  *     the kernels surface at the caller's next synchronisation, as for any HIP kernel.
  *   - The workspace `ws` (size from moe_workspace_bytes) must be zero-filled once before its first
- *     use; every call leaves its counters at zero again.  Calls that share a workspace must be
- *     ordered (the same stream, or synchronised); calls with distinct workspaces may overlap.
- *   - The library keeps no mutable global state; it is safe to call from several host threads.
+ *     use and stays bound to one device; the calls keep its counters consistent from then on.
+ *   - At most ONE moe_route / moe_decode_forward may be in flight per device at any time, whatever
+ *     the workspaces: a call runs one workgroup on every compute unit and its workgroups wait on
+ *     each other, so two calls running at once could each hold part of the GPU and wait on the
+ *     other.  Order the calls (one stream, or events between streams).
+ *   - A wait between workgroups that gives up (bounded at about a second; it happens only if the
+ *     rule above is broken) never leaves output that looks valid: the call's y elements, and the
+ *     routing weights of a token whose routing was cut short, are written as NaN, and the
+ *     workspace status word records MOE_ERR_TIMEOUT (see moe_read_status).
+ *   - The library's only host state is a per-device cache of device properties and kernel set-up,
+ *     filled on first use; it is safe to call from several host threads.
  *   - Matrices are row-major [out][in] with the input dimension K contiguous (nn.Linear layout).
  *     Every pointer must be 16-byte aligned.
  */
@@ -65,18 +73,23 @@ typedef enum {
                                are not 0 = o[0] <= o[1] <= ... <= o[R] = M */
     MOE_ERR_HIP = -6,       /* a HIP runtime call failed */
     MOE_ERR_ALIGN = -7,     /* a pointer is not 16-byte aligned */
-    MOE_ERR_TIMEOUT = -8    /* device status only: a cross-workgroup wait gave up (its results are
-                               invalid); happens only if the grid is not fully resident */
+    MOE_ERR_TIMEOUT = -8    /* device status only: a cross-workgroup wait gave up; that call's y
+                               was written as NaN (happens only if calls overlap on one device) */
 } moe_status_t;
 
 /* Largest supported values (checked on the host). */
-#define MOE_MAX_TOKENS 16   /* tokens per call (M) */
-#define MOE_MAX_EXPERTS 512 /* routed experts (E) */
-#define MOE_MAX_TOPK 16     /* experts per token (k) */
+#define MOE_MAX_TOKENS 16      /* tokens per call (M) */
+#define MOE_MAX_EXPERTS 512    /* routed experts (E) */
+#define MOE_MAX_TOPK 16        /* experts per token (k) */
+#define MOE_MAX_HIDDEN 2560    /* H, bf16 and MXFP4 weights */
+#define MOE_MAX_INTER 768      /* I and Is, bf16 and MXFP4 weights */
+#define MOE_MAX_HIDDEN_F32 256 /* H, binary32 layer */
+#define MOE_MAX_INTER_F32 256  /* I and Is, binary32 layer */
 
-/* Layer description.  H, I, Is multiples of 8 (of 32 for MXFP4); H <= 4096; I, Is <= 2048;
-   1 <= k <= min(E, 16); E <= 512; 1 <= max_tokens <= 16; max_tokens * H * (bytes per activation)
-   <= 96 KiB (the token rows are staged in LDS). */
+/* Layer description.  H, I, Is multiples of 8 (of 32 for MXFP4), within the maxima above;
+   1 <= k <= min(E, 16); E <= 512; 1 <= max_tokens <= 16.  A call whose shape leaves no room for the
+   kernel's on-chip (LDS) layout at the given M is rejected with MOE_ERR_SHAPE before anything is
+   enqueued (for example k = 16 with 16 tokens of Ling width). */
 typedef struct {
     int32_t hidden;        /* H */
     int32_t num_experts;   /* E */
@@ -118,14 +131,23 @@ typedef struct {
 /* Workspace size in bytes for this description, or 0 when the description is invalid. */
 size_t moe_workspace_bytes(const moe_desc_t* d);
 
-/* Router only: logits = x [M][H] . w_router [E][H]^T with fp32 accumulation, then per token the k
+/* Router only ("Chasing the Batch-1 Floor", section "PDL: stacking the latency floors of small
+   kernels": the router chain gate matvec -> top-k; section "bf16 router gate and lm_head": bf16 gate
+   weight, fp32 accumulation; "3 ways to boost MoE inference on NVIDIA DGX Spark", "Model and
+   baseline configuration": eight of 512 routed experts per token).
+   logits = x [M][H] . w_router [E][H]^T with fp32 accumulation, then per token the k
    largest logits (ties: lower expert id) and weights softmax-renormalised over those k.
    topk_ids [M][k] and topk_w [M][k] receive them in descending weight order.  `disp` (nullable)
    additionally receives the batch dispatch.  Same routing as inside moe_decode_forward. */
 int moe_route(const moe_desc_t* d, int32_t M, const void* x, const void* w_router, int32_t* topk_ids,
               float* topk_w, const moe_dispatch_t* disp, void* ws, size_t ws_bytes, void* stream);
 
-/* The whole layer: y [M][H] = sum_j w[m,j] * expert_{id[m,j]}(x_m) + shared(x_m), where
+/* The whole layer ("Chasing the Batch-1 Floor", section "PDL: stacking the latency floors of small
+   kernels": router chain, then align -> up-GEMM -> activation -> down-GEMM -> combine, the combine an
+   fp32 sum of weight x expert output with one final cast; section "Two fusions and a retune":
+   silu(gate) * up in float, 512 routed + 1 shared experts on the dispatch axis; "DSpark in SGLang",
+   "Ragged verify under full CUDA graphs": a packed ragged verify batch with cu_seqlens offsets).
+   y [M][H] = sum_j w[m,j] * expert_{id[m,j]}(x_m) + shared(x_m), where
    expert(x) = Wd (silu(Wg x) * (Wu x)).  Each distinct selected expert's weights are read from
    memory once per call, however many of the M tokens chose it.
    req_offsets: device int32 [R+1] packed-request offsets (0 = o[0] <= ... <= o[R] = M, requests may

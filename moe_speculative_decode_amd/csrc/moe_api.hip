@@ -3,6 +3,9 @@
 // memory or synchronises, except moe_read_status which says so in its name.
 #include <string.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace {
@@ -50,15 +53,15 @@ int check_desc(const moe_desc_t* d) {
     if (f32 && d->weight_format != MOE_FMT_F32) return MOE_ERR_FORMAT;
     if (!f32 && d->weight_format != MOE_FMT_BF16 && d->weight_format != MOE_FMT_MXFP4) return MOE_ERR_FORMAT;
     const int mult = d->weight_format == MOE_FMT_MXFP4 ? 32 : 8;
-    if (d->hidden <= 0 || d->hidden > 4096 || d->hidden % mult) return MOE_ERR_SHAPE;
+    // the kernel instances cover H <= 2560 and I, Is <= 768 (bf16, MXFP4), and the small binary32
+    // layer H, I, Is <= 256
+    const int maxH = f32 ? MOE_MAX_HIDDEN_F32 : MOE_MAX_HIDDEN, maxI = f32 ? MOE_MAX_INTER_F32 : MOE_MAX_INTER;
+    if (d->hidden <= 0 || d->hidden > maxH || d->hidden % mult) return MOE_ERR_SHAPE;
     if (d->num_experts <= 0 || d->num_experts > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
     if (d->top_k <= 0 || d->top_k > MOE_MAX_TOPK || d->top_k > d->num_experts) return MOE_ERR_SHAPE;
-    if (d->inter <= 0 || d->inter > 2048 || d->inter % mult) return MOE_ERR_SHAPE;
-    if (d->shared_inter < 0 || d->shared_inter > 2048 || d->shared_inter % mult) return MOE_ERR_SHAPE;
+    if (d->inter <= 0 || d->inter > maxI || d->inter % mult) return MOE_ERR_SHAPE;
+    if (d->shared_inter < 0 || d->shared_inter > maxI || d->shared_inter % mult) return MOE_ERR_SHAPE;
     if (d->max_tokens <= 0 || d->max_tokens > MOE_MAX_TOKENS) return MOE_ERR_SHAPE;
-    // the gate/up kernel stages all M token rows in LDS
-    const size_t xbytes = (size_t)d->max_tokens * d->hidden * (f32 ? 4 : 2);
-    if (xbytes > 96 * 1024) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -125,12 +128,30 @@ int check_weights(const moe_desc_t* d, const moe_weights_t* w) {
     return MOE_OK;
 }
 
-int num_cus(int* out) {
+// Workgroups per call: one per compute unit of the current device (cached per device).
+int grid_size(int* out) {
+    static std::atomic<int> cache[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
-    if (hipDeviceGetAttribute(out, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MOE_ERR_HIP;
-    if (*out <= 0) return MOE_ERR_HIP;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return MOE_ERR_HIP;
+        n = std::min(n, moe::kMaxGrid);
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    *out = n;
     return MOE_OK;
+}
+
+// Plans the call for this device's grid (a shape whose LDS layout does not fit is rejected here,
+// before anything is enqueued) and launches it.
+int plan_and_launch(Params& p, hipStream_t stream) {
+    int G = 0;
+    int st = grid_size(&G);
+    if (st) return st;
+    if (moe::plan_layer(p, G) != hipSuccess) return MOE_ERR_SHAPE;
+    return moe::launch_layer(p, G, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // namespace
@@ -153,9 +174,7 @@ int moe_route(const moe_desc_t* d, int32_t M, const void* x, const void* w_route
     if (disp) p.disp = *disp;
     p.disp.req_unique = nullptr;
     p.route_only = 1;
-    int cus = 0;
-    if ((st = num_cus(&cus))) return st;
-    return moe::launch_layer(p, cus, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return plan_and_launch(p, (hipStream_t)stream);
 }
 
 int moe_decode_forward(const moe_desc_t* d, int32_t M, const void* x, const void* w_router, const moe_weights_t* w,
@@ -176,9 +195,7 @@ int moe_decode_forward(const moe_desc_t* d, int32_t M, const void* x, const void
     p.topk_w = topk_w_out;
     if (disp) p.disp = *disp;
     if (!req_offsets) p.disp.req_unique = nullptr;
-    int cus = 0;
-    if ((st = num_cus(&cus))) return st;
-    return moe::launch_layer(p, cus, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return plan_and_launch(p, (hipStream_t)stream);
 }
 
 int moe_read_status(void* ws, void* stream, int32_t* status) {
@@ -202,7 +219,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_OFFSETS: return "request offsets out of range or not monotone from 0 to M";
     case MOE_ERR_HIP: return "a HIP runtime call failed";
     case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case MOE_ERR_TIMEOUT: return "a cross-workgroup wait timed out (grid not fully resident?)";
+    case MOE_ERR_TIMEOUT: return "a cross-workgroup wait timed out; that call's y was written as NaN";
     default: return "unknown status";
     }
 }

@@ -27,13 +27,20 @@ constexpr int kMaxPools = kMaxGrid / 8;                   // work pools: one per
 constexpr int kLinePoolC0 = kLineRouted + kRoutedStripes; // [kMaxPools] gate/up chunks handed out
 constexpr int kLinePoolD0 = kLinePoolC0 + kMaxPools;      // [kMaxPools] down chunks handed out
 constexpr int kLineDownDone = kLinePoolD0 + kMaxPools;    // workgroups whose down partials have landed
-constexpr int kSetLines = kLineDownDone + 1;
+constexpr int kLineFault = kLineDownDone + 1;             // nonzero: a wait of this call gave up
+constexpr int kSetLines = kLineFault + 1;
 constexpr int kSetWords = kSetLines * kLineWords;
 
-// workspace header words
-constexpr int kHdrStatus = 0;  // OR of status bits
-constexpr int kHdrCall = 1;    // number of calls made with this workspace
-constexpr int kHdrBytes = 256;
+// Workspace header.  Word 0 is the status word (OR of status bits, cleared by moe_read_status).
+// The call index comes from arrival counters: every workgroup of every call adds 1 to the 64-bit
+// counter of its stripe (b mod kArriveStripes, each on its own line) and divides the old value by
+// the number of workgroups on that stripe.  Reading the index and advancing it are one atomic, so
+// no workgroup can read an index that another workgroup of the same call has already advanced.
+constexpr int kHdrStatus = 0;
+constexpr int kHdrSpin = 1;  // test hook: nonzero = polls before a wait gives up (0: the default, ~1 s)
+constexpr int kArriveStripes = 8;
+constexpr int kHdrArrive = kLineWords;  // word offset of stripe 0; stripe s at kHdrArrive + kLineWords * s
+constexpr int kHdrBytes = 4 * kLineWords * (1 + kArriveStripes);
 
 // status bits set by the kernel
 constexpr uint32_t kStatusOffsets = 1u;
@@ -83,7 +90,11 @@ struct Params {
     int sh_gu_mfma;      // MXFP4: the shared expert's gate/up rows on the matrix cores too
 };
 
-// Enqueues one call.
-hipError_t launch_layer(const Params& p, int num_cus, hipStream_t stream);
+// Fills the launch plan of p (modes, LDS layout) for a grid of G workgroups.  Returns
+// hipErrorInvalidValue when the shape does not fit (LDS); nothing is launched then.
+hipError_t plan_layer(Params& p, int G);
+
+// Enqueues one call planned by plan_layer with the same G.
+hipError_t launch_layer(const Params& p, int G, hipStream_t stream);
 
 }  // namespace moe

@@ -34,6 +34,7 @@
 // counter is bumped only after the stores have completed; there are no cache-wide fences.
 // Every wait is bounded: on a timeout the status word is flagged and the kernel still finishes.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -386,15 +387,35 @@ __device__ __forceinline__ void publish() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
 }
+// Where a wait that gives up reports it: the workspace status word (sticky until moe_read_status)
+// and this call's fault line, which the workgroups read before they write y.  s_fault is the
+// workgroup's own record.  A wait gives up only if the grid is not fully resident or a producer
+// never arrives; its results are then invalid and y is written as NaN.
+struct Fault {
+    uint32_t* status;
+    uint32_t* flag;
+    int spin;  // polls before a wait gives up
+};
+__shared__ uint32_t s_fault;
+// Called by one lane.  The flag has reached memory before this wave issues anything else, so a
+// consumer that sees data this workgroup publishes later also sees the flag.
+__device__ __forceinline__ void raise_timeout(const Fault& f) {
+    __hip_atomic_fetch_or(f.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(f.flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_fault = 1u;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 // Thread 0 waits until *c >= target (bounded); the whole workgroup continues together.
-__device__ __forceinline__ void wait_geq(const uint32_t* c, uint32_t target, uint32_t* status) {
+__device__ __forceinline__ void wait_geq(const uint32_t* c, uint32_t target, const Fault& f) {
     if (threadIdx.x == 0) {
         int i = 0;
-        while (ld_dev(c) < target && i < kSpinLimit) {
+        while (ld_dev(c) < target && i < f.spin) {
             __builtin_amdgcn_s_sleep(1);
             ++i;
         }
-        if (i == kSpinLimit) atomicOr(status, kStatusTimeout);
+        if (i >= f.spin) raise_timeout(f);
     }
     __syncthreads();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -413,7 +434,7 @@ __device__ __forceinline__ uint32_t routed_rows(uint32_t* set) {
 }
 // Every wave of the workgroup continues once the routed SwiGLU rows have reached `target` and the
 // shared expert's counter `sh_target` (bounded).
-__device__ __forceinline__ void wait_units(uint32_t* set, uint32_t target, uint32_t sh_target, uint32_t* status) {
+__device__ __forceinline__ void wait_units(uint32_t* set, uint32_t target, uint32_t sh_target, const Fault& f) {
     if (wave_id() == 0) {
         const int lane = threadIdx.x & 63;
         for (int it = 0;; ++it) {
@@ -421,8 +442,8 @@ __device__ __forceinline__ void wait_units(uint32_t* set, uint32_t target, uint3
             bool ok = rr >= target;
             if (lane == 0) ok = ok && ld_dev(line(set, kLineShared)) >= sh_target;
             if (__ballot(!ok) == 0ull) break;
-            if (it >= kSpinLimit) {
-                if (lane == 0) atomicOr(status, kStatusTimeout);
+            if (it >= f.spin) {
+                if (lane == 0) raise_timeout(f);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -612,11 +633,12 @@ __device__ __forceinline__ void stage_rows_bf16(LDS char* dst, const float* src,
 // lowest index is kept, so ties resolve to the lower id.  The winning lane drops that logit and
 // recomputes its maximum.  Writes ids, logits and softmax-over-the-k weights in order.  Every id
 // written is in [0, E).
-__device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, uint32_t tag, uint32_t* status,
+__device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, uint32_t tag, const Fault& fault,
                                           LDS int* out_id, LDS float* out_w, LDS float* out_v) {
     const int lane = threadIdx.x & 63;
     const __amdgpu_buffer_rsrc_t rs = dev_rsrc(lrow, (uint32_t)E * 8);  // loads past E return 0
     float v[8];
+    bool gave_up = false;
     for (int it = 0;; ++it) {
         bool ok = true;
 #pragma unroll
@@ -627,8 +649,9 @@ __device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, ui
             ok = ok && (8 * lane + 2 * h >= E || q[1] == tag) && (8 * lane + 2 * h + 1 >= E || q[3] == tag);
         }
         if (__ballot(!ok) == 0ull) break;
-        if (it >= kSpinLimit) {
-            if (lane == 0) atomicOr(status, kStatusTimeout);
+        if (it >= fault.spin) {
+            if (lane == 0) raise_timeout(fault);
+            gave_up = true;
             break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -674,7 +697,7 @@ __device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, ui
     if (lane < k) {
         out_id[lane] = my_id;
         out_v[lane] = my_v;
-        out_w[lane] = ex / z;
+        out_w[lane] = gave_up ? __builtin_nanf("") : ex / z;  // NaN weights: every use of this token is invalid
     }
 }
 
@@ -694,7 +717,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // and the batch compaction into this workgroup's LDS tables.  Workgroup 0 (`publish_outputs`)
 // also writes the caller-visible routing outputs.  Returns U.
 __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, LDS char* sel, bool publish_outputs,
-                                                 uint32_t tag, int poll_wave) {
+                                                 uint32_t tag, int poll_wave, const Fault& fault) {
     const int E = p.E, M = p.M, k = p.k, NP = M * k;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const bool has_sh = p.Is > 0;
@@ -711,14 +734,14 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
 
     if (!p.route_delegate) {
         for (int m = wave; m < M; m += kWaves)
-            wave_topk(p.ws.logits + (int64_t)m * logit_stride(E), E, k, tag, p.ws.hdr + kHdrStatus, sid + m * k,
+            wave_topk(p.ws.logits + (int64_t)m * logit_stride(E), E, k, tag, fault, sid + m * k,
                       sw + m * k, sv + m * k);
     } else {
         // workgroup m < M selects token m's experts and publishes them as tagged words; every
         // workgroup then reads the M * k published (id, weight) pairs instead of M * E logits
         const int b = blockIdx.x;
         if (b < M && wave == 0) {
-            wave_topk(p.ws.logits + (int64_t)b * logit_stride(E), E, k, tag, p.ws.hdr + kHdrStatus, sid + b * k,
+            wave_topk(p.ws.logits + (int64_t)b * logit_stride(E), E, k, tag, fault, sid + b * k,
                       sw + b * k, sv + b * k);
             if (lane < k) {
                 uint64_t* dst = p.ws.route + 2 * (int64_t)(b * k + lane);
@@ -752,8 +775,12 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
                     }
                     break;
                 }
-                if (it >= kSpinLimit) {
-                    if (lane == 0) atomicOr(p.ws.hdr + kHdrStatus, kStatusTimeout);
+                if (it >= fault.spin) {
+                    if (lane == 0) raise_timeout(fault);
+                    for (int q = lane; q < NP; q += 64) {  // the routing is invalid: NaN weights
+                        sid[q] = 0;
+                        sw[q] = __builtin_nanf("");
+                    }
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -1726,7 +1753,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     // mode), or null
     const LDS uint8_t* sclw_sh = WF == MOE_FMT_MXFP4 && p.scl_sh ? (const LDS uint8_t*)(lds + p.lds_scl) : nullptr;
     const LDS uint8_t* sclw = WF == MOE_FMT_MXFP4 && p.scl_rt ? (const LDS uint8_t*)(lds + p.lds_scl) + p.scl_sh : nullptr;
-    __shared__ uint32_t s_call;
+    __shared__ uint32_t s_call, s_spin;
     MOE_TRACE_INIT;
     MOE_TRACE(0);
 
@@ -1736,7 +1763,15 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     const int64_t rbI = row_bytes<WF>(I);
 
     // ---- A: call index, token rows, router rows, shared-expert down rows of the slice ----
-    if (threadIdx.x == 0) s_call = ld_dev(p.ws.hdr + kHdrCall);
+    if (threadIdx.x == 0) {
+        // one atomic both reads and advances the index: stripe s counts the workgroups b = s mod 8
+        const int st = b % kArriveStripes;
+        const uint64_t n = (uint64_t)((G - st + kArriveStripes - 1) / kArriveStripes);
+        uint64_t* a = (uint64_t*)(p.ws.hdr + kHdrArrive + kLineWords * st);
+        s_call = (uint32_t)(__hip_atomic_fetch_add(a, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) / n);
+        s_spin = ld_dev(p.ws.hdr + kHdrSpin);
+        s_fault = 0u;
+    }
     async_rows_pitch((char*)xs, (const uint8_t*)p.x, M, H * XB, p.xpitch);
     const int e0 = (int)((int64_t)E * b / G), e1 = (int)((int64_t)E * (b + 1) / G);
     const int nrw = min(e1 - e0, kWaves);  // waves with router rows
@@ -1771,6 +1806,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     MOE_TRACE(1);
     const uint32_t call = s_call;
     uint32_t* set = p.ws.ctr + (int64_t)(call & 1u) * kSetWords;
+    const Fault fault{p.ws.hdr + kHdrStatus, line(set, kLineFault), s_spin ? (int)min(s_spin, (uint32_t)kSpinLimit) : kSpinLimit};
+    // this call's fault line, read after the last wait for other workgroups' data (a producer
+    // raises it before it publishes anything): nonzero -> y is written as NaN
+    uint32_t call_fault = 0u;
     if (b == 0) {
         uint32_t* nxt = p.ws.ctr + (int64_t)((call + 1u) & 1u) * kSetWords;
         for (int l = threadIdx.x; l < kSetLines; l += kThreads) line(nxt, l)[0] = 0u;
@@ -1842,10 +1881,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     // the published expert pairs are polled by the highest wave without shared gate/up tasks (those
     // run on the vector ALU and, at 16 tokens with E2M1 decode, would hold the poll back by µs)
     const int U = route_and_compact(p, tab, (LDS char*)cst, b == 0, call + 1u,
-                                    sh_waves >= kWaves ? kWaves - 1 : kWaves - 1 - sh_waves);
+                                    sh_waves >= kWaves ? kWaves - 1 : kWaves - 1 - sh_waves, fault);
     MOE_TRACE(5);
-    if (b == 0 && threadIdx.x == 0)
-        __hip_atomic_store(p.ws.hdr + kHdrCall, call + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (p.route_only) {
         MOE_TRACE_FLUSH;
         return;
@@ -2049,7 +2086,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     auto shared_down = [&]() {
         if constexpr (WF != MOE_FMT_F32 && NJD <= 3) {
             if (has_sh && nown > 0 && mf_sh && !SLICE) {
-                wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
+                wait_geq(line(set, kLineShared), (uint32_t)Is, fault);
                 const int apitch = 2 * p.act_stride + 16;  // rows 4 banks apart: no conflicts among the B columns
                 stage_rows_bf16((LDS char*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is, apitch);
                 __syncthreads();
@@ -2068,7 +2105,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             }
         }
         if (has_sh && nown > 0 && !SLICE && !mf_sh) {
-            wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
+            wait_geq(line(set, kLineShared), (uint32_t)Is, fault);
             stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
             __syncthreads();
             const uint8_t* dsb = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
@@ -2118,7 +2155,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 t.acts = (const LDS float*)xs + (int64_t)t.prow * astride;
             };
             auto ready = [&]() {
-                wait_units(set, (uint32_t)(U * I), has_sh ? (uint32_t)Is : 0u, p.ws.hdr + kHdrStatus);
+                wait_units(set, (uint32_t)(U * I), has_sh ? (uint32_t)Is : 0u, fault);
+                call_fault = ld_dev(fault.flag);  // used at the y write, long after it lands
                 MOE_TRACE(9);
                 stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act, astride, NP + (has_sh ? M : 0), astride);
                 __syncthreads();
@@ -2130,7 +2168,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     const int apitch = 2 * astride + 16;  // rows 4 banks apart: no conflicts among the B columns
                     const int nsh = has_sh ? 1 : 0;  // the shared unit first: it needs no wait
                     if (has_sh) {
-                        wait_geq(line(set, kLineShared), (uint32_t)Is, p.ws.hdr + kHdrStatus);
+                        wait_geq(line(set, kLineShared), (uint32_t)Is, fault);
                         stage_rows_b16((LDS char*)xs + (int64_t)NP * apitch, act16 + (int64_t)NP * astride, astride,
                                         M, Is, apitch);
                         __syncthreads();
@@ -2160,7 +2198,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                         t.acts = (const LDS char*)xs + (int64_t)t.prow * apitch;
                     };
                     auto ready_bf16 = [&]() {  // the shared expert's rows were staged above
-                        wait_units(set, (uint32_t)(U * I), 0u, p.ws.hdr + kHdrStatus);
+                        wait_units(set, (uint32_t)(U * I), 0u, fault);
+                        call_fault = ld_dev(fault.flag);  // used at the y write, long after it lands
                         MOE_TRACE(9);
                         stage_rows_b16((LDS char*)xs, act16, astride, NP, astride, apitch);
                         if constexpr (WF == MOE_FMT_BF16)
@@ -2176,6 +2215,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     MOE_TRACE(11);
                     const LDS int* s_pair = tab + kTabPair;
                     const LDS float* s_roww = (const LDS float*)(tab + kTabRowW);
+                    const bool bad = (call_fault | s_fault) != 0u;
                     for (int i = threadIdx.x; i < M * nown; i += kThreads) {
                         const int m = i / nown, hh = i - m * nown, h = h0 + hh;
                         float acc = 0.0f;
@@ -2184,7 +2224,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                             acc = fmaf(s_roww[row], pst[row * nown + hh], acc);
                         }
                         if (has_sh) acc += pst[(NP + m) * nown + hh];
-                        ((uint16_t*)p.y)[(int64_t)m * H + h] = f32_to_bf16_rne(acc);
+                        ((uint16_t*)p.y)[(int64_t)m * H + h] = f32_to_bf16_rne(bad ? __builtin_nanf("") : acc);
                     }
                     MOE_TRACE_FLUSH;
                     return;
@@ -2197,6 +2237,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             // ---- E (slice mode): combine from LDS ----
             const LDS int* s_pair = tab + kTabPair;
             const LDS float* s_roww = (const LDS float*)(tab + kTabRowW);
+            const bool bad = (call_fault | s_fault) != 0u;
             for (int i = threadIdx.x; i < M * nown; i += kThreads) {
                 const int m = i / nown, hh = i - m * nown, h = h0 + hh;
                 float acc = 0.0f;
@@ -2205,6 +2246,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     acc = fmaf(s_roww[row], pst[row * nown + hh], acc);
                 }
                 if (has_sh) acc += pst[(NP + m) * nown + hh];
+                if (bad) acc = __builtin_nanf("");
                 if constexpr (AF == MOE_FMT_F32)
                     ((float*)p.y)[(int64_t)m * H + h] = acc;
                 else
@@ -2285,7 +2327,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 t.acts = (const LDS float*)xs + aoff[sg];
             };
             auto ready = [&]() {
-                wait_units(set, (uint32_t)(U * I), 0u, p.ws.hdr + kHdrStatus);
+                wait_units(set, (uint32_t)(U * I), 0u, fault);
                 MOE_TRACE(9);
                 for (int sg = 0; sg < nseg; ++sg) {
                     const int u = sg_u[sg];
@@ -2319,7 +2361,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 const int pb = min(hb, pa + rows_per_pass);
                 auto ready = [&]() {
                     if (!staged) {
-                        wait_units(set, (uint32_t)(U * I), 0u, p.ws.hdr + kHdrStatus);
+                        wait_units(set, (uint32_t)(U * I), 0u, fault);
                         if (first) MOE_TRACE(9);
                         stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)row0 * p.act_stride, p.act_stride, t, I);
                         __syncthreads();
@@ -2384,8 +2426,9 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
 
     // ---- E: combine this workgroup's slice of y ----
     if (nown > 0) {
-        wait_geq(line(set, kLineDownDone), (uint32_t)G, p.ws.hdr + kHdrStatus);
+        wait_geq(line(set, kLineDownDone), (uint32_t)G, fault);
         MOE_TRACE(12);
+        call_fault = ld_dev(fault.flag);  // in flight with the partials' loads
         const LDS int* s_pair = tab + kTabPair;
         const LDS float* s_roww = (const LDS float*)(tab + kTabRowW);
         for (int i = threadIdx.x; i < M * nown; i += kThreads) {
@@ -2396,6 +2439,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 acc = fmaf(s_roww[row], ld_dev(p.ws.part + (int64_t)row * H + h), acc);
             }
             if (has_sh) acc += ysh[m * nown + hh];
+            if ((call_fault | s_fault) != 0u) acc = __builtin_nanf("");
             if constexpr (AF == MOE_FMT_F32)
                 ((float*)p.y)[(int64_t)m * H + h] = acc;
             else
@@ -2411,10 +2455,26 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
 
 int round16(int64_t v) { return (int)((v + 15) / 16 * 16); }
 
-template <int AF, int WF, int NJ, int NJD>
-hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
+constexpr int kLdsBudget = kLdsBytes - 512;  // dynamic LDS; the rest holds the static LDS variables
+
+// Chunks per lane: NJ for the router and gate/up rows (K = H), NJD for the down rows (K = I, Is).
+// Two instances per format: the Ling shapes (H <= 2560, I, Is <= 768) and small layers
+// (H <= 512, I, Is <= 256); the host rejects larger shapes.
+template <int WF>
+void chunks(const Params& p, int* nj, int* njd) {
+    const int ka = std::max(p.I, p.Is);
+    *nj = (p.H / Geo<WF>::EPC + Geo<WF>::LPR_G - 1) / Geo<WF>::LPR_G;
+    *njd = (ka / Geo<WF>::EPC + Geo<WF>::LPR_D - 1) / Geo<WF>::LPR_D;
+}
+
+// The launch plan of one call: modes and the LDS layout, on the host.
+template <int AF, int WF>
+hipError_t plan_t(Params& p, int G) {
     constexpr int XB = AF == MOE_FMT_F32 ? 4 : 2;
-    const int G = std::min(num_cus, kMaxGrid);
+    int nj, njd;
+    chunks<WF>(p, &nj, &njd);
+    const bool fits = (nj <= 1 && njd <= 1) || (WF != MOE_FMT_F32 && nj <= 5 && njd <= 3);
+    if (!fits) return hipErrorInvalidValue;  // no kernel instance for this shape
     const int M = p.M, H = p.H;
     const int64_t NP = (int64_t)p.k * M;
     const int ka = std::max(p.I, p.Is);
@@ -2423,14 +2483,14 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
     // and for MXFP4 weights while all pair rows' SwiGLU outputs fit in LDS as bfloat16 (the slices'
     // 4-bit down rows mostly fit the LDS window; no partial write-out, no down barrier):
     // then every workgroup stages all pair rows' SwiGLU outputs; otherwise unit-major down rows
-    const bool mx_slice = WF == MOE_FMT_MXFP4 && NJD <= 3 && nown <= 16 && (NP + M) * (ka * 2 + 16) <= 96 * 1024;
+    const bool mx_slice = WF == MOE_FMT_MXFP4 && njd <= 3 && nown <= 16 && (NP + M) * (ka * 2 + 16) <= 96 * 1024;
     p.slice_mode = (NP <= 16 || mx_slice) ? 1 : 0;
     // from three tokens on, the M * E logits that every workgroup would read are more polling traffic
     // than one extra hand-off costs: workgroup m selects token m's experts and publishes them
     p.route_delegate = (!p.route_only && M >= 3 && M <= G) ? 1 : 0;
     // slice mode on the matrix cores (bf16 and MXFP4 weights, up to 16 rows per workgroup, K <= 768):
     // bfloat16 SwiGLU rows, swizzled weight windows
-    p.sh_mfma = (WF != MOE_FMT_F32 && NJD <= 3 && nown <= 16) ? 1 : 0;
+    p.sh_mfma = (WF != MOE_FMT_F32 && njd <= 3 && nown <= 16) ? 1 : 0;
     p.slice_mfma = (p.slice_mode && p.sh_mfma) ? 1 : 0;
     // staging area: routing scratch; routed SwiGLU results of one workgroup's tasks; down partials
     // (slice mode: [NP][nown]; unit-major: any size, larger means fewer passes)
@@ -2489,32 +2549,56 @@ hipError_t launch_t(Params p, int num_cus, hipStream_t s) {
         if (p.slice_mfma && (p.I / 32) % 4 == 0) p.scl_rt = (int)round16(units * nown * (p.I / 32));
     }
     p.lds_dn = p.lds_scl + p.scl_sh + p.scl_rt;
-    const int budget = kLdsBytes - 512;  // room for the static LDS variables
+    const int budget = kLdsBudget;
     p.dn_bytes = p.route_only ? 0 : std::max(0, (budget - p.lds_dn) / 16 * 16);
     p.lds_total = p.lds_dn + p.dn_bytes;
-    if (p.lds_total > budget) return hipErrorInvalidConfiguration;
+    if (p.lds_total > budget) return hipErrorInvalidValue;
+    return hipSuccess;
+}
+
+constexpr int kMaxDevices = 64;
+
+// Per device and kernel instance, once: allow the whole LDS budget and check that one workgroup
+// fits a CU.  Idempotent, so concurrent first calls are harmless.
+template <typename K>
+hipError_t prepare(K kern, int dev) {
+    static std::atomic<int> state[kMaxDevices];  // 0 unknown, 1 ready, 2 failed
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int st = state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        st = 2;
+        if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) ==
+            hipSuccess) {
+            int occ = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, kThreads, kLdsBudget) ==
+                    hipSuccess &&
+                occ >= 1)
+                st = 1;
+        }
+        state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? hipSuccess : hipErrorInvalidConfiguration;
+}
+
+template <int AF, int WF, int NJ, int NJD>
+hipError_t launch_t(const Params& p, int G, int dev, hipStream_t s) {
     auto go = [&](auto kern) -> hipError_t {
-        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_total);
-        int occ = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, kThreads, p.lds_total) != hipSuccess)
-            return hipErrorInvalidValue;
-        if (occ < 1) return hipErrorInvalidConfiguration;
+        const hipError_t e = prepare(kern, dev);
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), p.lds_total, s, p);
         return hipGetLastError();
     };
     return p.slice_mode ? go(k_layer<AF, WF, NJ, NJD, 1>) : go(k_layer<AF, WF, NJ, NJD, 0>);
 }
 
-// chunks per lane: NJ for the router and gate/up rows (K = H), NJD for the down rows (K = I, Is)
 template <int AF, int WF>
-hipError_t launch_shape(const Params& p, int num_cus, hipStream_t s) {
-    const int nj = (p.H / Geo<WF>::EPC + Geo<WF>::LPR_G - 1) / Geo<WF>::LPR_G;
-    const int ka = std::max(p.I, p.Is);
-    const int njd = (ka / Geo<WF>::EPC + Geo<WF>::LPR_D - 1) / Geo<WF>::LPR_D;
-    if (nj <= 1 && njd <= 1) return launch_t<AF, WF, 1, 1>(p, num_cus, s);
-    if (nj <= 5 && njd <= 3) return launch_t<AF, WF, 5, 3>(p, num_cus, s);
-    if (nj <= 8 && njd <= 8) return launch_t<AF, WF, 8, 8>(p, num_cus, s);
-    return hipErrorInvalidConfiguration;
+hipError_t launch_fmt(const Params& p, int G, int dev, hipStream_t s) {
+    int nj, njd;
+    chunks<WF>(p, &nj, &njd);
+    if (nj <= 1 && njd <= 1) return launch_t<AF, WF, 1, 1>(p, G, dev, s);
+    if constexpr (WF != MOE_FMT_F32)
+        if (nj <= 5 && njd <= 3) return launch_t<AF, WF, 5, 3>(p, G, dev, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -2525,10 +2609,19 @@ extern "C" int moe_trace_set(void* buf) {
 }
 #endif
 
-hipError_t launch_layer(const Params& p, int num_cus, hipStream_t s) {
-    if (p.act_fmt == MOE_FMT_F32) return launch_shape<MOE_FMT_F32, MOE_FMT_F32>(p, num_cus, s);
-    if (p.w_fmt == MOE_FMT_BF16) return launch_shape<MOE_FMT_BF16, MOE_FMT_BF16>(p, num_cus, s);
-    return launch_shape<MOE_FMT_BF16, MOE_FMT_MXFP4>(p, num_cus, s);
+hipError_t plan_layer(Params& p, int G) {
+    if (G < 1 || G > kMaxGrid) return hipErrorInvalidValue;
+    if (p.act_fmt == MOE_FMT_F32) return plan_t<MOE_FMT_F32, MOE_FMT_F32>(p, G);
+    if (p.w_fmt == MOE_FMT_BF16) return plan_t<MOE_FMT_BF16, MOE_FMT_BF16>(p, G);
+    return plan_t<MOE_FMT_BF16, MOE_FMT_MXFP4>(p, G);
+}
+
+hipError_t launch_layer(const Params& p, int G, hipStream_t s) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (p.act_fmt == MOE_FMT_F32) return launch_fmt<MOE_FMT_F32, MOE_FMT_F32>(p, G, dev, s);
+    if (p.w_fmt == MOE_FMT_BF16) return launch_fmt<MOE_FMT_BF16, MOE_FMT_BF16>(p, G, dev, s);
+    return launch_fmt<MOE_FMT_BF16, MOE_FMT_MXFP4>(p, G, dev, s);
 }
 
 }  // namespace moe

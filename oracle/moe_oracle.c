@@ -216,53 +216,79 @@ void oracle_route(const oracle_desc* d, int32_t M, const void* x, const void* wr
     free(xm);
 }
 
-/* The whole layer (steps 1-5) for M tokens; y [M][H] fp64.  Tokens are independent, so they may
-   be spread over threads (nthreads <= 0: the OpenMP default) without changing any result.
-   ids/w/gap as in oracle_route (nullable). */
+/* The whole layer (steps 1-5) for M tokens; y [M][H] fp64.  ids/w/gap as in oracle_route
+   (nullable).  Work is spread over threads (nthreads <= 0: the OpenMP default) without changing
+   any result: the routing of every token first, then each (token, expert) output o_{m,j} on its
+   own (j = k: the shared expert), then per token the same sum in the same order,
+   y = ((w_0 o_0 + w_1 o_1) + ... + w_{k-1} o_{k-1}) + o_shared. */
 void oracle_moe_forward(const oracle_desc* d, const oracle_weights* W, int32_t M, const void* x,
                         const void* wr, double* y, int32_t* ids_out, double* w_out, double* gap_out,
                         int32_t nthreads) {
     const int H = d->hidden, E = d->num_experts, k = d->top_k, I = d->inter, Is = d->shared_inter;
     const int wf = d->weight_fmt;
+    const int units = k + 1; /* per token: k routed experts and the shared one */
     omat Wr = {d->act_fmt, wr, NULL, E, H};
+    double* xs = (double*)malloc(sizeof(double) * (size_t)M * H);
+    double* ws = (double*)malloc(sizeof(double) * (size_t)M * k);
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)M * k);
+    double* gaps = (double*)malloc(sizeof(double) * (size_t)M);
+    double* o = (double*)malloc(sizeof(double) * (size_t)M * units * H);
 #ifdef _OPENMP
     if (nthreads <= 0) nthreads = omp_get_max_threads();
+#endif
+    /* steps 1-2 per token */
+#ifdef _OPENMP
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
 #endif
     for (int m = 0; m < M; ++m) {
-        double* xm = (double*)malloc(sizeof(double) * H);
-        double* o = (double*)malloc(sizeof(double) * H);
-        double* w = (double*)malloc(sizeof(double) * k);
-        int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * k);
-        double gap;
-        load_row(d->act_fmt, x, m, H, xm);
-        route_token(d, xm, &Wr, NULL, ids, w, &gap);
-        double* ym = y + (int64_t)m * H;
-        for (int h = 0; h < H; ++h) ym[h] = 0.0;
-        for (int j = 0; j < k; ++j) {
-            omat Wg = expert_mat(wf, W->gate, W->gate_s, ids[j], I, H);
-            omat Wu = expert_mat(wf, W->up, W->up_s, ids[j], I, H);
-            omat Wd = expert_mat(wf, W->down, W->down_s, ids[j], H, I);
-            swiglu_expert(&Wg, &Wu, &Wd, xm, o);
-            for (int h = 0; h < H; ++h) ym[h] += w[j] * o[h];
-        }
-        if (Is > 0) {
+        load_row(d->act_fmt, x, m, H, xs + (int64_t)m * H);
+        route_token(d, xs + (int64_t)m * H, &Wr, NULL, ids + (int64_t)m * k, ws + (int64_t)m * k, gaps + m);
+    }
+    /* steps 3-4: every expert output of every token */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int q = 0; q < M * units; ++q) {
+        const int m = q / units, j = q % units;
+        const double* xm = xs + (int64_t)m * H;
+        double* oq = o + (int64_t)q * H;
+        if (j < k) {
+            const int32_t e = ids[(int64_t)m * k + j];
+            omat Wg = expert_mat(wf, W->gate, W->gate_s, e, I, H);
+            omat Wu = expert_mat(wf, W->up, W->up_s, e, I, H);
+            omat Wd = expert_mat(wf, W->down, W->down_s, e, H, I);
+            swiglu_expert(&Wg, &Wu, &Wd, xm, oq);
+        } else if (Is > 0) {
             omat Sg = expert_mat(wf, W->sh_gate, W->sh_gate_s, 0, Is, H);
             omat Su = expert_mat(wf, W->sh_up, W->sh_up_s, 0, Is, H);
             omat Sd = expert_mat(wf, W->sh_down, W->sh_down_s, 0, H, Is);
-            swiglu_expert(&Sg, &Su, &Sd, xm, o);
-            for (int h = 0; h < H; ++h) ym[h] += o[h];
+            swiglu_expert(&Sg, &Su, &Sd, xm, oq);
+        }
+    }
+    /* step 5 per token */
+    for (int m = 0; m < M; ++m) {
+        double* ym = y + (int64_t)m * H;
+        for (int h = 0; h < H; ++h) ym[h] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            const double wj = ws[(int64_t)m * k + j];
+            const double* oj = o + ((int64_t)m * units + j) * H;
+            for (int h = 0; h < H; ++h) ym[h] += wj * oj[h];
+        }
+        if (Is > 0) {
+            const double* osh = o + ((int64_t)m * units + k) * H;
+            for (int h = 0; h < H; ++h) ym[h] += osh[h];
         }
         if (ids_out)
-            for (int j = 0; j < k; ++j) ids_out[(int64_t)m * k + j] = ids[j];
+            for (int j = 0; j < k; ++j) ids_out[(int64_t)m * k + j] = ids[(int64_t)m * k + j];
         if (w_out)
-            for (int j = 0; j < k; ++j) w_out[(int64_t)m * k + j] = w[j];
-        if (gap_out) gap_out[m] = gap;
-        free(xm);
-        free(o);
-        free(w);
-        free(ids);
+            for (int j = 0; j < k; ++j) w_out[(int64_t)m * k + j] = ws[(int64_t)m * k + j];
+        if (gap_out) gap_out[m] = gaps[m];
     }
+    free(xs);
+    free(ws);
+    free(ids);
+    free(gaps);
+    free(o);
 }
 
 /* Dispatch compaction over the (token, slot) pairs of a batch.

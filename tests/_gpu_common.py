@@ -21,8 +21,13 @@ TOL = {synth.F32: 1e-4, synth.BF16: 2e-2, synth.MXFP4: 5e-2}
 W_TOL = 1e-5  # routing weights, absolute
 
 
+SUMMARY = []  # every logged line, repeated in the run's terminal summary (conftest)
+
+
 def log(*a):
-    print("[gpu-test]", *a, flush=True)
+    line = " ".join(str(x) for x in a)
+    SUMMARY.append(line)
+    print("[gpu-test]", line, flush=True)
 
 
 def _layer_key(cfg):

@@ -44,8 +44,17 @@ def test_workspace_bytes():
     assert mdl.moe_workspace_bytes(ling(max_tokens=1)) < n
     for bad in (ling(top_k=0), ling(top_k=600), ling(num_experts=513), ling(hidden=2564), ling(max_tokens=17),
                 ling(act_format=mdl.MOE_FMT_F32), ling(weight_format=7), ling(inter=0),
-                ling(weight_format=mdl.MOE_FMT_MXFP4, hidden=2560 + 8), ling(hidden=8192)):
+                ling(weight_format=mdl.MOE_FMT_MXFP4, hidden=2560 + 8), ling(hidden=8192),
+                # beyond the kernel instances: no accepted shape reaches untested code
+                ling(hidden=2560 + 32), ling(inter=768 + 32), ling(shared_inter=1024),
+                ling(weight_format=mdl.MOE_FMT_MXFP4, hidden=3072),
+                ling(act_format=mdl.MOE_FMT_F32, weight_format=mdl.MOE_FMT_F32, hidden=264, inter=64,
+                     shared_inter=64),
+                ling(act_format=mdl.MOE_FMT_F32, weight_format=mdl.MOE_FMT_F32, hidden=128, inter=264,
+                     shared_inter=64)):
         assert mdl.moe_workspace_bytes(bad) == 0
+    assert mdl.moe_workspace_bytes(ling(act_format=mdl.MOE_FMT_F32, weight_format=mdl.MOE_FMT_F32, hidden=256,
+                                        inter=256, shared_inter=256)) > 0
 
 
 def call_route(desc, M=1, x=FAKE, wr=FAKE, ids=FAKE, w=FAKE, ws=FAKE, ws_bytes=1 << 30):

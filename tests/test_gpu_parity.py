@@ -41,7 +41,8 @@ SMALL = [
     small("bf16_k_eq_E", E=8, k=8, lens=(3,)),
     small("bf16_k16", E=128, k=16, lens=(16,)),
     small("bf16_E512", E=512, k=8, lens=(8,)),
-    # top-k split over several waves per token (parts of 64 * L experts, then a merge pass)
+    # many experts per top-k wave (one wave per token, eight logits per lane), every workgroup
+    # redoing the top-k below three tokens and the delegated top-k from three tokens on
     small("bf16_E512_m2", E=512, k=8, lens=(2,)),
     small("bf16_E384_m3", E=384, k=6, lens=(3,)),
     small("bf16_E512_k16_m1", E=512, k=16, lens=(1,), recipe="iid"),
@@ -113,6 +114,72 @@ def test_deterministic_and_permutation_equivariant():
     assert torch.equal(yp, y1[perm])
     for m in range(case.M):
         assert set(idsp[m].tolist()) == set(ids1[perm[m]].tolist())
+
+
+@pytest.mark.parametrize("fmt", [BF16, MXFP4], ids=["bf16", "mxfp4"])
+def test_permutation_equivariant_slice_mode(fmt):
+    """Few pair rows: every workgroup computes its own columns of every unit on the matrix cores.
+    The result is bit-identical across token orders (fixed operand order per token column)."""
+    cfg = small("perm_slice", fmt, k=4, lens=(4,))
+    case = G.Case(cfg)
+    y1, ids1, _ = case.run()
+    perm = torch.tensor([2, 0, 3, 1], device="cuda")
+    yp, idsp, _ = case.run(x=case.x[perm].contiguous())
+    torch.cuda.synchronize()
+    err, _ = G.y_error(y1, case.y_ref)
+    G.log("perm_slice", synth.FORMAT_NAMES[fmt], "err/rms=%.3e" % err)
+    assert err <= G.TOL[fmt]
+    assert torch.equal(yp, y1[perm])
+    for m in range(case.M):
+        assert set(idsp[m].tolist()) == set(ids1[perm[m]].tolist())
+
+
+@pytest.mark.parametrize("lens", [(1,), (6,)], ids=["m1_slice", "m6_unit_major"])
+def test_repeated_calls_fewer_experts_than_cus(lens):
+    """E = 64 routed experts on 256 compute units: most workgroups own no router row.  Ten calls in
+    a row on one workspace, alternating two token batches, each against the oracle."""
+    cfg = small("rep", lens=lens, recipe="iid" if lens == (1,) else "shared_base")
+    a = G.Case(cfg)
+    b = G.Case(cfg, x_host=G.accepted_hidden(cfg, a.layer, start=50)[0])
+    b.ws = a.ws
+    for i in range(10):
+        c = a if i % 2 == 0 else b
+        y, ids, w = c.run()
+        torch.cuda.synchronize()
+        G.check_routing(ids, w, c.ids_ref, c.w_ref)
+        err, _ = G.y_error(y, c.y_ref)
+        assert err <= G.TOL[BF16], (i, err)
+    assert mdl.moe_read_status(a.ws) == mdl.MOE_OK
+
+
+@pytest.mark.parametrize("lens", [(1,), (6,)], ids=["m1_slice", "m6_unit_major"])
+def test_wait_timeout_writes_nan(lens):
+    """A wait that gives up leaves no output that looks valid.  Forced from the host: the workspace
+    header's spin-limit word is set to 16 polls and the arrival counter of stripe 0 is advanced, so
+    the workgroups on that stripe take another call index than the rest and their tags and counter
+    sets never meet.  Every wait is bounded, so every workgroup exits; y and the routing weights
+    come out NaN and the status word reads MOE_ERR_TIMEOUT.  A fresh workspace then works."""
+    cfg = small("timeout", lens=lens, recipe="iid" if lens == (1,) else "shared_base")
+    case = G.Case(cfg)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n0 = (min(cus, 1024) + 7) // 8  # workgroups on arrival stripe 0
+    words = case.ws.view(torch.int32)
+    words[1] = 16  # spin-limit test hook
+    case.ws.view(torch.int64)[256 // 8] = 3 * n0  # stripe 0 takes call index 3, the others 0
+    torch.cuda.synchronize()
+    y, ids, w = case.run()
+    torch.cuda.synchronize()
+    G.log("timeout", lens, "nan y: %d of %d" % (int(torch.isnan(y.float()).sum()), y.numel()))
+    assert mdl.moe_read_status(case.ws) == mdl.MOE_ERR_TIMEOUT
+    assert torch.isnan(y.float()).all()
+    assert torch.isnan(w).all()
+    assert int(ids.min()) >= 0 and int(ids.max()) < cfg.num_experts
+    case.ws = dev.workspace(case.desc)
+    y, ids, w = case.run()
+    torch.cuda.synchronize()
+    assert mdl.moe_read_status(case.ws) == mdl.MOE_OK
+    G.check_routing(ids, w, case.ids_ref, case.w_ref)
+    assert G.y_error(y, case.y_ref)[0] <= G.TOL[BF16]
 
 
 def test_identical_tokens_share_experts():

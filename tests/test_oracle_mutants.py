@@ -12,16 +12,16 @@ from tests import test_oracle_pins as P
 
 MUTANTS = {
     "silu_sign": ("a[r] = g[r] / (1.0 + exp(-g[r])) * v[r];", "a[r] = g[r] / (1.0 + exp(g[r])) * v[r];"),
-    "no_shared": ("            for (int h = 0; h < H; ++h) ym[h] += o[h];\n", "\n"),
+    "no_shared": ("            for (int h = 0; h < H; ++h) ym[h] += osh[h];\n", "\n"),
     "no_renorm": ("w[j] = p[j].v / kept;", "w[j] = p[j].v;"),
     "tie_order": ("return (x->id > y->id) - (x->id < y->id);", "return (x->id < y->id) - (x->id > y->id);"),
     "nibble_swap": ("(c & 1) ? (byte >> 4) : (byte & 15)", "(c & 1) ? (byte & 15) : (byte >> 4)"),
     "scale_index": ("A->scales[r * (A->cols / 32) + c / 32]", "A->scales[r * (A->cols / 32) + c / 64]"),
-    "gate_up_swapped": ("omat Wg = expert_mat(wf, W->gate, W->gate_s, ids[j], I, H);",
-                        "omat Wg = expert_mat(wf, W->up, W->up_s, ids[j], I, H);"),
-    "no_route_weight": ("ym[h] += w[j] * o[h];", "ym[h] += o[h];"),
-    "wrong_expert": ("omat Wd = expert_mat(wf, W->down, W->down_s, ids[j], H, I);",
-                     "omat Wd = expert_mat(wf, W->down, W->down_s, ids[0], H, I);"),
+    "gate_up_swapped": ("omat Wg = expert_mat(wf, W->gate, W->gate_s, e, I, H);",
+                        "omat Wg = expert_mat(wf, W->up, W->up_s, e, I, H);"),
+    "no_route_weight": ("ym[h] += wj * oj[h];", "ym[h] += oj[h];"),
+    "wrong_expert": ("omat Wd = expert_mat(wf, W->down, W->down_s, e, H, I);",
+                     "omat Wd = expert_mat(wf, W->down, W->down_s, ids[(int64_t)m * k], H, I);"),
     "bf16_shift": ("return dec_f32((uint32_t)b << 16);", "return dec_f32((uint32_t)b << 15);"),
     "e2m1_bias": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e - 2)"),
     "compact_slot": ("row_slot[row] = p % k;", "row_slot[row] = p / k;"),
