@@ -32,15 +32,15 @@ constexpr int kSetLines = kLineFault + 1;
 constexpr int kSetWords = kSetLines * kLineWords;
 
 // Workspace header.  Word 0 is the status word (OR of status bits, cleared by moe_read_status).
-// The call index comes from arrival counters: every workgroup of every call adds 1 to the 64-bit
-// counter of its stripe (b mod kArriveStripes, each on its own line) and divides the old value by
-// the number of workgroups on that stripe.  Reading the index and advancing it are one atomic, so
-// no workgroup can read an index that another workgroup of the same call has already advanced.
+// The call index is counted per workgroup: workgroup b reads its own counter at word
+// kHdrCall + kCallStride * b and stores it plus one.  No other workgroup touches that word and the
+// next call reads it only after this kernel has ended, so every workgroup of a call takes the same
+// index (each has been launched once per call) and no read can race an advance.
 constexpr int kHdrStatus = 0;
 constexpr int kHdrSpin = 1;  // test hook: nonzero = polls before a wait gives up (0: the default, ~1 s)
-constexpr int kArriveStripes = 8;
-constexpr int kHdrArrive = kLineWords;  // word offset of stripe 0; stripe s at kHdrArrive + kLineWords * s
-constexpr int kHdrBytes = 4 * kLineWords * (1 + kArriveStripes);
+constexpr int kHdrCall = kLineWords;
+constexpr int kCallStride = 4;  // words between two workgroups' counters
+constexpr int kHdrBytes = 4 * (kHdrCall + kCallStride * kMaxGrid);
 
 // status bits set by the kernel
 constexpr uint32_t kStatusOffsets = 1u;

@@ -1763,12 +1763,9 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     const int64_t rbI = row_bytes<WF>(I);
 
     // ---- A: call index, token rows, router rows, shared-expert down rows of the slice ----
+    uint32_t* const call_ctr = p.ws.hdr + kHdrCall + kCallStride * b;  // this workgroup's own call counter
     if (threadIdx.x == 0) {
-        // one atomic both reads and advances the index: stripe s counts the workgroups b = s mod 8
-        const int st = b % kArriveStripes;
-        const uint64_t n = (uint64_t)((G - st + kArriveStripes - 1) / kArriveStripes);
-        uint64_t* a = (uint64_t*)(p.ws.hdr + kHdrArrive + kLineWords * st);
-        s_call = (uint32_t)(__hip_atomic_fetch_add(a, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) / n);
+        s_call = ld_dev(call_ctr);
         s_spin = ld_dev(p.ws.hdr + kHdrSpin);
         s_fault = 0u;
     }
@@ -1805,6 +1802,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     __syncthreads();
     MOE_TRACE(1);
     const uint32_t call = s_call;
+    if (threadIdx.x == 0) __hip_atomic_store(call_ctr, call + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t* set = p.ws.ctr + (int64_t)(call & 1u) * kSetWords;
     const Fault fault{p.ws.hdr + kHdrStatus, line(set, kLineFault), s_spin ? (int)min(s_spin, (uint32_t)kSpinLimit) : kSpinLimit};
     // this call's fault line, read after the last wait for other workgroups' data (a producer

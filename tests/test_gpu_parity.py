@@ -155,17 +155,17 @@ def test_repeated_calls_fewer_experts_than_cus(lens):
 @pytest.mark.parametrize("lens", [(1,), (6,)], ids=["m1_slice", "m6_unit_major"])
 def test_wait_timeout_writes_nan(lens):
     """A wait that gives up leaves no output that looks valid.  Forced from the host: the workspace
-    header's spin-limit word is set to 16 polls and the arrival counter of stripe 0 is advanced, so
-    the workgroups on that stripe take another call index than the rest and their tags and counter
+    header's spin-limit word is set to 16 polls and the call counters of every eighth workgroup are
+    advanced, so those workgroups take another call index than the rest and their tags and counter
     sets never meet.  Every wait is bounded, so every workgroup exits; y and the routing weights
     come out NaN and the status word reads MOE_ERR_TIMEOUT.  A fresh workspace then works."""
     cfg = small("timeout", lens=lens, recipe="iid" if lens == (1,) else "shared_base")
     case = G.Case(cfg)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    n0 = (min(cus, 1024) + 7) // 8  # workgroups on arrival stripe 0
+    cus = min(torch.cuda.get_device_properties(0).multi_processor_count, 1024)
     words = case.ws.view(torch.int32)
     words[1] = 16  # spin-limit test hook
-    case.ws.view(torch.int64)[256 // 8] = 3 * n0  # stripe 0 takes call index 3, the others 0
+    for b in range(0, cus, 8):  # workgroup b's call counter: word 64 + 4 b
+        words[64 + 4 * b] = 3
     torch.cuda.synchronize()
     y, ids, w = case.run()
     torch.cuda.synchronize()
