@@ -73,8 +73,10 @@ typedef enum {
                                are not 0 = o[0] <= o[1] <= ... <= o[R] = M */
     MOE_ERR_HIP = -6,       /* a HIP runtime call failed */
     MOE_ERR_ALIGN = -7,     /* a pointer is not 16-byte aligned */
-    MOE_ERR_TIMEOUT = -8    /* device status only: a cross-workgroup wait gave up; that call's y
+    MOE_ERR_TIMEOUT = -8,   /* device status only: a cross-workgroup wait gave up; that call's y
                                was written as NaN (happens only if calls overlap on one device) */
+    MOE_ERR_SCRATCH = -9    /* moe_decode_forward_noalloc: the description needs more than its fixed
+                               scratch (max_tokens * (top_k + 1) > 144 pair rows) */
 } moe_status_t;
 
 /* Largest supported values (checked on the host). */
@@ -158,6 +160,24 @@ int moe_decode_forward(const moe_desc_t* d, int32_t M, const void* x, const void
                        const moe_weights_t* w, const int32_t* req_offsets, int32_t R, void* y,
                        int32_t* topk_ids_out, float* topk_w_out, const moe_dispatch_t* disp, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under hipGraph capture, tight serving loops,
+   harnesses that forbid hipMalloc): moe_decode_forward without a workspace argument.  The library's
+   own per-device scratch of MOE_NOALLOC_SCRATCH_BYTES (a static device array, held by every GPU the
+   library runs on until the process ends) takes the workspace's place, so nothing is allocated by
+   this call or by the library.  It serves descriptions with max_tokens * (top_k + 1) <= 144 pair
+   rows (every Ling-shaped workload up to 16 tokens at top-8); larger ones return MOE_ERR_SCRATCH
+   before anything is enqueued.  The first call on a device also enqueues, on `stream`, a clear of
+   the scratch's counters.  All calls on one GPU share its scratch and its state carries over from
+   call to call, so these calls must not overlap on one device (the same rule as for every call of
+   this library); overlapping calls race.  Arguments, outputs and results are those of
+   moe_decode_forward; the device status word of the scratch is not readable by the caller (a wait
+   that gives up still writes y as NaN). */
+#define MOE_NOALLOC_SCRATCH_BYTES 2138112
+int moe_decode_forward_noalloc(const moe_desc_t* d, int32_t M, const void* x, const void* w_router,
+                               const moe_weights_t* w, const int32_t* req_offsets, int32_t R, void* y,
+                               int32_t* topk_ids_out, float* topk_w_out, const moe_dispatch_t* disp,
+                               void* stream);
 
 /* Debug helper, NOT for the hot path: synchronises `stream`, copies the workspace's device status
    word to *status (MOE_OK, MOE_ERR_OFFSETS or MOE_ERR_TIMEOUT, accumulated over the calls since the

@@ -18,9 +18,12 @@ MOE_FMT_F32, MOE_FMT_BF16, MOE_FMT_MXFP4 = 0, 1, 2
 MOE_OK = 0
 MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_FORMAT, MOE_ERR_WORKSPACE = -1, -2, -3, -4
 MOE_ERR_OFFSETS, MOE_ERR_HIP, MOE_ERR_ALIGN, MOE_ERR_TIMEOUT = -5, -6, -7, -8
+MOE_ERR_SCRATCH = -9
+MOE_NOALLOC_SCRATCH_BYTES = 2138112
 MOE_MAX_TOKENS, MOE_MAX_EXPERTS, MOE_MAX_TOPK = 16, 512, 16
 
-EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_decode_forward", "moe_read_status", "moe_status_string")
+EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_decode_forward", "moe_decode_forward_noalloc",
+            "moe_read_status", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -66,6 +69,9 @@ def lib():
         L.moe_decode_forward.restype = ctypes.c_int
         L.moe_decode_forward.argtypes = [ctypes.POINTER(moe_desc_t), i32, vp, vp, ctypes.POINTER(moe_weights_t),
                                          vp, i32, vp, vp, vp, ctypes.POINTER(moe_dispatch_t), vp, sz, vp]
+        L.moe_decode_forward_noalloc.restype = ctypes.c_int
+        L.moe_decode_forward_noalloc.argtypes = [ctypes.POINTER(moe_desc_t), i32, vp, vp, ctypes.POINTER(moe_weights_t),
+                                                 vp, i32, vp, vp, vp, ctypes.POINTER(moe_dispatch_t), vp]
         L.moe_read_status.restype = ctypes.c_int
         L.moe_read_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -119,6 +125,14 @@ def moe_decode_forward(desc, M, x, w_router, weights: moe_weights_t, y, ws, req_
                                   ctypes.byref(disp) if disp is not None else None, _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_decode_forward")
+
+
+def moe_decode_forward_noalloc(desc, M, x, w_router, weights: moe_weights_t, y, req_offsets=None, R: int = 0,
+                               topk_ids=None, topk_w=None, disp: Optional[moe_dispatch_t] = None, stream=None):
+    st = lib().moe_decode_forward_noalloc(ctypes.byref(desc), M, _ptr(x), _ptr(w_router), ctypes.byref(weights),
+                                          _ptr(req_offsets), R, _ptr(y), _ptr(topk_ids), _ptr(topk_w),
+                                          ctypes.byref(disp) if disp is not None else None, _stream(stream))
+    _check(st, "moe_decode_forward_noalloc")
 
 
 def moe_read_status(ws, stream=None) -> int:

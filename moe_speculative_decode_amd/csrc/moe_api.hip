@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -12,6 +13,7 @@ namespace {
 
 using moe::Params;
 using moe::Workspace;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr size_t kAlign = 256;
 
@@ -65,14 +67,13 @@ int check_desc(const moe_desc_t* d) {
     return MOE_OK;
 }
 
-int fill_common(Params& p, const moe_desc_t* d, int32_t M, const void* x, const void* wr, void* ws, size_t ws_bytes) {
-    int st = check_desc(d);
-    if (st) return st;
+// Checks the description, M, x and the router, and fills the call's parameters with the workspace
+// regions of layout L at base.
+int fill_params(Params& p, const moe_desc_t* d, int32_t M, const void* x, const void* wr, char* base,
+                const Layout& L) {
     if (M < 1 || M > d->max_tokens) return MOE_ERR_SHAPE;
-    if (!x || !wr || !ws) return MOE_ERR_NULL;
-    if (!is_aligned(x) || !is_aligned(wr) || !is_aligned(ws)) return MOE_ERR_ALIGN;
-    const Layout L = layout(*d);
-    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (!x || !wr || !base) return MOE_ERR_NULL;
+    if (!is_aligned(x) || !is_aligned(wr) || !is_aligned(base)) return MOE_ERR_ALIGN;
     memset(&p, 0, sizeof(p));
     p.H = d->hidden;
     p.E = d->num_experts;
@@ -85,15 +86,24 @@ int fill_common(Params& p, const moe_desc_t* d, int32_t M, const void* x, const 
     p.act_stride = d->inter > d->shared_inter ? d->inter : d->shared_inter;
     p.x = x;
     p.wr = wr;
-    char* b = (char*)ws;
     Workspace& W = p.ws;
-    W.hdr = (uint32_t*)(b + L.hdr);
-    W.ctr = (uint32_t*)(b + L.ctr);
-    W.logits = (uint64_t*)(b + L.logits);
-    W.route = (uint64_t*)(b + L.route);
-    W.act = (float*)(b + L.act);
-    W.part = (float*)(b + L.part);
+    W.hdr = (uint32_t*)(base + L.hdr);
+    W.ctr = (uint32_t*)(base + L.ctr);
+    W.logits = (uint64_t*)(base + L.logits);
+    W.route = (uint64_t*)(base + L.route);
+    W.act = (float*)(base + L.act);
+    W.part = (float*)(base + L.part);
     return MOE_OK;
+}
+
+int fill_common(Params& p, const moe_desc_t* d, int32_t M, const void* x, const void* wr, void* ws, size_t ws_bytes) {
+    int st = check_desc(d);
+    if (st) return st;
+    if (M < 1 || M > d->max_tokens) return MOE_ERR_SHAPE;
+    if (!ws) return MOE_ERR_NULL;
+    const Layout L = layout(*d);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    return fill_params(p, d, M, x, wr, (char*)ws, L);
 }
 
 int check_weights(const moe_desc_t* d, const moe_weights_t* w) {
@@ -154,6 +164,91 @@ int plan_and_launch(Params& p, hipStream_t stream) {
     return moe::launch_layer(p, G, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// The forward call's weights, outputs and request offsets (checked on the host).
+int fill_forward(Params& p, const moe_desc_t* d, const moe_weights_t* w, const int32_t* req_offsets, int32_t R,
+                 void* y, int32_t* topk_ids_out, float* topk_w_out, const moe_dispatch_t* disp) {
+    int st = check_weights(d, w);
+    if (st) return st;
+    if (!y) return MOE_ERR_NULL;
+    if (!is_aligned(y)) return MOE_ERR_ALIGN;
+    if (req_offsets && (R < 1 || R > MOE_MAX_TOKENS)) return MOE_ERR_OFFSETS;
+    p.w = *w;
+    p.req_off = req_offsets;
+    p.R = req_offsets ? R : 0;
+    p.y = y;
+    p.topk_ids = topk_ids_out;
+    p.topk_w = topk_w_out;
+    if (disp) p.disp = *disp;
+    if (!req_offsets) p.disp.req_unique = nullptr;
+    return MOE_OK;
+}
+
+// ---- the fixed scratch of moe_decode_forward_noalloc ---------------------------------------
+// Its regions sit at fixed offsets sized for the largest description it serves (max_tokens * (k + 1)
+// <= kScratchRows pair rows, E <= 512, H <= 2560, I, Is <= 768), so a region only ever holds its
+// own kind of data whatever the description: the tagged logit and routing words never share bytes
+// with SwiGLU rows or partial outputs of an earlier call.
+constexpr int64_t kScratchRows = 144;  // 16 tokens x (8 routed + 1 shared)
+
+constexpr Layout scratch_layout() {
+    Layout L{};
+    size_t o = 0;
+    L.hdr = o;
+    o += moe::kHdrBytes;
+    L.ctr = o;
+    o = (o + 2 * sizeof(uint32_t) * (size_t)moe::kSetWords + kAlign - 1) / kAlign * kAlign;
+    L.logits = o;
+    o = (o + 8 * (size_t)MOE_MAX_TOKENS * MOE_MAX_EXPERTS + kAlign - 1) / kAlign * kAlign;
+    L.route = o;
+    o = (o + 16 * (size_t)kScratchRows + kAlign - 1) / kAlign * kAlign;
+    L.act = o;
+    o = (o + 4 * (size_t)kScratchRows * MOE_MAX_INTER + kAlign - 1) / kAlign * kAlign;
+    L.part = o;
+    o = (o + 4 * (size_t)kScratchRows * MOE_MAX_HIDDEN + kAlign - 1) / kAlign * kAlign;
+    L.total = o;
+    return L;
+}
+constexpr size_t kScratchBytes = scratch_layout().total;  // 2,138,112 bytes
+static_assert(kScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "header and layout disagree");
+
+// One copy per GPU, held until the process ends.  In host code `scratch` names a host-side
+// stand-in: its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Zero-fill of n 16-byte words (plain vector stores).
+__global__ void k_clear(u32x4_t* p, uint32_t n) {
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = u32x4_t{0, 0, 0, 0};
+}
+
+// This device's scratch address.  The first call on a device looks it up (with that device
+// current) and enqueues, on the caller's stream, a clear of the header, the counter sets and the
+// tagged logit and routing words: everything that must start at zero.  The SwiGLU rows and
+// partial outputs need no clearing (counters gate every read of them).  Replaying the clear (if
+// the first call was captured into a graph) only restores that initial state.
+int scratch_on_device(hipStream_t stream, char** out) {
+    static std::mutex mu;
+    static std::atomic<char*> addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+    char* a = addr[dev].load(std::memory_order_acquire);
+    if (!a) {
+        std::lock_guard<std::mutex> g(mu);
+        a = addr[dev].load(std::memory_order_acquire);
+        if (!a) {
+            void* ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+            constexpr Layout L = scratch_layout();
+            const uint32_t n16 = (uint32_t)((L.act - L.hdr) / 16);
+            hipLaunchKernelGGL(k_clear, dim3(64), dim3(256), 0, stream, (u32x4_t*)ptr, n16);
+            if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+            a = (char*)ptr;
+            addr[dev].store(a, std::memory_order_release);
+        }
+    }
+    *out = a;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,18 +278,21 @@ int moe_decode_forward(const moe_desc_t* d, int32_t M, const void* x, const void
     Params p;
     int st = fill_common(p, d, M, x, w_router, ws, ws_bytes);
     if (st) return st;
-    if ((st = check_weights(d, w))) return st;
-    if (!y) return MOE_ERR_NULL;
-    if (!is_aligned(y)) return MOE_ERR_ALIGN;
-    if (req_offsets && (R < 1 || R > MOE_MAX_TOKENS)) return MOE_ERR_OFFSETS;
-    p.w = *w;
-    p.req_off = req_offsets;
-    p.R = req_offsets ? R : 0;
-    p.y = y;
-    p.topk_ids = topk_ids_out;
-    p.topk_w = topk_w_out;
-    if (disp) p.disp = *disp;
-    if (!req_offsets) p.disp.req_unique = nullptr;
+    if ((st = fill_forward(p, d, w, req_offsets, R, y, topk_ids_out, topk_w_out, disp))) return st;
+    return plan_and_launch(p, (hipStream_t)stream);
+}
+
+int moe_decode_forward_noalloc(const moe_desc_t* d, int32_t M, const void* x, const void* w_router,
+                               const moe_weights_t* w, const int32_t* req_offsets, int32_t R, void* y,
+                               int32_t* topk_ids_out, float* topk_w_out, const moe_dispatch_t* disp, void* stream) {
+    int st = check_desc(d);
+    if (st) return st;
+    if ((int64_t)d->max_tokens * (d->top_k + 1) > kScratchRows) return MOE_ERR_SCRATCH;
+    char* base = nullptr;
+    if ((st = scratch_on_device((hipStream_t)stream, &base))) return st;
+    Params p;
+    if ((st = fill_params(p, d, M, x, w_router, base, scratch_layout()))) return st;
+    if ((st = fill_forward(p, d, w, req_offsets, R, y, topk_ids_out, topk_w_out, disp))) return st;
     return plan_and_launch(p, (hipStream_t)stream);
 }
 
@@ -219,6 +317,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_OFFSETS: return "request offsets out of range or not monotone from 0 to M";
     case MOE_ERR_HIP: return "a HIP runtime call failed";
     case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MOE_ERR_SCRATCH: return "the description needs more than the fixed scratch of moe_decode_forward_noalloc (max_tokens * (top_k + 1) > 144 pair rows); use moe_decode_forward with a workspace";
     case MOE_ERR_TIMEOUT: return "a cross-workgroup wait timed out; that call's y was written as NaN";
     default: return "unknown status";
     }

@@ -110,8 +110,25 @@ def test_forward_rejects():
     assert call_fwd(d, ws_bytes=100) == mdl.MOE_ERR_WORKSPACE
 
 
+def test_noalloc_rejects_on_host():
+    """The fixed scratch serves max_tokens * (top_k + 1) <= 144 pair rows; larger descriptions are
+    rejected before any HIP call (so this runs without a GPU), as are invalid descriptions."""
+    W = mdl.moe_weights_t(*([FAKE] * 12))
+    L = mdl.lib()
+
+    def call(desc):
+        return L.moe_decode_forward_noalloc(ctypes.byref(desc), 1, FAKE, FAKE, ctypes.byref(W), None, 0, FAKE, None,
+                                            None, None, None)
+    assert call(ling(top_k=16, max_tokens=16)) == mdl.MOE_ERR_SCRATCH
+    assert call(ling(top_k=8, max_tokens=16 + 1)) == mdl.MOE_ERR_SHAPE
+    assert call(ling(top_k=9, max_tokens=15)) == mdl.MOE_ERR_SCRATCH  # 150 rows
+    assert call(ling(hidden=4096)) == mdl.MOE_ERR_SHAPE
+    assert L.moe_decode_forward_noalloc(None, 1, FAKE, FAKE, ctypes.byref(W), None, 0, FAKE, None, None, None,
+                                        None) == mdl.MOE_ERR_NULL
+
+
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert mdl.moe_status_string(s) and mdl.moe_status_string(s) != "unknown status"
     assert mdl.moe_status_string(-99) == "unknown status"
     with pytest.raises(mdl.MoeError):
