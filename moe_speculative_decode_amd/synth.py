@@ -39,6 +39,10 @@ FORMAT_NAMES = {F32: "f32", BF16: "bf16", MXFP4: "mxfp4"}
 
 # stream tags
 T_ROUTER, T_GATE, T_UP, T_DOWN, T_SH_GATE, T_SH_UP, T_SH_DOWN, T_HIDDEN_BASE, T_HIDDEN_NOISE = range(9)
+T_NORM, T_BIAS = 9, 10
+
+NORM_GAIN_STD = 0.1   # RMSNorm gain g = 1 + 0.1 N(0,1), in the activation format
+BIAS_STD = 0.5        # selection bias b ~ N(0, 0.5^2), binary32: half the spread of the logits
 
 WEIGHT_STD = 0.02
 MX_BLOCK = 32
@@ -58,6 +62,10 @@ class LayerConfig:
     hidden_recipe: str   # "iid" or "shared_base"
     layer_seed: int = 0
     description: str = ""
+    router_norm: bool = False   # RMSNorm prologue before the router (and the experts)
+    router_bias: bool = False   # bias-corrected top-k selection
+    norm_eps: float = 1e-6
+    hidden_scale: float = 1.0   # hidden states drawn times this (a residual stream before its norm)
 
     @property
     def M(self) -> int:
@@ -71,7 +79,10 @@ class LayerConfig:
         return out
 
 
-def _ling(name, fmt, lens, recipe, desc):
+def _ling(name, fmt, lens, recipe, desc, router=False):
+    if router:  # the router chain's RMSNorm prologue and bias-corrected selection, on un-normed states
+        return LayerConfig(name, 2560, 512, 8, 768, 768, BF16, fmt, tuple(lens), recipe, 0, desc,
+                           router_norm=True, router_bias=True, norm_eps=1e-6, hidden_scale=4.0)
     return LayerConfig(name, 2560, 512, 8, 768, 768, BF16, fmt, tuple(lens), recipe, 0, desc)
 
 
@@ -90,6 +101,16 @@ CONFIGS: Dict[str, LayerConfig] = {
                            "Ling shapes, MXFP4 expert weights, bf16 router/activations, M=1"),
     "ling_mxfp4_m16_ragged": _ling("ling_mxfp4_m16_ragged", MXFP4, (2, 6, 3, 5), "shared_base",
                                    "Ling shapes, MXFP4 expert weights, M=16 ragged verify, requests {2,6,3,5}"),
+    # the router chain with its RMSNorm prologue and bias-corrected top-k (hidden states x4)
+    "ling_bf16_m1_router": _ling("ling_bf16_m1_router", BF16, (1,), "iid",
+                                 "Ling shapes, bf16, M=1, RMSNorm prologue + bias-corrected top-k", True),
+    "ling_bf16_m6_router": _ling("ling_bf16_m6_router", BF16, (6,), "shared_base",
+                                 "Ling shapes, bf16, M=6, RMSNorm prologue + bias-corrected top-k", True),
+    "ling_bf16_m16_ragged_router": _ling("ling_bf16_m16_ragged_router", BF16, (2, 6, 3, 5), "shared_base",
+                                         "Ling shapes, bf16, M=16 ragged, RMSNorm prologue + bias-corrected top-k",
+                                         True),
+    "ling_mxfp4_m6_router": _ling("ling_mxfp4_m6_router", MXFP4, (6,), "shared_base",
+                                  "Ling shapes, MXFP4, M=6, RMSNorm prologue + bias-corrected top-k", True),
 }
 
 
@@ -189,6 +210,12 @@ class Layer:
         H, E, I, Is = cfg.hidden, cfg.num_experts, cfg.inter, cfg.shared_inter
         s, wf = cfg.layer_seed, cfg.weight_fmt
         self.router = encode_act(normal(s, T_ROUTER, 0, E * H).reshape(E, H) * WEIGHT_STD, cfg.act_fmt)
+        self.norm_w = None    # [H] activation format
+        self.router_bias = None  # [E] float32
+        if cfg.router_norm:
+            self.norm_w = encode_act(1.0 + NORM_GAIN_STD * normal(s, T_NORM, 0, H), cfg.act_fmt)
+        if cfg.router_bias:
+            self.router_bias = f32_bits(BIAS_STD * normal(s, T_BIAS, 0, E))
         self.shared = None
         if Is > 0:
             self.shared = {
@@ -241,7 +268,7 @@ def make_hidden(cfg: LayerConfig, hidden_seed: int) -> np.ndarray:
             noise = normal(hidden_seed, T_HIDDEN_NOISE, t, H)
             rows.append(noise if base is None else base + 0.5 * noise)
             t += 1
-    return encode_act(np.stack(rows), cfg.act_fmt)
+    return encode_act(np.stack(rows) * cfg.hidden_scale, cfg.act_fmt)
 
 
 _SEEDS_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),

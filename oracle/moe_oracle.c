@@ -7,11 +7,19 @@
  *
  * What it computes, per token, in the order the definition states it (every input is first
  * widened exactly to double; no blocking, fusion or reordering beyond that):
+ *   0. optional RMSNorm prologue (the first link of the router chain norm -> gate matvec -> top-k,
+ *      "Chasing the Batch-1 Floor", section "PDL: stacking the latency floors of small kernels"):
+ *      r = 1 / sqrt(mean_h x[h]^2 + eps), xn[h] = bf16(g[h] * (x[h] * r)), the normed activation
+ *      rounded once to the activation format (bfloat16) as a norm kernel of a bf16 model writes it;
+ *      xn then replaces x for the router and for every expert
  *   1. router logits  l_e = sum_h x[h] * Wr[e,h], summed in ascending h
  *      ("Chasing the Batch-1 Floor", sections "PDL: stacking the latency floors of small kernels"
  *       and "bf16 router gate and lm_head": router chain norm -> gate matvec -> top-k, bf16 gate)
  *   2. p = softmax(l) over all E experts, keep the k largest (ties: lower expert id first),
- *      renormalise the kept probabilities to sum to 1
+ *      renormalise the kept probabilities to sum to 1.  With the bias-corrected selection (the
+ *      page's "the router top-k prefetches its bias"), the kept experts are instead the k largest
+ *      keys l_e + b_e (ties: lower id), while their weights are still p renormalised over them;
+ *      the kept experts are reported in descending weight order (ties: lower id)
  *      ("3 ways to boost MoE inference on NVIDIA DGX Spark", "Model and baseline configuration":
  *       each token goes to eight of 512 routed experts plus one shared expert)
  *   3. for each kept expert: g = Wg x, v = Wu x, a = silu(g) * v with silu(z) = z / (1 + exp(-z)),
@@ -66,6 +74,33 @@ double oracle_e2m1_to_f64(uint8_t code) {
 /* E8M0 (OCP MX v1.0): an unsigned biased exponent, value 2^(S-127); S = 255 is NaN. */
 double oracle_e8m0_to_f64(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
 
+/* The bfloat16 value nearest to v (ties: the even significand), as a double: bfloat16 keeps 8
+   significant bits, its normal exponents run from -126 to 127 and below 2^-126 its spacing stays
+   2^-133 (subnormals).  Values beyond the largest finite bfloat16 round to infinity. */
+double oracle_round_bf16(double v) {
+    if (v == 0.0 || isnan(v) || isinf(v)) return v;
+    int e;
+    frexp(fabs(v), &e); /* |v| = f * 2^e, f in [0.5, 1): the leading bit has weight 2^(e-1) */
+    int lead = e - 1;
+    if (lead < -126) lead = -126;
+    const double ulp = ldexp(1.0, lead - 7);
+    double q = v / ulp; /* exact: a power-of-two scale */
+    double fl = floor(q), r = q - fl;
+    double n = (r > 0.5 || (r == 0.5 && fmod(fl, 2.0) != 0.0)) ? fl + 1.0 : fl;
+    double out = n * ulp;
+    if (fabs(out) >= ldexp(2.0 - ldexp(1.0, -8), 127)) return v > 0 ? INFINITY : -INFINITY;
+    return out;
+}
+
+/* RMSNorm of one activation row: xn[h] = bf16(g[h] * (x[h] * r)), r = 1 / sqrt(mean(x^2) + eps),
+   the mean summed in ascending h. */
+static void rms_norm(const double* x, const double* g, int H, double eps, double* xn) {
+    double ss = 0.0;
+    for (int h = 0; h < H; ++h) ss += x[h] * x[h];
+    const double r = 1.0 / sqrt(ss / H + eps);
+    for (int h = 0; h < H; ++h) xn[h] = oracle_round_bf16(g[h] * (x[h] * r));
+}
+
 /* A row-major [rows][cols] matrix in one of the storage formats. */
 typedef struct {
     int fmt;
@@ -117,7 +152,17 @@ typedef struct {
     int32_t hidden, num_experts, top_k, inter, shared_inter; /* H, E, k, I, Is (Is = 0: none) */
     int32_t act_fmt;    /* x and Wr: OF_F32 or OF_BF16 */
     int32_t weight_fmt; /* routed + shared expert weights: OF_F32, OF_BF16 or OF_MXFP4 */
+    int32_t router_flags; /* ORACLE_NORM: RMSNorm prologue; ORACLE_BIAS: bias-corrected selection */
+    double norm_eps;      /* the RMSNorm epsilon */
 } oracle_desc;
+
+enum { ORACLE_NORM = 1, ORACLE_BIAS = 2 };
+
+/* The router's optional tensors (either may be NULL when its flag is off). */
+typedef struct {
+    const void* norm_w; /* [H] in the activation format: the RMSNorm gain g */
+    const float* bias;  /* [E] binary32: the selection bias b */
+} oracle_router_aux;
 
 typedef struct {
     const void *gate, *up, *down;          /* [E][I][H], [E][I][H], [E][H][I] */
@@ -142,14 +187,17 @@ static int cmp_desc(const void* a, const void* b) {
     return (x->id > y->id) - (x->id < y->id);
 }
 
-/* Routes one token.  logits[E] out (may be NULL); ids[k], w[k] out in descending-weight order;
-   *gap out = l_(k) - l_(k+1) of the logits sorted descending (+inf when k == E). */
-static void route_token(const oracle_desc* d, const double* x, const omat* Wr, double* logits_out,
-                        int32_t* ids, double* w, double* gap) {
+/* Routes one token.  logits[E] out (may be NULL); ids[k], w[k] out in descending-weight order
+   (ties: lower id); *gap out = the k-th largest selection key minus the (k+1)-th (+inf when k == E).
+   The selection key of expert e is l_e, or l_e + bias[e] with the bias-corrected selection. */
+static void route_token(const oracle_desc* d, const double* x, const omat* Wr, const float* bias,
+                        double* logits_out, int32_t* ids, double* w, double* gap) {
     const int E = d->num_experts, k = d->top_k;
+    const int biased = (d->router_flags & ORACLE_BIAS) != 0;
     double* l = (double*)malloc(sizeof(double) * E);
-    keyed* p = (keyed*)malloc(sizeof(keyed) * E);
-    keyed* ls = (keyed*)malloc(sizeof(keyed) * E);
+    double* p = (double*)malloc(sizeof(double) * E);
+    keyed* key = (keyed*)malloc(sizeof(keyed) * E);
+    keyed* kept = (keyed*)malloc(sizeof(keyed) * k);
     matvec(Wr, x, l); /* step 1 */
     /* step 2: softmax over all E, stabilised by the max logit */
     double lmax = l[0];
@@ -157,24 +205,28 @@ static void route_token(const oracle_desc* d, const double* x, const omat* Wr, d
     double z = 0.0;
     for (int e = 0; e < E; ++e) z += exp(l[e] - lmax);
     for (int e = 0; e < E; ++e) {
-        p[e].v = exp(l[e] - lmax) / z;
-        p[e].id = e;
-        ls[e].v = l[e];
-        ls[e].id = e;
+        p[e] = exp(l[e] - lmax) / z;
+        key[e].v = biased ? l[e] + (double)bias[e] : l[e]; /* the selection key */
+        key[e].id = e;
     }
-    qsort(p, E, sizeof(keyed), cmp_desc); /* top-k of the probabilities */
-    double kept = 0.0;
-    for (int j = 0; j < k; ++j) kept += p[j].v;
+    qsort(key, E, sizeof(keyed), cmp_desc); /* the k largest keys, ties: lower id */
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += p[key[j].id];
     for (int j = 0; j < k; ++j) {
-        ids[j] = p[j].id;
-        w[j] = p[j].v / kept; /* renormalise over the kept experts */
+        kept[j].id = key[j].id;
+        kept[j].v = p[key[j].id] / sum; /* renormalise over the kept experts */
     }
-    qsort(ls, E, sizeof(keyed), cmp_desc);
-    *gap = (k < E) ? ls[k - 1].v - ls[k].v : INFINITY;
+    qsort(kept, k, sizeof(keyed), cmp_desc); /* reported by descending weight, ties: lower id */
+    for (int j = 0; j < k; ++j) {
+        ids[j] = kept[j].id;
+        w[j] = kept[j].v;
+    }
+    *gap = (k < E) ? key[k - 1].v - key[k].v : INFINITY;
     if (logits_out) memcpy(logits_out, l, sizeof(double) * E);
     free(l);
     free(p);
-    free(ls);
+    free(key);
+    free(kept);
 }
 
 /* ---- step 3 + 4: one SwiGLU expert on one token ----------------------------------------- */
@@ -201,17 +253,32 @@ static void load_row(int fmt, const void* base, int64_t m, int64_t n, double* ou
 
 /* ---- public entry points ---------------------------------------------------------------- */
 
-/* Routing only (steps 1-2) for M tokens.  x [M][H] and Wr [E][H] in d->act_fmt.
-   logits [M][E] (nullable), ids [M][k], w [M][k], gap [M]. */
-void oracle_route(const oracle_desc* d, int32_t M, const void* x, const void* wr, double* logits,
-                  int32_t* ids, double* w, double* gap) {
+/* The routing input of token m: its activation row, RMSNorm'd when the prologue is on. */
+static void token_input(const oracle_desc* d, const oracle_router_aux* aux, const void* x, int64_t m, double* out) {
+    const int H = d->hidden;
+    load_row(d->act_fmt, x, m, H, out);
+    if (d->router_flags & ORACLE_NORM) {
+        double* g = (double*)malloc(sizeof(double) * H);
+        double* raw = (double*)malloc(sizeof(double) * H);
+        load_row(d->act_fmt, aux->norm_w, 0, H, g);
+        memcpy(raw, out, sizeof(double) * H);
+        rms_norm(raw, g, H, d->norm_eps, out);
+        free(g);
+        free(raw);
+    }
+}
+
+/* Routing only (steps 0-2) for M tokens.  x [M][H] and Wr [E][H] in d->act_fmt; aux nullable
+   when no router flag is set.  logits [M][E] (nullable), ids [M][k], w [M][k], gap [M]. */
+void oracle_route(const oracle_desc* d, int32_t M, const void* x, const void* wr, const oracle_router_aux* aux,
+                  double* logits, int32_t* ids, double* w, double* gap) {
     const int H = d->hidden, E = d->num_experts, k = d->top_k;
     omat Wr = {d->act_fmt, wr, NULL, E, H};
     double* xm = (double*)malloc(sizeof(double) * H);
     for (int m = 0; m < M; ++m) {
-        load_row(d->act_fmt, x, m, H, xm);
-        route_token(d, xm, &Wr, logits ? logits + (int64_t)m * E : NULL, ids + (int64_t)m * k,
-                    w + (int64_t)m * k, gap + m);
+        token_input(d, aux, x, m, xm);
+        route_token(d, xm, &Wr, aux ? aux->bias : NULL, logits ? logits + (int64_t)m * E : NULL,
+                    ids + (int64_t)m * k, w + (int64_t)m * k, gap + m);
     }
     free(xm);
 }
@@ -222,8 +289,8 @@ void oracle_route(const oracle_desc* d, int32_t M, const void* x, const void* wr
    own (j = k: the shared expert), then per token the same sum in the same order,
    y = ((w_0 o_0 + w_1 o_1) + ... + w_{k-1} o_{k-1}) + o_shared. */
 void oracle_moe_forward(const oracle_desc* d, const oracle_weights* W, int32_t M, const void* x,
-                        const void* wr, double* y, int32_t* ids_out, double* w_out, double* gap_out,
-                        int32_t nthreads) {
+                        const void* wr, const oracle_router_aux* aux, double* y, int32_t* ids_out,
+                        double* w_out, double* gap_out, int32_t nthreads) {
     const int H = d->hidden, E = d->num_experts, k = d->top_k, I = d->inter, Is = d->shared_inter;
     const int wf = d->weight_fmt;
     const int units = k + 1; /* per token: k routed experts and the shared one */
@@ -236,13 +303,14 @@ void oracle_moe_forward(const oracle_desc* d, const oracle_weights* W, int32_t M
 #ifdef _OPENMP
     if (nthreads <= 0) nthreads = omp_get_max_threads();
 #endif
-    /* steps 1-2 per token */
+    /* steps 0-2 per token */
 #ifdef _OPENMP
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
 #endif
     for (int m = 0; m < M; ++m) {
-        load_row(d->act_fmt, x, m, H, xs + (int64_t)m * H);
-        route_token(d, xs + (int64_t)m * H, &Wr, NULL, ids + (int64_t)m * k, ws + (int64_t)m * k, gaps + m);
+        token_input(d, aux, x, m, xs + (int64_t)m * H);
+        route_token(d, xs + (int64_t)m * H, &Wr, aux ? aux->bias : NULL, NULL, ids + (int64_t)m * k,
+                    ws + (int64_t)m * k, gaps + m);
     }
     /* steps 3-4: every expert output of every token */
 #ifdef _OPENMP

@@ -34,10 +34,18 @@ def build(force: bool = True, src: str = SRC, out: str = LIB) -> str:
     return out
 
 
+NORM, BIAS = 1, 2  # router flags: RMSNorm prologue, bias-corrected selection
+
+
 class _Desc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
-                ("act_fmt", ctypes.c_int32), ("weight_fmt", ctypes.c_int32)]
+                ("act_fmt", ctypes.c_int32), ("weight_fmt", ctypes.c_int32),
+                ("router_flags", ctypes.c_int32), ("norm_eps", ctypes.c_double)]
+
+
+class _Aux(ctypes.Structure):
+    _fields_ = [("norm_w", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
 
 
 class _Weights(ctypes.Structure):
@@ -55,12 +63,15 @@ def load(path: str):
     L.oracle_e2m1_to_f64.argtypes = [ctypes.c_uint8]
     L.oracle_e8m0_to_f64.restype = ctypes.c_double
     L.oracle_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+    L.oracle_round_bf16.restype = ctypes.c_double
+    L.oracle_round_bf16.argtypes = [ctypes.c_double]
     L.oracle_route.restype = None
     L.oracle_route.argtypes = [ctypes.POINTER(_Desc), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
-                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+                               ctypes.POINTER(_Aux), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p]
     L.oracle_moe_forward.restype = None
     L.oracle_moe_forward.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Weights), ctypes.c_int32,
-                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Aux), ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
     L.oracle_compact.restype = ctypes.c_int32
     L.oracle_compact.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -112,8 +123,18 @@ def _ptr(a: Optional[np.ndarray]):
     return a.ctypes.data
 
 
-def desc(H, E, k, I, Is, act_fmt, weight_fmt) -> _Desc:
-    return _Desc(H, E, k, I, Is, act_fmt, weight_fmt)
+def desc(H, E, k, I, Is, act_fmt, weight_fmt, router_flags=0, norm_eps=1e-6) -> _Desc:
+    return _Desc(H, E, k, I, Is, act_fmt, weight_fmt, router_flags, norm_eps)
+
+
+def round_bf16(v: float) -> float:
+    return lib().oracle_round_bf16(v)
+
+
+def _aux(norm_w, bias):
+    if norm_w is None and bias is None:
+        return None
+    return ctypes.byref(_Aux(_ptr(norm_w), _ptr(bias)))
 
 
 def bf16_to_f64(b: int) -> float:
@@ -128,18 +149,21 @@ def e8m0_to_f64(s: int) -> float:
     return lib().oracle_e8m0_to_f64(s)
 
 
-def route(d: _Desc, x: np.ndarray, wr: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
-    """-> (logits [M,E] f64, ids [M,k] i32, w [M,k] f64, gap [M] f64)."""
+def route(d: _Desc, x: np.ndarray, wr: np.ndarray, norm_w=None, bias=None
+          ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """-> (logits [M,E] f64, ids [M,k] i32, w [M,k] f64, gap [M] f64).  norm_w ([H], activation
+    format) and bias ([E] float32) are the router's prologue tensors, used when d's flags say so."""
     M = x.shape[0]
     logits = np.zeros((M, d.num_experts))
     ids = np.zeros((M, d.top_k), np.int32)
     w = np.zeros((M, d.top_k))
     gap = np.zeros(M)
-    lib().oracle_route(ctypes.byref(d), M, _ptr(x), _ptr(wr), _ptr(logits), _ptr(ids), _ptr(w), _ptr(gap))
+    lib().oracle_route(ctypes.byref(d), M, _ptr(x), _ptr(wr), _aux(norm_w, bias), _ptr(logits), _ptr(ids), _ptr(w),
+                       _ptr(gap))
     return logits, ids, w, gap
 
 
-def forward(d: _Desc, weights: dict, x: np.ndarray, wr: np.ndarray, threads: int = 0):
+def forward(d: _Desc, weights: dict, x: np.ndarray, wr: np.ndarray, threads: int = 0, norm_w=None, bias=None):
     """Whole layer.  weights: dict with keys gate, up, down (+ _s scales for MXFP4) and sh_*.
     -> (y [M,H] f64, ids [M,k], w [M,k], gap [M])."""
     M = x.shape[0]
@@ -150,8 +174,8 @@ def forward(d: _Desc, weights: dict, x: np.ndarray, wr: np.ndarray, threads: int
     ids = np.zeros((M, d.top_k), np.int32)
     w = np.zeros((M, d.top_k))
     gap = np.zeros(M)
-    lib().oracle_moe_forward(ctypes.byref(d), ctypes.byref(W), M, _ptr(x), _ptr(wr), _ptr(y), _ptr(ids),
-                             _ptr(w), _ptr(gap), threads)
+    lib().oracle_moe_forward(ctypes.byref(d), ctypes.byref(W), M, _ptr(x), _ptr(wr), _aux(norm_w, bias), _ptr(y),
+                             _ptr(ids), _ptr(w), _ptr(gap), threads)
     return y, ids, w, gap
 
 
@@ -200,5 +224,11 @@ def layer_weights(layer) -> dict:
 
 
 def layer_desc(cfg) -> _Desc:
+    flags = (NORM if getattr(cfg, "router_norm", False) else 0) | (BIAS if getattr(cfg, "router_bias", False) else 0)
     return desc(cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter, cfg.shared_inter, cfg.act_fmt,
-                cfg.weight_fmt)
+                cfg.weight_fmt, flags, getattr(cfg, "norm_eps", 1e-6))
+
+
+def router_aux(layer) -> dict:
+    """The router prologue tensors of a synth.Layer as keyword arguments of route / forward."""
+    return {"norm_w": getattr(layer, "norm_w", None), "bias": getattr(layer, "router_bias", None)}

@@ -27,17 +27,54 @@ def dec(fmt, data, scales=None):
     return vals * np.repeat(sc, 32, axis=-1)
 
 
-def route(logits, k):
-    """ids [M,k] by (logit desc, id asc); weights = softmax restricted to the selected logits."""
+def _bf16_table():
+    """Every finite bfloat16 value (one per value: -0 dropped) in ascending order, with its bits."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        vals = (bits << 16).view(np.float32).astype(np.float64)
+    keep = np.isfinite(vals) & ~((vals == 0) & np.signbit(vals))
+    order = np.argsort(vals[keep], kind="stable")
+    return vals[keep][order], bits[keep][order].astype(np.uint16)
+
+
+_BF16_VALS, _BF16_BITS = _bf16_table()
+
+
+def round_bf16(v):
+    """Nearest bfloat16 value of each float64 (ties: the candidate with an even bit pattern), by
+    comparing the distances to the two bracketing finite bfloat16 values.  Finite inputs inside the
+    finite range only."""
+    v = np.asarray(v, dtype=np.float64)
+    hi = np.clip(np.searchsorted(_BF16_VALS, v, side="left"), 1, len(_BF16_VALS) - 1)
+    lo = hi - 1
+    a, b = _BF16_VALS[lo], _BF16_VALS[hi]
+    da, db = np.abs(v - a), np.abs(b - v)
+    even_lo = (_BF16_BITS[lo] & 1) == 0
+    pick_lo = (da < db) | ((da == db) & even_lo)
+    out = np.where(pick_lo, a, b)
+    return np.where(v == _BF16_VALS[hi], _BF16_VALS[hi], out)
+
+
+def rms_norm(x, g, eps):
+    """RMSNorm rows of x with gain g, rounded once to bfloat16."""
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+    return round_bf16(g[None, :] * (x * r))
+
+
+def route(logits, k, bias=None):
+    """ids [M,k]: the k largest keys (logit, or logit + bias) by (key desc, id asc); weights =
+    softmax of the logits restricted to the selected experts; reported by (weight desc, id asc)."""
     M, E = logits.shape
+    keys = logits if bias is None else logits + np.asarray(bias, dtype=np.float64)[None, :]
     ids = np.zeros((M, k), np.int64)
     w = np.zeros((M, k))
     for m in range(M):
-        order = np.lexsort((np.arange(E), -logits[m]))
-        sel = order[:k]
-        ids[m] = sel
+        sel = np.lexsort((np.arange(E), -keys[m]))[:k]
         z = np.exp(logits[m, sel] - logits[m, sel].max())
-        w[m] = z / z.sum()
+        ww = z / z.sum()
+        o = np.lexsort((sel, -ww))
+        ids[m] = sel[o]
+        w[m] = ww[o]
     return ids, w
 
 
@@ -45,13 +82,16 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def forward(cfg_tuple, x, wr, W):
-    """cfg_tuple = (H, E, k, I, Is, act_fmt, weight_fmt); W = oracle-style storage dict.
+def forward(cfg_tuple, x, wr, W, norm_w=None, bias=None, eps=1e-6):
+    """cfg_tuple = (H, E, k, I, Is, act_fmt, weight_fmt); W = oracle-style storage dict; norm_w
+    (activation format) turns on the RMSNorm prologue, bias the biased selection.
     Returns (y [M,H], ids, w)."""
     H, E, k, I, Is, af, wf = cfg_tuple
     xd = dec(af, x)
+    if norm_w is not None:
+        xd = rms_norm(xd, dec(af, norm_w), eps)
     logits = xd @ dec(af, wr).T
-    ids, w = route(logits, k)
+    ids, w = route(logits, k, bias)
     M = xd.shape[0]
     y = np.zeros((M, H))
     gate = dec(wf, W["gate"], W.get("gate_s"))

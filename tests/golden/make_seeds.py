@@ -1,6 +1,7 @@
 """Writes tests/golden/seeds.json: for every named workload, the first hidden-state seed whose
-tokens all have a router-logit gap of at least 1e-3 between the k-th and (k+1)-th largest logit,
-so that the selected expert set cannot flip under fp32-vs-fp64 accumulation.
+tokens all have a gap of at least 1e-3 between the k-th and (k+1)-th largest selection key (the
+router logit, or logit + bias with the bias-corrected selection), so that the selected expert set
+cannot flip under fp32-vs-fp64 accumulation.
 
 Calls only the oracle (for the logits) and the input generator.  Run from the repo root:
     python tests/golden/make_seeds.py
@@ -19,12 +20,12 @@ MIN_GAP = 1e-3
 
 
 def accept(cfg, max_tries=100):
-    layer_router = synth.Layer(cfg, experts=[]).router
+    layer = synth.Layer(cfg, experts=[])
     d = O.layer_desc(cfg)
     tried = []
     for seed in range(max_tries):
         x = synth.make_hidden(cfg, seed)
-        _, ids, w, gap = O.route(d, x, layer_router)
+        _, ids, w, gap = O.route(d, x, layer.router, **O.router_aux(layer))
         tried.append(float(gap.min()))
         if gap.min() >= MIN_GAP:
             comp = O.compact(ids, w, cfg.num_experts)

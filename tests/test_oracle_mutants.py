@@ -13,7 +13,7 @@ from tests import test_oracle_pins as P
 MUTANTS = {
     "silu_sign": ("a[r] = g[r] / (1.0 + exp(-g[r])) * v[r];", "a[r] = g[r] / (1.0 + exp(g[r])) * v[r];"),
     "no_shared": ("            for (int h = 0; h < H; ++h) ym[h] += osh[h];\n", "\n"),
-    "no_renorm": ("w[j] = p[j].v / kept;", "w[j] = p[j].v;"),
+    "no_renorm": ("kept[j].v = p[key[j].id] / sum;", "kept[j].v = p[key[j].id];"),
     "tie_order": ("return (x->id > y->id) - (x->id < y->id);", "return (x->id < y->id) - (x->id > y->id);"),
     "nibble_swap": ("(c & 1) ? (byte >> 4) : (byte & 15)", "(c & 1) ? (byte & 15) : (byte >> 4)"),
     "scale_index": ("A->scales[r * (A->cols / 32) + c / 32]", "A->scales[r * (A->cols / 32) + c / 64]"),
@@ -25,8 +25,19 @@ MUTANTS = {
     "bf16_shift": ("return dec_f32((uint32_t)b << 16);", "return dec_f32((uint32_t)b << 15);"),
     "e2m1_bias": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e - 2)"),
     "compact_slot": ("row_slot[row] = p % k;", "row_slot[row] = p / k;"),
-    "gap_index": ("ls[k - 1].v - ls[k].v", "ls[k - 2].v - ls[k].v"),
-    "softmax_sign": ("p[e].v = exp(l[e] - lmax) / z;", "p[e].v = exp(lmax - l[e]) / z;"),
+    "gap_index": ("key[k - 1].v - key[k].v", "key[k - 2].v - key[k].v"),
+    "softmax_sign": ("p[e] = exp(l[e] - lmax) / z;", "p[e] = exp(lmax - l[e]) / z;"),
+    # router prologue
+    "bias_ignored": ("key[e].v = biased ? l[e] + (double)bias[e] : l[e];", "key[e].v = l[e];"),
+    "bias_in_weights": ("kept[j].v = p[key[j].id] / sum;", "kept[j].v = key[j].v / sum;"),
+    "bias_sign": ("l[e] + (double)bias[e]", "l[e] - (double)bias[e]"),
+    "order_by_key": ("qsort(kept, k, sizeof(keyed), cmp_desc);", ";"),
+    "norm_no_gain": ("xn[h] = oracle_round_bf16(g[h] * (x[h] * r));", "xn[h] = oracle_round_bf16(x[h] * r);"),
+    "norm_no_round": ("xn[h] = oracle_round_bf16(g[h] * (x[h] * r));", "xn[h] = g[h] * (x[h] * r);"),
+    "norm_no_eps": ("sqrt(ss / H + eps)", "sqrt(ss / H)"),
+    "norm_mean": ("sqrt(ss / H + eps)", "sqrt(ss / (H - 1) + eps)"),
+    "norm_skipped": ("    if (d->router_flags & ORACLE_NORM) {", "    if (0) {"),
+    "round_ties_up": ("(r > 0.5 || (r == 0.5 && fmod(fl, 2.0) != 0.0))", "(r >= 0.5)"),
 }
 
 # pins that run quickly; together they must catch each mutant
@@ -40,6 +51,13 @@ PINS = [
     lambda: P.test_dense_brute_force(synth.MXFP4, 64, 16, 4, 32, 64, (3, 3)),
     lambda: P.test_closed_form_swiglu(synth.BF16, 2.0, 0.5),
     lambda: P.test_compaction_vs_sets(6, 8, 512),
+    P.test_round_bf16_nearest_with_ties_to_even,
+    P.test_rmsnorm_of_constant_vector_is_the_gain,
+    P.test_rmsnorm_eps_closed_form,
+    P.test_rmsnorm_vs_brute_force,
+    P.test_biased_selection_vs_full_sort,
+    P.test_biased_selection_constructed,
+    lambda: P.test_dense_brute_force_with_router_prologue(synth.BF16, (2, 3)),
 ]
 
 

@@ -163,11 +163,156 @@ def test_tie_break_lower_id_first():
 def test_seed_file_gaps():
     seeds = json.load(open(os.path.join(GOLDEN, "seeds.json")))
     for name, cfg in synth.CONFIGS.items():
-        layer_router = synth.Layer(cfg, experts=[]).router
+        layer = synth.Layer(cfg, experts=[])
         x = synth.make_hidden(cfg, seeds[name]["hidden_seed"])
-        _, ids, w, gap = O.route(O.layer_desc(cfg), x, layer_router)
+        _, ids, w, gap = O.route(O.layer_desc(cfg), x, layer.router, **O.router_aux(layer))
         assert gap.min() >= 1e-3, name
         assert O.compact(ids, w, cfg.num_experts)["U"] == seeds[name]["U"]
+
+
+# ---------------------------------------------------------------------------------------------
+# router prologue: RMSNorm before the gate matvec, bias-corrected selection
+# ---------------------------------------------------------------------------------------------
+
+def test_round_bf16_nearest_with_ties_to_even():
+    """Against the nearest of the two bracketing bfloat16 values (a search over every pattern):
+    random values over many binades, every exact midpoint between neighbours of a range of
+    patterns (ties go to the even pattern) and the doubles one ulp either side of them."""
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal(20000) * np.exp(rng.uniform(-40, 40, 20000))
+    bits = np.arange(0x3F00, 0x3F80, dtype=np.uint32)  # [0.5, 1)
+    lo = (bits << 16).view(np.float32).astype(np.float64)
+    hi = ((bits + 1) << 16).view(np.float32).astype(np.float64)
+    mid = (lo + hi) / 2  # exact in binary64
+    for arr in (v, mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf), -mid, mid * 2.0 ** -100):
+        got = np.array([O.round_bf16(float(t)) for t in arr])
+        assert np.array_equal(got, B.round_bf16(arr))
+    # a midpoint between 1 and 1 + 2^-7 goes to 1 (even), the next one to 1 + 2^-6 (even)
+    assert O.round_bf16(1.0 + 2 ** -8) == 1.0
+    assert O.round_bf16(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6
+
+
+def _identity_router_cfg(H=64, flags=O.NORM, eps=1e-6):
+    """E = H experts whose router rows are unit vectors: logit e = (normed) x[e] exactly."""
+    wr = synth.encode_act(np.eye(H), synth.BF16)
+    d = O.desc(H, H, 1, 32, 0, synth.BF16, synth.BF16, flags, eps)
+    return d, wr
+
+
+def test_rmsnorm_of_constant_vector_is_the_gain():
+    H = 64
+    d, wr = _identity_router_cfg(H)
+    g = synth.encode_act(1.0 + 0.1 * synth.normal(1, 9, 0, H), synth.BF16)
+    for c in (3.0, -0.75, 40.0):
+        x = synth.encode_act(np.full((1, H), c), synth.BF16)
+        logits = O.route(d, x, wr, norm_w=g)[0][0]
+        # x / rms(x) = sign(c) (1 - eps / 2c^2 ...): within a tiny fraction of a bf16 step of sign(c) g
+        assert np.array_equal(logits, np.sign(c) * B.dec(synth.BF16, g))
+
+
+def test_rmsnorm_eps_closed_form():
+    """A constant vector c with eps = 3 c^2: x / sqrt(mean(x^2) + eps) = c / (2 |c|) = +-1/2 exactly,
+    so the normed row is exactly +-g / 2."""
+    H = 64
+    g = synth.encode_act(1.0 + 0.1 * synth.normal(1, 9, 3, H), synth.BF16)
+    for c in (1.0, 2.0, -4.0, 0.25):
+        d, wr = _identity_router_cfg(H, eps=3.0 * c * c)
+        x = synth.encode_act(np.full((1, H), c), synth.BF16)
+        logits = O.route(d, x, wr, norm_w=g)[0][0]
+        assert np.array_equal(logits, np.sign(c) * B.dec(synth.BF16, g) / 2)
+
+
+def test_rmsnorm_scale_invariant_without_eps():
+    H = 96
+    d, wr = _identity_router_cfg(H, eps=0.0)
+    g = synth.encode_act(1.0 + 0.1 * synth.normal(1, 9, 1, H), synth.BF16)
+    x = synth.encode_act(synth.normal(2, 8, 0, 3 * H).reshape(3, H), synth.BF16)
+    a = O.route(d, x, wr, norm_w=g)[0]
+    b = O.route(d, np.ascontiguousarray(synth.encode_act(B.dec(synth.BF16, x) * 4.0, synth.BF16)), wr, norm_w=g)[0]
+    assert np.array_equal(a, b)  # power-of-two scaling is exact throughout
+
+
+def test_rmsnorm_vs_brute_force():
+    H = 256
+    d, wr = _identity_router_cfg(H)
+    g = synth.encode_act(1.0 + 0.1 * synth.normal(1, 9, 2, H), synth.BF16)
+    x = synth.encode_act(4.0 * synth.normal(2, 8, 1, 5 * H).reshape(5, H), synth.BF16)
+    got = O.route(d, x, wr, norm_w=g)[0]
+    xd = B.dec(synth.BF16, x)
+    r = 1.0 / np.sqrt(np.mean(xd * xd, axis=1, keepdims=True) + 1e-6)
+    exact = B.dec(synth.BF16, g)[None, :] * (xd * r)
+    ref = B.round_bf16(exact)
+    # the two computations of g x r may differ in the last bits of binary64; compare away from ties
+    step = np.abs(B.round_bf16(exact * (1 + 2 ** -7)) - ref) + 1e-300
+    near_tie = np.abs(np.abs(exact - ref) - step / 2) < 1e-9 * np.abs(exact)
+    assert np.array_equal(got[~near_tie], ref[~near_tie])
+    assert near_tie.mean() < 1e-3
+
+
+def test_zero_bias_routes_like_plain_softmax_topk():
+    cfg = tiny_cfg(synth.BF16, H=96, E=40, k=6, lens=(9,))
+    layer = synth.Layer(cfg, experts=[])
+    x = accepted_x(cfg, layer)
+    plain = O.route(O.layer_desc(cfg), x, layer.router)
+    biased = O.route(O.desc(96, 40, 6, 32, 32, synth.BF16, synth.BF16, O.BIAS), x, layer.router,
+                     bias=np.zeros(40, np.float32))
+    for a, b in zip(plain, biased):
+        assert np.array_equal(a, b)
+
+
+def test_biased_selection_vs_full_sort():
+    cfg = tiny_cfg(synth.BF16, H=96, E=40, k=6, lens=(9,))
+    layer = synth.Layer(cfg, experts=[])
+    bias = synth.f32_bits(0.5 * synth.normal(3, 10, 0, 40))
+    d = O.desc(96, 40, 6, 32, 32, synth.BF16, synth.BF16, O.BIAS)
+    x = synth.make_hidden(cfg, 0)
+    logits, ids, w, gap = O.route(d, x, layer.router, bias=bias)
+    lref = B.dec(synth.BF16, x) @ B.dec(synth.BF16, layer.router).T
+    ids_ref, w_ref = B.route(lref, 6, bias)
+    assert np.array_equal(ids, ids_ref)
+    assert np.allclose(w, w_ref, rtol=0, atol=1e-13)
+    keys = -np.sort(-(lref + bias.astype(np.float64)), axis=1)
+    assert np.allclose(gap, keys[:, 5] - keys[:, 6], atol=1e-12)
+    # the bias really moved experts in and out for some token
+    plain_ids, _ = B.route(lref, 6)
+    assert any(set(ids[m]) != set(plain_ids[m]) for m in range(x.shape[0]))
+
+
+def test_biased_selection_constructed():
+    """Logits 3, 2, 1, 0 with bias (0, 0, 5, 0): the keys 3, 2, 6, 0 select experts 2 and 0; their
+    weights are the softmax of the logits 1 and 3, reported by weight: expert 0 first."""
+    H = 4
+    wr = synth.encode_act(np.eye(H), synth.BF16)
+    x = synth.encode_act(np.array([[3.0, 2.0, 1.0, 0.0]]), synth.BF16)
+    d = O.desc(H, 4, 2, 32, 0, synth.BF16, synth.BF16, O.BIAS)
+    _, ids, w, gap = O.route(d, x, wr, bias=np.array([0, 0, 5, 0], np.float32))
+    assert ids[0].tolist() == [0, 2]
+    e = np.exp(-2.0)
+    assert np.allclose(w[0], [1 / (1 + e), e / (1 + e)], rtol=1e-15)
+    assert gap[0] == 1.0  # keys 6, 3 | 2, 0
+
+
+@pytest.mark.parametrize("fmt,lens", [(synth.BF16, (2, 3)), (synth.MXFP4, (4,))])
+def test_dense_brute_force_with_router_prologue(fmt, lens):
+    cfg = dataclasses.replace(tiny_cfg(fmt, H=64, E=16, k=4, I=32, Is=32, lens=lens, recipe="shared_base"),
+                              router_norm=True, router_bias=True, hidden_scale=4.0)
+    layer = synth.Layer(cfg)
+    d = O.layer_desc(cfg)
+    aux = O.router_aux(layer)
+    for s in range(200):
+        x = synth.make_hidden(cfg, s)
+        if O.route(d, x, layer.router, **aux)[3].min() >= 1e-6:
+            break
+    W = O.layer_weights(layer)
+    y, ids, w, gap = O.forward(d, W, x, layer.router, **aux)
+    y_ref, ids_ref, w_ref = B.forward(cfg_tuple(cfg), x, layer.router, W, norm_w=layer.norm_w,
+                                      bias=layer.router_bias, eps=cfg.norm_eps)
+    assert np.array_equal(ids, ids_ref)
+    assert np.allclose(w, w_ref, rtol=0, atol=1e-13)
+    assert np.max(np.abs(y - y_ref)) <= 1e-12 * np.sqrt(np.mean(y_ref ** 2))
+    # and the prologue matters: the plain layer on the same inputs routes differently or scales y
+    y_plain, *_ = O.forward(O.desc(*cfg_tuple(cfg)), W, x, layer.router)
+    assert not np.allclose(y, y_plain)
 
 
 # ---------------------------------------------------------------------------------------------
