@@ -104,7 +104,7 @@ def cpu_baseline(cfg, layer, x, budget_s: float):
         t0 = time.perf_counter()
         n = 0
         while True:
-            O.forward(d, W, x, layer.router, threads=threads)
+            O.forward(d, W, x, layer.router, threads=threads, **O.router_aux(layer))
             n += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -191,7 +191,7 @@ def measure_format(torch, mdl, dev, synth, names, args, stream_ref):
         seed = synth.accepted_hidden_seed(cfg.name)
         x_host = synth.make_hidden(cfg, seed)
         x = dev.to_device(x_host)
-        desc = dev.desc_of(cfg)
+        desc = dev.desc_of(cfg, layer=base)
         ws = dev.workspace(desc)
         M = cfg.M
         y = torch.empty((M, cfg.hidden), dtype=dev.act_dtype(cfg), device="cuda")

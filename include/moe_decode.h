@@ -101,7 +101,25 @@ typedef struct {
     int32_t max_tokens;    /* largest M the workspace is sized for */
     int32_t act_format;    /* x, router weight and y: MOE_FMT_BF16, or MOE_FMT_F32 with F32 weights */
     int32_t weight_format; /* routed and shared expert weights: F32 (with F32 act), BF16 or MXFP4 */
+    /* The router chain's optional steps either side of the gate matvec ("Chasing the Batch-1
+       Floor", section "PDL: stacking the latency floors of small kernels": norm -> gate matvec ->
+       top-k, the top-k with a bias).  All zero (the default of a zero-filled struct): neither. */
+    int32_t router_flags;  /* MOE_ROUTER_NORM | MOE_ROUTER_BIAS */
+    float norm_eps;        /* MOE_ROUTER_NORM: the epsilon (> 0 recommended, e.g. 1e-6) */
+    const void* norm_weight;  /* MOE_ROUTER_NORM: gain g [H], device memory, activation format */
+    const float* router_bias; /* MOE_ROUTER_BIAS: selection bias b [E], device memory, binary32 */
 } moe_desc_t;
+
+/* router_flags.
+   MOE_ROUTER_NORM: every token row is RMSNorm'd first, xn = bf16(g * (x / sqrt(mean(x^2) + eps)))
+     (mean over the H elements, fp32 arithmetic, rounded once to bfloat16), and xn replaces x for
+     the router and for every expert: y = MoE(RMSNorm(x)).  bfloat16 activations only
+     (MOE_ERR_FORMAT otherwise).
+   MOE_ROUTER_BIAS: the k experts kept per token are those with the largest l_e + b_e (ties: lower
+     id); their weights are still the softmax of the logits l over the kept experts, and topk_ids /
+     topk_w list them by descending weight (ties: lower id). */
+#define MOE_ROUTER_NORM 1
+#define MOE_ROUTER_BIAS 2
 
 /* Expert weights.  Routed stacks are expert-major: gate, up [E][I][H]; down [E][H][I].
    Shared expert: sh_gate, sh_up [Is][H]; sh_down [H][Is].  For MXFP4 the data pointers hold the

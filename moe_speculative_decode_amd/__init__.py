@@ -32,10 +32,15 @@ class MoeError(RuntimeError):
         self.status = status
 
 
+MOE_ROUTER_NORM, MOE_ROUTER_BIAS = 1, 2
+
+
 class moe_desc_t(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
-                ("act_format", ctypes.c_int32), ("weight_format", ctypes.c_int32)]
+                ("act_format", ctypes.c_int32), ("weight_format", ctypes.c_int32),
+                ("router_flags", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("norm_weight", ctypes.c_void_p), ("router_bias", ctypes.c_void_p)]
 
 
 class moe_weights_t(ctypes.Structure):

@@ -64,6 +64,22 @@ int check_desc(const moe_desc_t* d) {
     if (d->inter <= 0 || d->inter > maxI || d->inter % mult) return MOE_ERR_SHAPE;
     if (d->shared_inter < 0 || d->shared_inter > maxI || d->shared_inter % mult) return MOE_ERR_SHAPE;
     if (d->max_tokens <= 0 || d->max_tokens > MOE_MAX_TOKENS) return MOE_ERR_SHAPE;
+    if (d->router_flags & ~(MOE_ROUTER_NORM | MOE_ROUTER_BIAS)) return MOE_ERR_FORMAT;
+    if ((d->router_flags & MOE_ROUTER_NORM) && f32) return MOE_ERR_FORMAT;  // bf16 activations only
+    if ((d->router_flags & MOE_ROUTER_NORM) && !(d->norm_eps >= 0.0f)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+// The router prologue tensors of a call (checked on the host).
+int check_router(const moe_desc_t* d) {
+    if (d->router_flags & MOE_ROUTER_NORM) {
+        if (!d->norm_weight) return MOE_ERR_NULL;
+        if (!is_aligned(d->norm_weight)) return MOE_ERR_ALIGN;
+    }
+    if (d->router_flags & MOE_ROUTER_BIAS) {
+        if (!d->router_bias) return MOE_ERR_NULL;
+        if (!is_aligned(d->router_bias)) return MOE_ERR_ALIGN;
+    }
     return MOE_OK;
 }
 
@@ -74,7 +90,13 @@ int fill_params(Params& p, const moe_desc_t* d, int32_t M, const void* x, const 
     if (M < 1 || M > d->max_tokens) return MOE_ERR_SHAPE;
     if (!x || !wr || !base) return MOE_ERR_NULL;
     if (!is_aligned(x) || !is_aligned(wr) || !is_aligned(base)) return MOE_ERR_ALIGN;
+    int st = check_router(d);
+    if (st) return st;
     memset(&p, 0, sizeof(p));
+    p.router_flags = d->router_flags;
+    p.norm_eps = d->norm_eps;
+    p.norm_w = d->norm_weight;
+    p.rbias = d->router_bias;
     p.H = d->hidden;
     p.E = d->num_experts;
     p.k = d->top_k;

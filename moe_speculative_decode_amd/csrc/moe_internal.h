@@ -88,6 +88,10 @@ struct Params {
     int gu_ksplit;       // MXFP4 gate/up: (tile, stage) items, partials in the staging area at
     int gu_part;         // this float offset
     int sh_gu_mfma;      // MXFP4: the shared expert's gate/up rows on the matrix cores too
+    int router_flags;    // MOE_ROUTER_NORM | MOE_ROUTER_BIAS
+    float norm_eps;
+    const void* norm_w;  // [H] activation format
+    const float* rbias;  // [E] binary32
 };
 
 // Fills the launch plan of p (modes, LDS layout) for a grid of G workgroups.  Returns

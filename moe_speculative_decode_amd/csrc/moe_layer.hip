@@ -620,6 +620,63 @@ __device__ __forceinline__ void stage_rows_bf16(LDS char* dst, const float* src,
 }
 
 // ------------------------------------------------------------------------------------------
+// router prologue: RMSNorm of the token rows ("Chasing the Batch-1 Floor", section "PDL:
+// stacking the latency floors of small kernels": the router chain norm -> gate matvec -> top-k)
+// ------------------------------------------------------------------------------------------
+
+// Token rows xn = bf16(g * (x * r)), r = 1 / sqrt(mean(x^2) + eps), written into the LDS token rows
+// that the router and every expert read.  One wave per token: lane l holds the 16-byte chunks
+// l + 64 j of the row and of the gain in registers; the sum of squares (each exact in fp32) runs
+// in a fixed order per lane and a fixed DPP tree across lanes, so the result does not depend on
+// timing.  bfloat16 activations only.
+template <int NJ>
+__device__ __forceinline__ void rms_norm_rows(const Params& p, LDS char* xs) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int H = p.H, nch = H / 8;
+    if (wave >= p.M) return;
+    u32x4 g[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) g[j] = *(const u32x4*)((const uint8_t*)p.norm_w + 16 * min(lane + 64 * j, nch - 1));
+    for (int m = wave; m < p.M; m += kWaves) {
+        const uint8_t* xrow = (const uint8_t*)p.x + (int64_t)m * H * 2;
+        u32x4 xv[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) xv[j] = *(const u32x4*)(xrow + 16 * min(lane + 64 * j, nch - 1));
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (lane + 64 * j < nch) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w = xv[j][q];
+                    const float a = __uint_as_float(w << 16), c = __uint_as_float(w & 0xFFFF0000u);
+                    ss = fmaf(a, a, ss);
+                    ss = fmaf(c, c, ss);
+                }
+            }
+        }
+        const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum_hi(ss)), 63));
+        const float r = 1.0f / __builtin_sqrtf(tot / (float)H + p.norm_eps);
+        LDS char* dst = xs + (int64_t)m * p.xpitch;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int c = lane + 64 * j;
+            if (c < nch) {
+                u32x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w = xv[j][q], gw = g[j][q];
+                    const float a = __uint_as_float(w << 16) * r, b2 = __uint_as_float(w & 0xFFFF0000u) * r;
+                    const float ga = __uint_as_float(gw << 16), gb = __uint_as_float(gw & 0xFFFF0000u);
+                    o[q] = (uint32_t)f32_to_bf16_rne(ga * a) | ((uint32_t)f32_to_bf16_rne(gb * b2) << 16);
+                }
+                *(LDS u32x4*)(dst + 16 * c) = o;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // routing: top-k of one token with one wave, batch compaction with one workgroup
 // ------------------------------------------------------------------------------------------
 
@@ -634,9 +691,21 @@ __device__ __forceinline__ void stage_rows_bf16(LDS char* dst, const float* src,
 // recomputes its maximum.  Writes ids, logits and softmax-over-the-k weights in order.  Every id
 // written is in [0, E).
 __device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, uint32_t tag, const Fault& fault,
-                                          LDS int* out_id, LDS float* out_w, LDS float* out_v) {
+                                          const float* bias, LDS int* out_id, LDS float* out_w, LDS float* out_v) {
     const int lane = threadIdx.x & 63;
     const __amdgpu_buffer_rsrc_t rs = dev_rsrc(lrow, (uint32_t)E * 8);  // loads past E return 0
+    // selection bias of the lane's experts, loaded while the logits are polled (past E: 0)
+    float bv[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (bias) {
+        const __amdgpu_buffer_rsrc_t rb = dev_rsrc(bias, (uint32_t)E * 4);
+        const f32x4 b0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)lane * 32, 0, 0));
+        const f32x4 b1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)lane * 32 + 16, 0, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bv[i] = b0[i];
+            bv[4 + i] = b1[i];
+        }
+    }
     float v[8];
     bool gave_up = false;
     for (int it = 0;; ++it) {
@@ -657,47 +726,73 @@ __device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, ui
         __builtin_amdgcn_s_sleep(1);
         asm volatile("" ::: "memory");  // the next iteration reads memory again
     }
+    // selection keys: the logit, or the logit plus the expert's bias
+    float key[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        if (8 * lane + i >= E) v[i] = -INFINITY;
+    for (int i = 0; i < 8; ++i) key[i] = 8 * lane + i >= E ? -INFINITY : v[i] + bv[i];
     auto local_max = [&](float& m, int& mi) {
-        m = v[0];
+        m = key[0];
         mi = 0;
 #pragma unroll
         for (int i = 1; i < 8; ++i) {
-            const bool gt = v[i] > m;
-            m = gt ? v[i] : m;
+            const bool gt = key[i] > m;
+            m = gt ? key[i] : m;
             mi = gt ? i : mi;
         }
     };
     float lm;
     int li;
     local_max(lm, li);
-    float my_v = -INFINITY;
+    float my_v = -INFINITY;  // lane r < k: the logit of the r-th selected expert
     int my_id = 0;
     for (int r = 0; r < k; ++r) {
         const float mx = wave_max_bcast(lm);
         const uint64_t ball = __ballot(lm == mx);
         const int wl = ball ? __ffsll((unsigned long long)ball) - 1 : 0;  // no match only for NaN inputs
         const int wi = __builtin_amdgcn_readlane(li, wl);
+        float raw = v[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) raw = i == wi ? v[i] : raw;
+        raw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, raw), wl));
         if (lane == r) {
-            my_v = mx;
+            my_v = raw;
             my_id = min(8 * wl + wi, E - 1);
         }
         if (lane == wl) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = i == wi ? -INFINITY : v[i];
+            for (int i = 0; i < 8; ++i) key[i] = i == wi ? -INFINITY : key[i];
             local_max(lm, li);
         }
     }
-    // weights: softmax over the k selected logits (lanes 0..k-1 of row 0; k <= 16)
-    const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
+    // weights: softmax over the k selected logits (lanes 0..k-1 of row 0; k <= 16); without a bias
+    // the first selected logit is the largest
+    float top;
+    if (bias) {
+        float t = my_v;  // lanes >= k hold -inf
+        t = fmaxf(t, dpp<0xB1>(t));
+        t = fmaxf(t, dpp<0x4E>(t));
+        t = fmaxf(t, dpp<0x141>(t));
+        t = fmaxf(t, dpp<0x140>(t));
+        top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), 0));
+    } else {
+        top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
+    }
     const float ex = lane < k ? __expf(my_v - top) : 0.0f;
     const float z = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_sum(ex)), 0));
+    // output position: selection order, or with a bias the rank by (logit desc, id asc)
+    int pos = lane;
+    if (bias) {
+        pos = 0;
+        for (int j = 0; j < k; ++j) {
+            const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), j));
+            const int ij = __builtin_amdgcn_readlane(my_id, j);
+            pos += (vj > my_v || (vj == my_v && ij < my_id)) ? 1 : 0;
+        }
+    }
     if (lane < k) {
-        out_id[lane] = my_id;
-        out_v[lane] = my_v;
-        out_w[lane] = gave_up ? __builtin_nanf("") : ex / z;  // NaN weights: every use of this token is invalid
+        out_id[pos] = my_id;
+        out_v[pos] = my_v;
+        out_w[pos] = gave_up ? __builtin_nanf("") : ex / z;  // NaN weights: every use of this token is invalid
     }
 }
 
@@ -721,6 +816,7 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
     const int E = p.E, M = p.M, k = p.k, NP = M * k;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const bool has_sh = p.Is > 0;
+    const float* rbias = (p.router_flags & MOE_ROUTER_BIAS) ? p.rbias : nullptr;
     LDS uint32_t* tokmask = (LDS uint32_t*)sel;              // [kMaxExperts]
     LDS int* offe = (LDS int*)(tokmask + kMaxExperts);       // [kMaxExperts] first pair row of an expert
     LDS int* sid = offe + kMaxExperts;                       // [kMaxTokens * kMaxTopK]
@@ -734,14 +830,14 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
 
     if (!p.route_delegate) {
         for (int m = wave; m < M; m += kWaves)
-            wave_topk(p.ws.logits + (int64_t)m * logit_stride(E), E, k, tag, fault, sid + m * k,
+            wave_topk(p.ws.logits + (int64_t)m * logit_stride(E), E, k, tag, fault, rbias, sid + m * k,
                       sw + m * k, sv + m * k);
     } else {
         // workgroup m < M selects token m's experts and publishes them as tagged words; every
         // workgroup then reads the M * k published (id, weight) pairs instead of M * E logits
         const int b = blockIdx.x;
         if (b < M && wave == 0) {
-            wave_topk(p.ws.logits + (int64_t)b * logit_stride(E), E, k, tag, fault, sid + b * k,
+            wave_topk(p.ws.logits + (int64_t)b * logit_stride(E), E, k, tag, fault, rbias, sid + b * k,
                       sw + b * k, sv + b * k);
             if (lane < k) {
                 uint64_t* dst = p.ws.route + 2 * (int64_t)(b * k + lane);
@@ -1769,7 +1865,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         s_spin = ld_dev(p.ws.hdr + kHdrSpin);
         s_fault = 0u;
     }
-    async_rows_pitch((char*)xs, (const uint8_t*)p.x, M, H * XB, p.xpitch);
+    const bool norm = AF == MOE_FMT_BF16 && (p.router_flags & MOE_ROUTER_NORM) != 0;
+    if (!norm) async_rows_pitch((char*)xs, (const uint8_t*)p.x, M, H * XB, p.xpitch);
     const int e0 = (int)((int64_t)E * b / G), e1 = (int)((int64_t)E * (b + 1) / G);
     const int nrw = min(e1 - e0, kWaves);  // waves with router rows
     Chunk rfirst[NJ];
@@ -1798,6 +1895,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         if (sclw_sh)
             async_dwords_to_lds((char*)sclw_sh, p.w.sh_down_s + (int64_t)h0 * (Is / 32), nown * (Is / 32));
     }
+    if constexpr (AF == MOE_FMT_BF16)
+        if (norm) rms_norm_rows<NJ>(p, xs);  // the normed token rows replace x everywhere
     __builtin_amdgcn_s_waitcnt(0);  // token rows (and the slice's shared down rows) in LDS
     __syncthreads();
     MOE_TRACE(1);

@@ -5,7 +5,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MOE_FMT_F32, moe_desc_t, moe_dispatch_t, moe_weights_t, moe_workspace_bytes)
+from . import (MOE_FMT_F32, MOE_ROUTER_BIAS, MOE_ROUTER_NORM, moe_desc_t, moe_dispatch_t, moe_weights_t,
+               moe_workspace_bytes)
 from . import synth
 
 
@@ -17,9 +18,17 @@ def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(a).to(device)
 
 
-def desc_of(cfg: synth.LayerConfig, max_tokens: int = None) -> moe_desc_t:
-    return moe_desc_t(cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter, cfg.shared_inter,
-                      max_tokens or cfg.M, cfg.act_fmt, cfg.weight_fmt)
+def desc_of(cfg: synth.LayerConfig, max_tokens: int = None, layer: "DeviceLayer" = None) -> moe_desc_t:
+    """The C descriptor of a layer configuration; the router prologue tensors come from `layer`."""
+    flags = (MOE_ROUTER_NORM if cfg.router_norm else 0) | (MOE_ROUTER_BIAS if cfg.router_bias else 0)
+    d = moe_desc_t(cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter, cfg.shared_inter,
+                   max_tokens or cfg.M, cfg.act_fmt, cfg.weight_fmt, flags, cfg.norm_eps)
+    if flags:
+        if layer is None:
+            raise ValueError("%s has a router prologue: pass its DeviceLayer" % cfg.name)
+        d.norm_weight = layer.t["norm_w"].data_ptr() if cfg.router_norm else None
+        d.router_bias = layer.t["router_bias"].data_ptr() if cfg.router_bias else None
+    return d
 
 
 class DeviceLayer:
@@ -28,6 +37,10 @@ class DeviceLayer:
     def __init__(self, layer: synth.Layer, device="cuda"):
         self.cfg = layer.cfg
         self.t = {"router": to_device(layer.router, device)}
+        if getattr(layer, "norm_w", None) is not None:
+            self.t["norm_w"] = to_device(layer.norm_w, device)
+        if getattr(layer, "router_bias", None) is not None:
+            self.t["router_bias"] = to_device(layer.router_bias, device)
         for name in ("gate", "up", "down"):
             data, sc = layer.stacks[name]
             self.t[name] = to_device(data, device)

@@ -33,13 +33,14 @@ def log(*a):
 def _layer_key(cfg):
     """Everything the layer's weights depend on (not the token workload)."""
     return (cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter, cfg.shared_inter, cfg.act_fmt, cfg.weight_fmt,
-            cfg.layer_seed)
+            cfg.layer_seed, cfg.router_norm, cfg.router_bias)
 
 
 @functools.lru_cache(maxsize=4)
 def _host_layer(key):
-    H, E, k, I, Is, af, wf, seed = key
-    return synth.Layer(synth.LayerConfig("layer", H, E, k, I, Is, af, wf, (1,), "iid", seed))
+    H, E, k, I, Is, af, wf, seed, rn, rb = key
+    return synth.Layer(synth.LayerConfig("layer", H, E, k, I, Is, af, wf, (1,), "iid", seed, router_norm=rn,
+                                         router_bias=rb))
 
 
 @functools.lru_cache(maxsize=2)
@@ -63,7 +64,7 @@ def accepted_hidden(cfg, layer, min_gap=1e-3, start=0):
     d = O.layer_desc(cfg)
     for s in range(start, start + 500):
         x = synth.make_hidden(cfg, s)
-        if O.route(d, x, layer.router)[3].min() >= min_gap:
+        if O.route(d, x, layer.router, **O.router_aux(layer))[3].min() >= min_gap:
             return x, s
     raise RuntimeError("no accepted hidden seed")
 
@@ -83,12 +84,13 @@ class Case:
                 x_host = synth.make_hidden(cfg, hidden_seed)
         self.x_host = np.ascontiguousarray(x_host)
         self.M = self.x_host.shape[0]
-        self.desc = dev.desc_of(cfg, max_tokens=max(self.M, cfg.M))
+        self.desc = dev.desc_of(cfg, max_tokens=max(self.M, cfg.M), layer=self.dl)
         self.x = dev.to_device(self.x_host)
         self.ws = dev.workspace(self.desc)
         d = O.layer_desc(cfg)
         self.y_ref, self.ids_ref, self.w_ref, self.gap = O.forward(d, O.layer_weights(self.layer), self.x_host,
-                                                                   self.layer.router, threads=oracle_threads)
+                                                                   self.layer.router, threads=oracle_threads,
+                                                                   **O.router_aux(self.layer))
         self.comp_ref = O.compact(self.ids_ref, self.w_ref, cfg.num_experts)
 
     def run(self, req_offsets=None, disp=None, stream=None, x=None):

@@ -79,6 +79,16 @@ def test_route_rejects(kw, M, status):
     assert call_route(ling(**kw), M=M) == status
 
 
+def test_router_prologue_checks():
+    assert call_route(ling(router_flags=4)) == mdl.MOE_ERR_FORMAT
+    assert call_route(ling(router_flags=mdl.MOE_ROUTER_NORM, norm_eps=1e-6)) == mdl.MOE_ERR_NULL
+    assert call_route(ling(router_flags=mdl.MOE_ROUTER_BIAS)) == mdl.MOE_ERR_NULL
+    assert call_route(ling(router_flags=mdl.MOE_ROUTER_BIAS, router_bias=FAKE + 4)) == mdl.MOE_ERR_ALIGN
+    assert call_route(ling(router_flags=mdl.MOE_ROUTER_NORM, norm_eps=-1.0, norm_weight=FAKE)) == mdl.MOE_ERR_SHAPE
+    assert call_route(ling(act_format=mdl.MOE_FMT_F32, weight_format=mdl.MOE_FMT_F32, hidden=128, inter=64,
+                           shared_inter=64, router_flags=mdl.MOE_ROUTER_NORM, norm_weight=FAKE)) == mdl.MOE_ERR_FORMAT
+
+
 def test_route_null_align_workspace():
     d = ling()
     assert call_route(d, x=None) == mdl.MOE_ERR_NULL

@@ -18,9 +18,10 @@ pytestmark = pytest.mark.gpu
 BF16, MXFP4, F32 = synth.BF16, synth.MXFP4, synth.F32
 
 
-def small(name, fmt=BF16, H=512, E=64, k=4, I=192, Is=128, lens=(5,), recipe="shared_base"):
+def small(name, fmt=BF16, H=512, E=64, k=4, I=192, Is=128, lens=(5,), recipe="shared_base", norm=False, bias=False):
     act = F32 if fmt == F32 else BF16
-    return synth.LayerConfig(name, H, E, k, I, Is, act, fmt, tuple(lens), recipe, 7)
+    return synth.LayerConfig(name, H, E, k, I, Is, act, fmt, tuple(lens), recipe, 7, router_norm=norm,
+                             router_bias=bias, hidden_scale=4.0 if norm else 1.0)
 
 
 SMALL = [
@@ -47,6 +48,16 @@ SMALL = [
     small("bf16_E384_m3", E=384, k=6, lens=(3,)),
     small("bf16_E512_k16_m1", E=512, k=16, lens=(1,), recipe="iid"),
     small("bf16_E200_m1", E=200, k=8, lens=(1,), recipe="iid"),
+    # the router chain's RMSNorm prologue and bias-corrected selection, alone and together, below
+    # and above the delegated top-k, with vector and matrix-core gate/up
+    small("router_nb_m1", lens=(1,), recipe="iid", norm=True, bias=True),
+    small("router_nb_m6", lens=(6,), norm=True, bias=True),
+    small("router_nb_m16", E=128, k=8, lens=(4, 5, 7), norm=True, bias=True),
+    small("router_norm_m3", lens=(3,), norm=True),
+    small("router_bias_m2", E=512, k=8, lens=(2,), bias=True),
+    small("router_bias_k16", E=128, k=16, lens=(5,), bias=True),
+    small("router_nb_mxfp4_m6", MXFP4, lens=(6,), norm=True, bias=True),
+    small("router_nb_tail", H=520, I=200, Is=72, lens=(7,), norm=True, bias=True),
 ]
 
 
@@ -80,7 +91,8 @@ def test_tiny_f32_config():
 
 
 @pytest.mark.parametrize("name", ["ling_bf16_m1", "ling_bf16_m6", "ling_bf16_m16_ragged", "ling_mxfp4_m1",
-                                  "ling_mxfp4_m6", "ling_mxfp4_m16_ragged"])
+                                  "ling_mxfp4_m6", "ling_mxfp4_m16_ragged", "ling_bf16_m1_router",
+                                  "ling_bf16_m6_router", "ling_bf16_m16_ragged_router", "ling_mxfp4_m6_router"])
 def test_ling_configs(name):
     cfg = synth.CONFIGS[name]
     G.log("ling", name, "generating layer")
@@ -132,6 +144,22 @@ def test_permutation_equivariant_slice_mode(fmt):
     assert torch.equal(yp, y1[perm])
     for m in range(case.M):
         assert set(idsp[m].tolist()) == set(ids1[perm[m]].tolist())
+
+
+def test_router_prologue_deterministic_and_permutation_equivariant():
+    cfg = small("perm_nb", lens=(11,), norm=True, bias=True)
+    case = G.Case(cfg)
+    y1, ids1, w1 = case.run()
+    y2, ids2, w2 = case.run()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(ids1, ids2) and torch.equal(w1, w2)
+    err, _ = G.y_error(y1, case.y_ref)
+    G.log("perm_nb", "err/rms=%.3e" % err)
+    assert err <= G.TOL[BF16]
+    perm = torch.tensor(np.random.default_rng(4).permutation(case.M), device="cuda")
+    yp, _, _ = case.run(x=case.x[perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y1[perm])
 
 
 @pytest.mark.parametrize("lens", [(1,), (6,)], ids=["m1_slice", "m6_unit_major"])
@@ -243,8 +271,9 @@ def test_hip_graph_replay_matches_eager():
         assert torch.equal(ye2, y_e)
 
 
-def test_route_only_matches_forward_routing():
-    cfg = small("route", lens=(9,))
+@pytest.mark.parametrize("norm,bias", [(False, False), (True, True)], ids=["plain", "norm_bias"])
+def test_route_only_matches_forward_routing(norm, bias):
+    cfg = small("route", lens=(9,), norm=norm, bias=bias)
     case = G.Case(cfg)
     ids = torch.full((case.M, cfg.top_k), -1, dtype=torch.int32, device="cuda")
     w = torch.zeros((case.M, cfg.top_k), dtype=torch.float32, device="cuda")
