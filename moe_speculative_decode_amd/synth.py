@@ -34,8 +34,10 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-F32, BF16, MXFP4 = 0, 1, 2
-FORMAT_NAMES = {F32: "f32", BF16: "bf16", MXFP4: "mxfp4"}
+F32, BF16, MXFP4, FP8 = 0, 1, 2, 3
+FORMAT_NAMES = {F32: "f32", BF16: "bf16", MXFP4: "mxfp4", FP8: "fp8"}
+FP8_BLOCK = 128      # FP8 weights: one binary32 scale per block of 128 rows x 128 columns
+FP8_MAX = 448.0      # largest finite E4M3 magnitude
 
 # stream tags
 T_ROUTER, T_GATE, T_UP, T_DOWN, T_SH_GATE, T_SH_UP, T_SH_DOWN, T_HIDDEN_BASE, T_HIDDEN_NOISE = range(9)
@@ -101,6 +103,11 @@ CONFIGS: Dict[str, LayerConfig] = {
                            "Ling shapes, MXFP4 expert weights, bf16 router/activations, M=1"),
     "ling_mxfp4_m16_ragged": _ling("ling_mxfp4_m16_ragged", MXFP4, (2, 6, 3, 5), "shared_base",
                                    "Ling shapes, MXFP4 expert weights, M=16 ragged verify, requests {2,6,3,5}"),
+    # FP8 (E4M3) expert weights with one binary32 scale per 128 x 128 block, bf16 router/activations
+    "ling_fp8_m1": _ling("ling_fp8_m1", FP8, (1,), "iid", "Ling shapes, FP8 block-128 expert weights, M=1"),
+    "ling_fp8_m6": _ling("ling_fp8_m6", FP8, (6,), "shared_base", "Ling shapes, FP8 block-128 expert weights, M=6"),
+    "ling_fp8_m16_ragged": _ling("ling_fp8_m16_ragged", FP8, (2, 6, 3, 5), "shared_base",
+                                 "Ling shapes, FP8 block-128 expert weights, M=16 ragged verify"),
     # the router chain with its RMSNorm prologue and bias-corrected top-k (hidden states x4)
     "ling_bf16_m1_router": _ling("ling_bf16_m1_router", BF16, (1,), "iid",
                                  "Ling shapes, bf16, M=1, RMSNorm prologue + bias-corrected top-k", True),
@@ -182,12 +189,49 @@ def mxfp4_encode(w: np.ndarray):
     return np.ascontiguousarray(packed), np.ascontiguousarray(scales)
 
 
+def _e4m3_round(q: np.ndarray) -> np.ndarray:
+    """float64 -> E4M3 code bytes (OCP 8-bit floating point): nearest value, ties to the even
+    mantissa, saturating at +-448.  Spacing 2^(e-3) in the binade [2^e, 2^(e+1)), e >= -6; below
+    2^-6 the subnormal spacing 2^-9."""
+    sign = (q < 0) | ((q == 0) & np.signbit(q))
+    a = np.minimum(np.abs(q), FP8_MAX)
+    _, ex = np.frexp(a)                       # a = f * 2^ex, f in [0.5, 1): binade 2^(ex-1)
+    e = np.maximum(ex.astype(np.int64) - 1, -6)
+    ulp = np.ldexp(1.0, e - 3)
+    n = np.rint(a / ulp)                      # numpy rint: ties to even
+    v = np.minimum(n * ulp, FP8_MAX)          # a carry into the next binade stays representable
+    _, ex2 = np.frexp(v)
+    e2 = np.maximum(ex2.astype(np.int64) - 1, -6)
+    normal = v >= 2.0 ** -6
+    field = np.where(normal, e2 + 7, 0)
+    mant = np.where(normal, np.rint(v / np.ldexp(1.0, e2 - 3)) - 8, np.rint(v / 2.0 ** -9))
+    code = (field << 3) | mant.astype(np.int64)
+    return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
+
+
+def fp8_block_encode(w: np.ndarray):
+    """float64 [N, K] -> (E4M3 codes uint8 [N, K], binary32 scales [N/128, K/128]).  Per block of
+    128 x 128 the scale is amax / 448 (rounded to binary32; 1 for an all-zero block) and each
+    element is encoded as w / scale."""
+    w = np.asarray(w, dtype=np.float64)
+    N, K = w.shape
+    assert N % FP8_BLOCK == 0 and K % FP8_BLOCK == 0
+    blk = w.reshape(N // FP8_BLOCK, FP8_BLOCK, K // FP8_BLOCK, FP8_BLOCK)
+    amax = np.abs(blk).max(axis=(1, 3))
+    scales = np.where(amax > 0, amax / FP8_MAX, 1.0).astype(np.float32)
+    q = blk / scales.astype(np.float64)[:, None, :, None]
+    codes = _e4m3_round(q).reshape(N, K)
+    return np.ascontiguousarray(codes), np.ascontiguousarray(scales)
+
+
 def encode_weight(w: np.ndarray, fmt: int):
     """float64 [N, K] -> storage of format fmt: (data, scales or None)."""
     if fmt == F32:
         return f32_bits(w), None
     if fmt == BF16:
         return bf16_bits(w), None
+    if fmt == FP8:
+        return fp8_block_encode(w)
     return mxfp4_encode(w)
 
 
@@ -228,6 +272,9 @@ class Layer:
             if wf == MXFP4:
                 self.stacks[name] = (np.zeros((E, rows, cols // 2), np.uint8),
                                      np.zeros((E, rows, cols // MX_BLOCK), np.uint8))
+            elif wf == FP8:
+                self.stacks[name] = (np.zeros((E, rows, cols), np.uint8),
+                                     np.zeros((E, rows // FP8_BLOCK, cols // FP8_BLOCK), np.float32))
             else:
                 dt = np.float32 if wf == F32 else np.uint16
                 self.stacks[name] = (np.zeros((E, rows, cols), dt), None)

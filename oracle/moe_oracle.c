@@ -33,7 +33,11 @@
  * Storage formats it decodes (each from its published definition, see the decode functions):
  *   fmt 0 = IEEE binary32, fmt 1 = bfloat16 (upper half of a binary32), fmt 2 = MXFP4
  *   (OCP Microscaling v1.0: E2M1 element codes, two per byte with element 2i in the low nibble,
- *   one E8M0 scale byte per 32 consecutive elements along the input dimension K).
+ *   one E8M0 scale byte per 32 consecutive elements along the input dimension K), fmt 3 = FP8
+ *   block-quantised weights (OCP 8-bit floating point E4M3 codes, one per byte, times one binary32
+ *   scale per block of 128 rows x 128 columns: "Chasing the Batch-1 Floor", section "Where the
+ *   time goes now": fp8 weights with block 128, which with moe_intermediate_size 768 rules out a
+ *   four-way split of the intermediate dimension, so the blocks span 128 along both dimensions).
  *
  * Batch-level dispatch (oracle_compact): the unique selected experts across all M tokens in
  * ascending id order, each with its (token, slot, weight) list stable in pair index m*k+j, and
@@ -49,7 +53,8 @@
 #include <omp.h>
 #endif
 
-enum { OF_F32 = 0, OF_BF16 = 1, OF_MXFP4 = 2 };
+enum { OF_F32 = 0, OF_BF16 = 1, OF_MXFP4 = 2, OF_FP8 = 3 };
+enum { FP8_BLOCK = 128 };
 
 /* ---- element decoders ------------------------------------------------------------------ */
 
@@ -73,6 +78,16 @@ double oracle_e2m1_to_f64(uint8_t code) {
 
 /* E8M0 (OCP MX v1.0): an unsigned biased exponent, value 2^(S-127); S = 255 is NaN. */
 double oracle_e8m0_to_f64(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
+
+/* E4M3 (OCP 8-bit floating point, E4M3): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits;
+   no infinities; exponent and mantissa all ones is NaN.  Exponent field 0 is subnormal:
+   0.m * 2^(1-7); otherwise 1.m * 2^(e-7).  The largest finite magnitude is 1.75 * 2^8 = 448. */
+double oracle_e4m3_to_f64(uint8_t code) {
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = (e == 0) ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
 
 /* The bfloat16 value nearest to v (ties: the even significand), as a double: bfloat16 keeps 8
    significant bits, its normal exponents run from -126 to 127 and below 2^-126 its spacing stays
@@ -104,8 +119,8 @@ static void rms_norm(const double* x, const double* g, int H, double eps, double
 /* A row-major [rows][cols] matrix in one of the storage formats. */
 typedef struct {
     int fmt;
-    const void* data;      /* f32 / bf16 elements, or MXFP4 packed codes [rows][cols/2] */
-    const uint8_t* scales; /* MXFP4 only: [rows][cols/32] */
+    const void* data;      /* f32 / bf16 elements, MXFP4 packed codes [rows][cols/2], FP8 codes [rows][cols] */
+    const uint8_t* scales; /* MXFP4: E8M0 bytes [rows][cols/32]; FP8: binary32 [rows/128][cols/128] */
     int64_t rows, cols;
 } omat;
 
@@ -113,6 +128,12 @@ static double mat_at(const omat* A, int64_t r, int64_t c) {
     switch (A->fmt) {
     case OF_F32: return dec_f32(((const uint32_t*)A->data)[r * A->cols + c]);
     case OF_BF16: return oracle_bf16_to_f64(((const uint16_t*)A->data)[r * A->cols + c]);
+    case OF_FP8: {
+        const uint8_t code = ((const uint8_t*)A->data)[r * A->cols + c];
+        uint32_t sbits;
+        memcpy(&sbits, A->scales + 4 * ((r / FP8_BLOCK) * (A->cols / FP8_BLOCK) + c / FP8_BLOCK), 4);
+        return oracle_e4m3_to_f64(code) * dec_f32(sbits);
+    }
     default: {
         uint8_t byte = ((const uint8_t*)A->data)[r * (A->cols / 2) + c / 2];
         uint8_t code = (c & 1) ? (byte >> 4) : (byte & 15);
@@ -139,6 +160,9 @@ static omat expert_mat(int fmt, const void* data, const uint8_t* scales, int64_t
     if (fmt == OF_MXFP4) {
         A.data = (const uint8_t*)data + e * rows * (cols / 2);
         A.scales = scales + e * rows * (cols / 32);
+    } else if (fmt == OF_FP8) {
+        A.data = (const uint8_t*)data + e * rows * cols;
+        A.scales = scales + 4 * e * (rows / FP8_BLOCK) * (cols / FP8_BLOCK);
     } else {
         A.data = (const uint8_t*)data + e * rows * cols * (fmt == OF_F32 ? 4 : 2);
         A.scales = NULL;

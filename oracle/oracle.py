@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "moe_oracle.c")
 LIB = os.path.join(HERE, "libmoe_oracle.so")
 
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, FP8 = 0, 1, 2, 3
 
 
 def build(force: bool = True, src: str = SRC, out: str = LIB) -> str:
@@ -63,6 +63,8 @@ def load(path: str):
     L.oracle_e2m1_to_f64.argtypes = [ctypes.c_uint8]
     L.oracle_e8m0_to_f64.restype = ctypes.c_double
     L.oracle_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+    L.oracle_e4m3_to_f64.restype = ctypes.c_double
+    L.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
     L.oracle_round_bf16.restype = ctypes.c_double
     L.oracle_round_bf16.argtypes = [ctypes.c_double]
     L.oracle_route.restype = None
@@ -147,6 +149,10 @@ def e2m1_to_f64(code: int) -> float:
 
 def e8m0_to_f64(s: int) -> float:
     return lib().oracle_e8m0_to_f64(s)
+
+
+def e4m3_to_f64(code: int) -> float:
+    return lib().oracle_e4m3_to_f64(code)
 
 
 def route(d: _Desc, x: np.ndarray, wr: np.ndarray, norm_w=None, bias=None

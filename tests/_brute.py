@@ -12,12 +12,22 @@ E2M1_TABLE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
                        -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
 
 
+def _e4m3_table():
+    """The 256 E4M3 values, from torch's float8_e4m3fn type (a library independent of the oracle)."""
+    import torch
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
 def dec(fmt, data, scales=None):
     """storage -> float64 (same shape as the logical matrix)."""
     if fmt == 0:
         return np.asarray(data, dtype=np.float32).astype(np.float64)
     if fmt == 1:
         return (np.asarray(data, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if fmt == 3:  # E4M3 codes times one binary32 scale per 128 x 128 block (last two axes)
+        vals = _e4m3_table()[np.asarray(data, dtype=np.uint8)]
+        sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
+        return vals * np.repeat(np.repeat(sc, 128, axis=-2), 128, axis=-1)
     codes = np.asarray(data, dtype=np.uint8)
     lo = codes & 15
     hi = codes >> 4

@@ -38,6 +38,17 @@ MUTANTS = {
     "norm_mean": ("sqrt(ss / H + eps)", "sqrt(ss / (H - 1) + eps)"),
     "norm_skipped": ("    if (d->router_flags & ORACLE_NORM) {", "    if (0) {"),
     "round_ties_up": ("(r > 0.5 || (r == 0.5 && fmod(fl, 2.0) != 0.0))", "(r >= 0.5)"),
+    # FP8 block-quantised weights
+    "e4m3_bias": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    "e4m3_subnormal": ("ldexp(m / 8.0, -6)", "ldexp(m / 8.0, -7)"),
+    "fp8_scale_col": ("4 * ((r / FP8_BLOCK) * (A->cols / FP8_BLOCK) + c / FP8_BLOCK)",
+                      "4 * ((r / FP8_BLOCK) * (A->cols / FP8_BLOCK) + c / 64)"),
+    "fp8_scale_row": ("4 * ((r / FP8_BLOCK) * (A->cols / FP8_BLOCK) + c / FP8_BLOCK)",
+                      "4 * ((r / 64) * (A->cols / FP8_BLOCK) + c / FP8_BLOCK)"),
+    "fp8_scale_transposed": ("4 * ((r / FP8_BLOCK) * (A->cols / FP8_BLOCK) + c / FP8_BLOCK)",
+                             "4 * ((c / FP8_BLOCK) * (A->rows / FP8_BLOCK) + r / FP8_BLOCK)"),
+    "fp8_expert_scales": ("A.scales = scales + 4 * e * (rows / FP8_BLOCK) * (cols / FP8_BLOCK);",
+                          "A.scales = scales;"),
 }
 
 # pins that run quickly; together they must catch each mutant
@@ -58,6 +69,9 @@ PINS = [
     P.test_biased_selection_vs_full_sort,
     P.test_biased_selection_constructed,
     lambda: P.test_dense_brute_force_with_router_prologue(synth.BF16, (2, 3)),
+    P.test_e4m3_all_codes,
+    P.test_fp8_block_scale_layout,
+    lambda: P.test_dense_brute_force(synth.FP8, 256, 8, 2, 128, 128, (3,)),
 ]
 
 

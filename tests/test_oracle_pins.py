@@ -112,6 +112,49 @@ def test_mxfp4_roundtrip_and_error_bound():
     assert abs(std / 0.02 - 1) < 0.10
 
 
+def test_e4m3_all_codes():
+    """OCP 8-bit floating point E4M3: every code against torch's float8_e4m3fn."""
+    ref = B._e4m3_table()
+    got = np.array([O.e4m3_to_f64(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    assert O.e4m3_to_f64(0x7E) == 448.0 and O.e4m3_to_f64(0x01) == 2.0 ** -9 and O.e4m3_to_f64(0x08) == 2.0 ** -6
+
+
+def test_fp8_block_scale_layout():
+    """A 256 x 384 matrix of one code per element and a distinct power-of-two scale per 128 x 128
+    block: element (r, c) decodes to value(code) * scale[r // 128][c // 128]."""
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 256, size=(256, 384), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x10  # no NaN codes
+    scales = np.array([[2.0 ** -1, 2.0 ** 2, 2.0 ** -5], [2.0 ** 3, 2.0 ** -2, 2.0 ** 0]], np.float32)
+    got = O.decode_matrix(synth.FP8, codes, scales, 256, 384)
+    table = np.array([O.e4m3_to_f64(c) for c in range(256)])
+    for (r, c) in [(0, 0), (127, 127), (128, 0), (0, 128), (255, 383), (130, 260), (5, 300)]:
+        assert got[r, c] == table[codes[r, c]] * scales[r // 128, c // 128]
+    assert np.array_equal(got, B.dec(synth.FP8, codes, scales))
+
+
+def test_fp8_roundtrip_and_error_bound():
+    w = synth.normal(3, 1, 1, 256 * 384).reshape(256, 384) * 0.02
+    codes, scales = synth.fp8_block_encode(w)
+    d = O.decode_matrix(synth.FP8, codes, scales, 256, 384)
+    S = np.repeat(np.repeat(scales.astype(np.float64), 128, 0), 128, 1)
+    q = np.abs(w) / S
+    # half the E4M3 spacing at |q|: 2^(floor(log2 q) - 4) in the normal range, 2^-10 below 2^-6
+    e = np.floor(np.log2(np.maximum(q, 2.0 ** -6)))
+    bound = np.ldexp(1.0, (e - 4).astype(np.int64)) * S
+    assert np.all(np.abs(d - w) <= bound * (1 + 2 ** -20))
+    # each block's largest magnitude maps to 448 (within the binary32 rounding of its scale)
+    assert np.allclose(np.abs(d).reshape(2, 128, 3, 128).max(axis=(1, 3)),
+                       np.abs(w).reshape(2, 128, 3, 128).max(axis=(1, 3)), rtol=2 ** -5)
+    big = synth.normal(4, 2, 1, 256 * 2560).reshape(256, 2560) * 0.02
+    c3, s3 = synth.fp8_block_encode(big)
+    assert abs(O.decode_matrix(synth.FP8, c3, s3, 256, 2560).std() / 0.02 - 1) < 0.02
+
+
 # ---------------------------------------------------------------------------------------------
 # routing
 # ---------------------------------------------------------------------------------------------
@@ -324,6 +367,7 @@ def test_dense_brute_force_with_router_prologue(fmt, lens):
     (synth.BF16, 64, 16, 4, 32, 32, (2, 3)),
     (synth.BF16, 96, 24, 3, 64, 0, (4,)),
     (synth.MXFP4, 64, 16, 4, 32, 64, (3, 3)),
+    (synth.FP8, 256, 8, 2, 128, 128, (3,)),
 ])
 def test_dense_brute_force(fmt, H, E, k, I, Is, lens):
     cfg = tiny_cfg(fmt, H=H, E=E, k=k, I=I, Is=Is, lens=lens, recipe="shared_base")
@@ -352,21 +396,25 @@ def test_config1_tiny_f32_brute_force():
 
 def _identity_storage(fmt, n, alpha=1.0):
     eye = np.eye(n) * alpha
+    if fmt == synth.FP8:  # alpha itself as the code, under unit scales (exact)
+        codes, _ = synth.fp8_block_encode(eye)
+        codes = np.where(eye != 0, synth._e4m3_round(np.full(eye.shape, alpha)), 0).astype(np.uint8)
+        return codes, np.ones((n // 128, n // 128), np.float32)
     return synth.encode_weight(eye, fmt)
 
 
-@pytest.mark.parametrize("fmt", [synth.F32, synth.BF16, synth.MXFP4])
+@pytest.mark.parametrize("fmt", [synth.F32, synth.BF16, synth.MXFP4, synth.FP8])
 @pytest.mark.parametrize("alpha,beta", [(1.0, 1.0), (2.0, 0.5), (0.5, 4.0)])
 def test_closed_form_swiglu(fmt, alpha, beta):
     """E = 1, k = 1, gate = alpha*I, up = beta*I, down = I, no shared expert:
     y = beta*x * (alpha*x) * sigmoid(alpha*x)."""
-    n = 64
+    n = 128 if fmt == synth.FP8 else 64
     act = synth.F32 if fmt == synth.F32 else synth.BF16
     g, gs = _identity_storage(fmt, n, alpha)
     u, us = _identity_storage(fmt, n, beta)
     dn, ds = _identity_storage(fmt, n, 1.0)
     W = {"gate": g[None], "up": u[None], "down": dn[None]}
-    if fmt == synth.MXFP4:
+    if fmt in (synth.MXFP4, synth.FP8):
         W.update(gate_s=gs[None], up_s=us[None], down_s=ds[None])
     W = {kk: np.ascontiguousarray(v) for kk, v in W.items()}
     x = synth.encode_act(synth.normal(9, 8, 0, 3 * n).reshape(3, n) * 2.0, act)
