@@ -318,6 +318,75 @@ def make_hidden(cfg: LayerConfig, hidden_seed: int) -> np.ndarray:
     return encode_act(np.stack(rows) * cfg.hidden_scale, cfg.act_fmt)
 
 
+# ----------------------------------------------------------------------------------------------
+# the LM head (vocabulary projection)
+# ----------------------------------------------------------------------------------------------
+
+T_LM_HEAD, T_LM_HIDDEN = 11, 12
+LM_ROWS_PER_STREAM = 4096  # rows drawn per random stream, so the 157,184 rows generate in parallel
+
+
+@dataclasses.dataclass(frozen=True)
+class LMHeadConfig:
+    name: str
+    hidden: int       # H
+    vocab: int        # V
+    weight_fmt: int   # BF16, or FP8 (E4M3 codes + one binary32 scale per row)
+    M: int            # tokens
+    seed: int = 0
+    description: str = ""
+
+
+LM_HEADS: Dict[str, LMHeadConfig] = {
+    # Ling-3.0-flash's vocabulary projection ("3 ways to boost MoE inference on NVIDIA DGX Spark",
+    # "Model and baseline configuration" and "Optimization 2": 157,184 x 2,560)
+    "lm_head_bf16_m1": LMHeadConfig("lm_head_bf16_m1", 2560, 157184, BF16, 1, 0, "LM head, bf16 weights, M=1"),
+    "lm_head_fp8_m1": LMHeadConfig("lm_head_fp8_m1", 2560, 157184, FP8, 1, 0,
+                                   "LM head, FP8 weights (per-row scale), M=1"),
+    "lm_head_bf16_m6": LMHeadConfig("lm_head_bf16_m6", 2560, 157184, BF16, 6, 0, "LM head, bf16 weights, M=6"),
+    "lm_head_fp8_m6": LMHeadConfig("lm_head_fp8_m6", 2560, 157184, FP8, 6, 0,
+                                   "LM head, FP8 weights (per-row scale), M=6"),
+}
+
+
+def fp8_row_encode(w: np.ndarray):
+    """float64 [V, H] -> (E4M3 codes uint8 [V, H], binary32 scales [V]): per row the scale is
+    amax / 448 (1 for an all-zero row) and each element is encoded as w / scale."""
+    w = np.asarray(w, dtype=np.float64)
+    amax = np.abs(w).max(axis=1)
+    scales = np.where(amax > 0, amax / FP8_MAX, 1.0).astype(np.float32)
+    codes = _e4m3_round(w / scales.astype(np.float64)[:, None])
+    return np.ascontiguousarray(codes), np.ascontiguousarray(scales)
+
+
+def lm_head_weights(cfg: LMHeadConfig, threads: int = 0):
+    """The LM head's weight [V, H] (bf16 storage, or FP8 codes) and its per-row scales (FP8) or None.
+    Rows are drawn N(0, 0.02^2) in streams of LM_ROWS_PER_STREAM rows."""
+    V, H = cfg.vocab, cfg.hidden
+    data = np.zeros((V, H), np.uint16 if cfg.weight_fmt == BF16 else np.uint8)
+    scales = np.zeros(V, np.float32) if cfg.weight_fmt == FP8 else None
+
+    def gen(i):
+        r0 = i * LM_ROWS_PER_STREAM
+        r1 = min(V, r0 + LM_ROWS_PER_STREAM)
+        w = normal(cfg.seed, T_LM_HEAD, i, (r1 - r0) * H).reshape(r1 - r0, H) * WEIGHT_STD
+        if cfg.weight_fmt == FP8:
+            data[r0:r1], scales[r0:r1] = fp8_row_encode(w)
+        else:
+            data[r0:r1] = bf16_bits(w)
+
+    n = (V + LM_ROWS_PER_STREAM - 1) // LM_ROWS_PER_STREAM
+    threads = threads or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(gen, range(n)))
+    return data, scales
+
+
+def lm_head_hidden(cfg: LMHeadConfig, seed: int = 0) -> np.ndarray:
+    """Token rows [M, H] bf16, N(0, 1)."""
+    return bf16_bits(normal(seed, T_LM_HIDDEN, 0, cfg.M * cfg.hidden).reshape(cfg.M, cfg.hidden))
+
+
 _SEEDS_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                            "tests", "golden", "seeds.json")
 

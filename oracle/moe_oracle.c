@@ -431,6 +431,43 @@ void oracle_decode_matrix(int32_t fmt, const void* data, const uint8_t* scales, 
         for (int64_t c = 0; c < cols; ++c) out[r * cols + c] = mat_at(&A, r, c);
 }
 
+/* ---- the LM head (vocabulary projection) ------------------------------------------------ */
+
+/* logits[m][v] = sum_h x[m][h] * W[v][h], summed in ascending h, for M bfloat16 token rows.
+   ("3 ways to boost MoE inference on NVIDIA DGX Spark", "Model and baseline configuration": the LM
+   head projects the hidden dimension 2,560 onto the vocabulary of 157,184; "Optimization 2: Online
+   FP8 LM head quantization": the same GEMM with FP8 weights halves the read; "Chasing the Batch-1
+   Floor", "bf16 router gate and lm_head": bf16 weights with fp32 accumulation.)
+   fmt OF_BF16: W [V][H] bfloat16.  fmt OF_FP8: W [V][H] E4M3 codes times one binary32 scale per row
+   (output channel), scales[v]; the reading of an online quantisation of a bf16 matrix. */
+void oracle_lm_head(int32_t fmt, int32_t H, int32_t V, int32_t M, const void* x, const void* w, const float* scales,
+                    double* logits, int32_t nthreads) {
+    double* xs = (double*)malloc(sizeof(double) * (size_t)M * H);
+    for (int m = 0; m < M; ++m) load_row(OF_BF16, x, m, H, xs + (int64_t)m * H);
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+#endif
+    for (int v = 0; v < V; ++v) {
+        double* wv = (double*)malloc(sizeof(double) * H);
+        if (fmt == OF_FP8) {
+            const uint8_t* codes = (const uint8_t*)w + (int64_t)v * H;
+            const double sc = (double)scales[v];
+            for (int h = 0; h < H; ++h) wv[h] = oracle_e4m3_to_f64(codes[h]) * sc;
+        } else {
+            load_row(OF_BF16, w, v, H, wv);
+        }
+        for (int m = 0; m < M; ++m) {
+            const double* xrow = xs + (int64_t)m * H;
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h) acc += xrow[h] * wv[h];
+            logits[(int64_t)m * V + v] = acc;
+        }
+        free(wv);
+    }
+    free(xs);
+}
+
 int32_t oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

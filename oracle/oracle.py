@@ -83,6 +83,9 @@ def load(path: str):
     L.oracle_decode_matrix.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_void_p]
     L.oracle_max_threads.restype = ctypes.c_int32
+    L.oracle_lm_head.restype = None
+    L.oracle_lm_head.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
     return L
 
 
@@ -205,6 +208,18 @@ def decode_matrix(fmt: int, data: np.ndarray, scales: Optional[np.ndarray], rows
     out = np.zeros((rows, cols))
     lib().oracle_decode_matrix(fmt, _ptr(np.ascontiguousarray(data)),
                                _ptr(None if scales is None else np.ascontiguousarray(scales)), rows, cols, _ptr(out))
+    return out
+
+
+def lm_head(fmt: int, x: np.ndarray, w: np.ndarray, scales: Optional[np.ndarray] = None, threads: int = 0):
+    """logits [M, V] fp64 of the LM head: x [M, H] bf16 storage, w [V, H] bf16 or FP8 codes with
+    per-row float32 scales [V]."""
+    M, H = x.shape
+    V = w.shape[0]
+    out = np.zeros((M, V))
+    lib().oracle_lm_head(fmt, H, V, M, _ptr(np.ascontiguousarray(x)), _ptr(np.ascontiguousarray(w)),
+                         _ptr(None if scales is None else np.ascontiguousarray(scales, dtype=np.float32)),
+                         _ptr(out), threads)
     return out
 
 

@@ -49,6 +49,11 @@ MUTANTS = {
                              "4 * ((c / FP8_BLOCK) * (A->rows / FP8_BLOCK) + r / FP8_BLOCK)"),
     "fp8_expert_scales": ("A.scales = scales + 4 * e * (rows / FP8_BLOCK) * (cols / FP8_BLOCK);",
                           "A.scales = scales;"),
+    # LM head
+    "lm_head_row_scale": ("const double sc = (double)scales[v];", "const double sc = (double)scales[0];"),
+    "lm_head_transposed": ("const uint8_t* codes = (const uint8_t*)w + (int64_t)v * H;",
+                           "const uint8_t* codes = (const uint8_t*)w + (int64_t)v;"),
+    "lm_head_token": ("const double* xrow = xs + (int64_t)m * H;", "const double* xrow = xs;"),
 }
 
 # pins that run quickly; together they must catch each mutant
@@ -72,6 +77,8 @@ PINS = [
     P.test_e4m3_all_codes,
     P.test_fp8_block_scale_layout,
     lambda: P.test_dense_brute_force(synth.FP8, 256, 8, 2, 128, 128, (3,)),
+    lambda: P.test_lm_head_vs_numpy(synth.FP8),
+    lambda: P.test_lm_head_identity_rows(synth.FP8),
 ]
 
 

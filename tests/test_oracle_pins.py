@@ -508,6 +508,51 @@ def test_compaction_vs_sets(M, k, E):
 
 
 # ---------------------------------------------------------------------------------------------
+# the LM head
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", [synth.BF16, synth.FP8])
+def test_lm_head_vs_numpy(fmt):
+    cfg = synth.LMHeadConfig("t", 256, 1000, fmt, 5, 3)
+    w, sc = synth.lm_head_weights(cfg)
+    x = synth.lm_head_hidden(cfg, 1)
+    got = O.lm_head(fmt, x, w, sc)
+    if fmt == synth.FP8:
+        wd = B._e4m3_table()[w] * sc.astype(np.float64)[:, None]
+    else:
+        wd = B.dec(synth.BF16, w)
+    ref = B.dec(synth.BF16, x) @ wd.T
+    assert got.shape == (5, 1000)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("fmt", [synth.BF16, synth.FP8])
+def test_lm_head_identity_rows(fmt):
+    """V = H rows of a scaled identity (alpha on the diagonal): logits = alpha * x exactly, and with
+    FP8 a row scale s multiplies its logit by s."""
+    H = 64
+    x = synth.lm_head_hidden(synth.LMHeadConfig("t", H, H, fmt, 3, 0), 2)
+    xd = B.dec(synth.BF16, x)
+    if fmt == synth.FP8:
+        codes = np.where(np.eye(H) != 0, synth._e4m3_round(np.full((H, H), 2.0)), 0).astype(np.uint8)
+        sc = np.ldexp(1.0, np.arange(H) % 5 - 2).astype(np.float32)
+        got = O.lm_head(fmt, x, codes, sc)
+        assert np.array_equal(got, xd * 2.0 * sc.astype(np.float64)[None, :])
+    else:
+        w = synth.bf16_bits(np.eye(H) * 2.0)
+        assert np.array_equal(O.lm_head(fmt, x, w), xd * 2.0)
+
+
+def test_fp8_row_encoder_bound():
+    w = synth.normal(5, 11, 0, 64 * 512).reshape(64, 512) * 0.02
+    codes, sc = synth.fp8_row_encode(w)
+    d = B._e4m3_table()[codes] * sc.astype(np.float64)[:, None]
+    q = np.abs(w) / sc.astype(np.float64)[:, None]
+    e = np.floor(np.log2(np.maximum(q, 2.0 ** -6)))
+    assert np.all(np.abs(d - w) <= np.ldexp(1.0, (e - 4).astype(np.int64)) * sc[:, None] * (1 + 2 ** -20))
+
+
+# ---------------------------------------------------------------------------------------------
 # generator
 # ---------------------------------------------------------------------------------------------
 
