@@ -38,7 +38,7 @@ PEAK_HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["moe_speculative_decode_amd/csrc/moe_layer.hip", "moe_speculative_decode_amd/csrc/moe_internal.h"]
 HEADLINE = "ling_bf16_m1"
 WORKLOADS = ["ling_bf16_m1", "ling_bf16_m6", "ling_bf16_m16_ragged", "ling_mxfp4_m1", "ling_mxfp4_m6",
-             "ling_mxfp4_m16_ragged"]
+             "ling_mxfp4_m16_ragged", "ling_fp8_m1", "ling_fp8_m6", "ling_fp8_m16_ragged"]
 COLD_BYTES = 1 << 30
 
 
@@ -52,6 +52,8 @@ def algorithmic_bytes(cfg, U: int) -> int:
     def mat(rows, cols):
         if cfg.weight_fmt == synth.MXFP4:
             return rows * cols // 2 + rows * cols // 32
+        if cfg.weight_fmt == synth.FP8:  # one byte a code, 4 bytes a 128 x 128 block scale
+            return rows * cols + 4 * (rows // synth.FP8_BLOCK) * (cols // synth.FP8_BLOCK)
         return rows * cols * (4 if cfg.weight_fmt == synth.F32 else 2)
 
     expert = 2 * mat(I, H) + mat(H, I)

@@ -60,7 +60,10 @@ extern "C" {
 typedef enum {
     MOE_FMT_F32 = 0,   /* IEEE binary32 */
     MOE_FMT_BF16 = 1,  /* bfloat16 */
-    MOE_FMT_MXFP4 = 2  /* OCP MX v1.0 FP4 (E2M1) codes + E8M0 scale per 32 elements of K */
+    MOE_FMT_MXFP4 = 2, /* OCP MX v1.0 FP4 (E2M1) codes + E8M0 scale per 32 elements of K */
+    MOE_FMT_FP8 = 3    /* OCP FP8 E4M3 codes, one per byte, + one binary32 scale per block of
+                          128 rows x 128 columns ("Chasing the Batch-1 Floor", section "Where the
+                          time goes now": fp8 expert weights with block 128) */
 } moe_format_t;
 
 typedef enum {
@@ -88,7 +91,8 @@ typedef enum {
 #define MOE_MAX_HIDDEN_F32 256 /* H, binary32 layer */
 #define MOE_MAX_INTER_F32 256  /* I and Is, binary32 layer */
 
-/* Layer description.  H, I, Is multiples of 8 (of 32 for MXFP4), within the maxima above;
+/* Layer description.  H, I, Is multiples of 8 (of 32 for MXFP4, of 128 for FP8), within the maxima
+   above (FP8 and MXFP4 use the bf16 maxima);
    1 <= k <= min(E, 16); E <= 512; 1 <= max_tokens <= 16.  A call whose shape leaves no room for the
    kernel's on-chip (LDS) layout at the given M is rejected with MOE_ERR_SHAPE before anything is
    enqueued (for example k = 16 with 16 tokens of Ling width). */
@@ -100,7 +104,7 @@ typedef struct {
     int32_t shared_inter;  /* Is, shared expert intermediate size; 0 = no shared expert */
     int32_t max_tokens;    /* largest M the workspace is sized for */
     int32_t act_format;    /* x, router weight and y: MOE_FMT_BF16, or MOE_FMT_F32 with F32 weights */
-    int32_t weight_format; /* routed and shared expert weights: F32 (with F32 act), BF16 or MXFP4 */
+    int32_t weight_format; /* routed and shared expert weights: F32 (with F32 act), BF16, MXFP4 or FP8 */
     /* The router chain's optional steps either side of the gate matvec ("Chasing the Batch-1
        Floor", section "PDL: stacking the latency floors of small kernels": norm -> gate matvec ->
        top-k, the top-k with a bias).  All zero (the default of a zero-filled struct): neither. */
@@ -123,8 +127,10 @@ typedef struct {
 
 /* Expert weights.  Routed stacks are expert-major: gate, up [E][I][H]; down [E][H][I].
    Shared expert: sh_gate, sh_up [Is][H]; sh_down [H][Is].  For MXFP4 the data pointers hold the
-   packed codes (K/2 bytes per row) and the *_s pointers the scales ([rows][K/32] bytes); the *_s
-   pointers are ignored (may be NULL) for the other formats. */
+   packed codes (K/2 bytes per row) and the *_s pointers the scales ([rows][K/32] bytes).  For FP8
+   the data pointers hold one E4M3 code per element ([rows][K] bytes) and the *_s pointers binary32
+   scales [rows/128][K/128] per matrix (expert-major like the codes): element (r, c) is
+   E4M3(code) * scale[r/128][c/128].  The *_s pointers are ignored (may be NULL) for bf16 and f32. */
 typedef struct {
     const void *gate, *up, *down;
     const uint8_t *gate_s, *up_s, *down_s;
@@ -196,6 +202,27 @@ int moe_decode_forward_noalloc(const moe_desc_t* d, int32_t M, const void* x, co
                                const moe_weights_t* w, const int32_t* req_offsets, int32_t R, void* y,
                                int32_t* topk_ids_out, float* topk_w_out, const moe_dispatch_t* disp,
                                void* stream);
+
+/* ---- The LM head --------------------------------------------------------------------------
+   The vocabulary projection of the decode step ("3 ways to boost MoE inference on NVIDIA DGX
+   Spark", "Model and baseline configuration": hidden 2,560 onto a vocabulary of 157,184;
+   "Optimization 2: Online FP8 LM head quantization": FP8 weights halve the read of this GEMM;
+   "Chasing the Batch-1 Floor", "bf16 router gate and lm_head": bf16 weights, fp32 accumulation,
+   a pure bandwidth cost at batch 1). */
+typedef struct {
+    int32_t hidden;        /* H: multiple of 8 (bf16) or 16 (FP8), at most 2560 */
+    int32_t vocab;         /* V: rows of the weight, >= 1 */
+    int32_t weight_format; /* MOE_FMT_BF16, or MOE_FMT_FP8: E4M3 codes with one binary32 scale per row */
+} moe_lm_head_desc_t;
+
+/* logits [M][V] (binary32) = x [M][H] (bf16) . W [V][H]^T, fp32 accumulation; with FP8 weights row v
+   is E4M3(code) * w_scale[v] (w_scale: device binary32 [V], NULL for bf16).  1 <= M <= 16.  Device
+   pointers x, w, logits 16-byte aligned (w_scale 4-byte).  Asynchronous on `stream`, allocates
+   nothing, uses no workspace and no cross-workgroup waits (so it may run beside other work);
+   graph capturable.  Host-side validation as for the layer; a shape whose logit staging does not
+   fit on chip (very large V) returns MOE_ERR_SHAPE. */
+int moe_lm_head(const moe_lm_head_desc_t* d, int32_t M, const void* x, const void* w, const float* w_scale,
+                float* logits, void* stream);
 
 /* Debug helper, NOT for the hot path: synchronises `stream`, copies the workspace's device status
    word to *status (MOE_OK, MOE_ERR_OFFSETS or MOE_ERR_TIMEOUT, accumulated over the calls since the

@@ -53,8 +53,10 @@ int check_desc(const moe_desc_t* d) {
     const bool f32 = d->act_format == MOE_FMT_F32;
     if (d->act_format != MOE_FMT_F32 && d->act_format != MOE_FMT_BF16) return MOE_ERR_FORMAT;
     if (f32 && d->weight_format != MOE_FMT_F32) return MOE_ERR_FORMAT;
-    if (!f32 && d->weight_format != MOE_FMT_BF16 && d->weight_format != MOE_FMT_MXFP4) return MOE_ERR_FORMAT;
-    const int mult = d->weight_format == MOE_FMT_MXFP4 ? 32 : 8;
+    if (!f32 && d->weight_format != MOE_FMT_BF16 && d->weight_format != MOE_FMT_MXFP4 &&
+        d->weight_format != MOE_FMT_FP8)
+        return MOE_ERR_FORMAT;
+    const int mult = d->weight_format == MOE_FMT_MXFP4 ? 32 : (d->weight_format == MOE_FMT_FP8 ? 128 : 8);
     // the kernel instances cover H <= 2560 and I, Is <= 768 (bf16, MXFP4), and the small binary32
     // layer H, I, Is <= 256
     const int maxH = f32 ? MOE_MAX_HIDDEN_F32 : MOE_MAX_HIDDEN, maxI = f32 ? MOE_MAX_INTER_F32 : MOE_MAX_INTER;
@@ -130,7 +132,7 @@ int fill_common(Params& p, const moe_desc_t* d, int32_t M, const void* x, const 
 
 int check_weights(const moe_desc_t* d, const moe_weights_t* w) {
     if (!w) return MOE_ERR_NULL;
-    const bool mx = d->weight_format == MOE_FMT_MXFP4;
+    const bool mx = d->weight_format == MOE_FMT_MXFP4 || d->weight_format == MOE_FMT_FP8;  // block scales
     const void* need[] = {w->gate, w->up, w->down};
     for (const void* q : need) {
         if (!q) return MOE_ERR_NULL;

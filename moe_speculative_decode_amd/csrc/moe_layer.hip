@@ -157,6 +157,12 @@ template <>
 struct Geo<MOE_FMT_MXFP4> {
     static constexpr int EPC = 32, LPR_G = 16, RL_G = 1, LPR_D = 8, RL_D = 1;
 };
+// FP8: 16 E4M3 codes per chunk, all in one 128-column scale block
+template <>
+struct Geo<MOE_FMT_FP8> {
+    static constexpr int EPC = 16, LPR_G = 64, RL_G = 1, LPR_D = 16, RL_D = 1;
+};
+constexpr int kFp8Block = 128;  // FP8 weights: one binary32 scale per 128 x 128 block
 template <int WF>
 __host__ __device__ constexpr int rt_gate() { return Geo<WF>::RL_G * (64 / Geo<WF>::LPR_G); }
 template <int WF>
@@ -165,12 +171,28 @@ __host__ __device__ constexpr int rt_down() { return Geo<WF>::RL_D * (64 / Geo<W
 // bytes of one row of K elements (MXFP4: the codes; the scales are K / 32 bytes more)
 template <int WF>
 __host__ __device__ constexpr int64_t row_bytes(int64_t K) {
-    return WF == MOE_FMT_F32 ? 4 * K : (WF == MOE_FMT_BF16 ? 2 * K : K / 2);
+    return WF == MOE_FMT_F32 ? 4 * K : (WF == MOE_FMT_BF16 ? 2 * K : (WF == MOE_FMT_FP8 ? K : K / 2));
+}
+
+// Block scales.  scale_mat: the scales of matrix e of a stack [E][rows][K]; scale_row: the scales
+// that apply to absolute row r of one matrix (MXFP4: its K / 32 E8M0 bytes; FP8: the K / 128
+// binary32 scales of its 128-row block).  Other formats have none.
+template <int WF>
+__device__ __forceinline__ const uint8_t* scale_mat(const uint8_t* s, int64_t e, int64_t rows, int64_t K) {
+    if constexpr (WF == MOE_FMT_MXFP4) return s + e * rows * (K / 32);
+    if constexpr (WF == MOE_FMT_FP8) return s + 4 * e * (rows / kFp8Block) * (K / kFp8Block);
+    return nullptr;
+}
+template <int WF>
+__device__ __forceinline__ const uint8_t* scale_row(const uint8_t* m, int64_t r, int64_t K) {
+    if constexpr (WF == MOE_FMT_MXFP4) return m + r * (K / 32);
+    if constexpr (WF == MOE_FMT_FP8) return m + 4 * (r / kFp8Block) * (K / kFp8Block);
+    return nullptr;
 }
 
 struct Chunk {
     u32x4 q;
-    uint32_t s;  // MXFP4 scale byte
+    uint32_t s;  // MXFP4: the block's E8M0 byte; FP8: the block's binary32 scale bits
 };
 
 // Makes the compiler wait for a chunk's load here, in straight-line code, and treat the value as
@@ -178,7 +200,7 @@ struct Chunk {
 // task's prefetch.
 template <int WF>
 __device__ __forceinline__ void settle(Chunk& r) {
-    if constexpr (WF == MOE_FMT_MXFP4)
+    if constexpr (WF == MOE_FMT_MXFP4 || WF == MOE_FMT_FP8)
         asm volatile("" : "+v"(r.q), "+v"(r.s));
     else
         asm volatile("" : "+v"(r.q));
@@ -198,12 +220,14 @@ template <int WF>
 __device__ __forceinline__ void ld_chunk(Chunk& r, const uint8_t* row, const uint8_t* srow, int c) {
     r.q = __builtin_nontemporal_load((const u32x4*)(row + 16 * c));
     if constexpr (WF == MOE_FMT_MXFP4) r.s = __builtin_nontemporal_load(srow + c);
+    if constexpr (WF == MOE_FMT_FP8) r.s = ((const uint32_t*)srow)[c / (kFp8Block / 16)];
 }
 // chunk c of a weight row held in LDS (the MXFP4 scales stay in global memory)
 template <int WF>
 __device__ __forceinline__ void ld_chunk_lds(Chunk& r, const LDS uint8_t* row, const uint8_t* srow, int c) {
     r.q = *(const LDS u32x4*)(row + 16 * c);
     if constexpr (WF == MOE_FMT_MXFP4) r.s = srow[c];
+    if constexpr (WF == MOE_FMT_FP8) r.s = ((const uint32_t*)srow)[c / (kFp8Block / 16)];
 }
 
 // Reinterprets a dword as two bf16.  Takes the dword by value: bit-casting a vector component
@@ -241,6 +265,23 @@ __device__ __forceinline__ void dot_x(const Chunk& r, const LDS char* xrow, int 
             acc[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1), as_bf16x2(x1), acc[1], false);
             acc[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2), as_bf16x2(x2), acc[2], false);
             acc[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3), as_bf16x2(x3), acc[3], false);
+        }
+    } else if constexpr (WF == MOE_FMT_FP8) {
+        // dword d of the codes holds elements 4d .. 4d+3 (byte b = element 4d+b), which are dwords
+        // 2d and 2d+1 of the 32 bytes of x; each E4M3 pair becomes a bfloat16 pair exactly (scale 1),
+        // and the chunk's partial sums take the block's scale once
+        const LDS u32x4* xp = (const LDS u32x4*)(xrow + 32 * c);
+        const u32x4 xa = xp[0], xb = xp[1];
+        const uint32_t xd[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+        const float sc = __uint_as_float(r.s);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t w = r.q[d];
+            float t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false),
+                                                      as_bf16x2(xd[2 * d]), 0.0f, false);
+            t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true),
+                                                as_bf16x2(xd[2 * d + 1]), t, false);
+            acc[d] = fmaf(t, sc, acc[d]);
         }
     } else {
         const f32x4 x = *(const LDS f32x4*)(xrow + 16 * c);
@@ -294,6 +335,25 @@ __device__ __forceinline__ void dot_a(const Chunk& r, const LDS char* arow, int 
             acc[1] = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(l1), acc[1], false);
             acc[2] = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(l2), acc[2], false);
             acc[3] = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(l3), acc[3], false);
+        }
+    } else if constexpr (WF == MOE_FMT_FP8) {
+        // as dot_x: chunk c covers elements 16c .. 16c+15, 32 bytes of each bfloat16 plane
+        const LDS u32x4* hp = (const LDS u32x4*)(arow + 32 * c);
+        const LDS u32x4* lp = (const LDS u32x4*)(arow + lo_off + 32 * c);
+        const u32x4 ha = hp[0], hb = hp[1], la = lp[0], lb = lp[1];
+        const uint32_t hd[8] = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+        const uint32_t ld[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
+        const float sc = __uint_as_float(r.s);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t w = r.q[d];
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+            float t = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(hd[2 * d]), 0.0f, false);
+            t = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(hd[2 * d + 1]), t, false);
+            t = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(ld[2 * d]), t, false);
+            t = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(ld[2 * d + 1]), t, false);
+            acc[d] = fmaf(t, sc, acc[d]);
         }
     } else {
         const f32x4 a = *(const LDS f32x4*)(arow + 16 * c);
@@ -1036,7 +1096,7 @@ __device__ __forceinline__ void router_rows(const Params& p, const LDS char* xs,
 struct GUTask {
     const uint8_t* g;
     const uint8_t* u;
-    const uint8_t* gs;  // MXFP4 scales of those rows
+    const uint8_t* gs;  // block scales of those rows (scale_row of the first row; FP8 tasks are one row)
     const uint8_t* us;
     uint32_t mask;      // the unit's tokens
     int slot;           // staging row of the task's first row
@@ -1057,6 +1117,7 @@ __device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, N
     const int H = p.H;
     const int nch = H / Geo<WF>::EPC;
     const int64_t rb = row_bytes<WF>(H), sb = H / 32;
+    static_assert(WF != MOE_FMT_FP8 || rt_gate<WF>() == 1, "an FP8 gate/up task is one row (one scale row)");
     int q = next(0);
     if (q < 0) return 0;
     Chunk ga[RL][NJ], ua[RL][NJ], gb[RL][NJ], ub[RL][NJ];
@@ -1342,18 +1403,19 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
     }
 }
 
-// Down rows [0, nrows) of one unit (row 0 at wbase / sbase, in LDS when FROM_LDS) with K inputs,
+// Down rows [0, nrows) of one unit (row 0 at wbase, in LDS when FROM_LDS; its block scales are those of
+// absolute row srow0 of the scale matrix smat) with K inputs,
 // for the unit's t tokens whose fp32 activations are at acts ([t][K], LDS).  Tasks of RT rows go
 // to the waves round robin, task 0 to the wave whose slot is 0.  `ready()` is called by every wave after its first loads are issued
 // and before any compute (it may contain workgroup barriers).  out(row, i, value) receives each
 // result in the row's last lane.
 template <int WF, int NJD, bool FROM_LDS, typename Ready, typename Out>
-__device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* sbase, int K, int nrows,
+__device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* smat, int64_t srow0, int K, int nrows,
                                          const LDS float* acts, int t, int wslot, Ready ready, Out out) {
     constexpr int LPR = Geo<WF>::LPR_D, RL = Geo<WF>::RL_D, RT = rt_down<WF>();
     const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
     const int nch = K / Geo<WF>::EPC;
-    const int64_t rb = row_bytes<WF>(K), sb = K / 32;
+    const int64_t rb = row_bytes<WF>(K);
     const int ntask = (nrows + RT - 1) / RT;
     int n = wslot;
     Chunk wa[RL][NJD], wb[RL][NJD];
@@ -1361,13 +1423,14 @@ __device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* sb
 #pragma unroll
         for (int rl = 0; rl < RL; ++rl) {
             const int64_t row = min(task * RT + gi * RL + rl, nrows - 1);
+            const uint8_t* srow = scale_row<WF>(smat, srow0 + row, K);
 #pragma unroll
             for (int j = 0; j < NJD; ++j) {
                 const int c = min(sl + LPR * j, nch - 1);
                 if constexpr (FROM_LDS)
-                    ld_chunk_lds<WF>(w[rl][j], (const LDS uint8_t*)wbase + row * rb, sbase + row * sb, c);
+                    ld_chunk_lds<WF>(w[rl][j], (const LDS uint8_t*)wbase + row * rb, srow, c);
                 else
-                    ld_chunk<WF>(w[rl][j], wbase + row * rb, sbase + row * sb, c);
+                    ld_chunk<WF>(w[rl][j], wbase + row * rb, srow, c);
             }
         }
     };
@@ -1420,7 +1483,8 @@ __device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* sb
 // One task of a flattened list of down rows: up to RT rows of one unit.
 struct DNTask {
     const uint8_t* w;       // the task's first weight row (an LDS address when lds)
-    const uint8_t* s;       // MXFP4 scales of that row (global memory)
+    const uint8_t* s;       // the scale matrix of the task's rows (scale_mat; global memory)
+    int srow;               // absolute row of the task's first row in that matrix
     const LDS float* acts;  // the unit's SwiGLU rows [t][astride] in LDS
     int lds;                // 1: the weights are in LDS
     int nrows;              // valid rows of the task
@@ -1443,17 +1507,18 @@ __device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Inf
     DNTask ta, tb;
     auto load = [&](Chunk(&w)[RL][NJD], const DNTask& t) {
         const int nch = t.K / Geo<WF>::EPC;
-        const int64_t rb = row_bytes<WF>(t.K), sb = t.K / 32;
+        const int64_t rb = row_bytes<WF>(t.K);
 #pragma unroll
         for (int rl = 0; rl < RL; ++rl) {
             const int64_t row = min(gi * RL + rl, t.nrows - 1);
+            const uint8_t* srow = scale_row<WF>(t.s, t.srow + row, t.K);
 #pragma unroll
             for (int j = 0; j < NJD; ++j) {
                 const int c = min(sl + LPR * j, nch - 1);
                 if (t.lds)
-                    ld_chunk_lds<WF>(w[rl][j], (const LDS uint8_t*)t.w + row * rb, t.s + row * sb, c);
+                    ld_chunk_lds<WF>(w[rl][j], (const LDS uint8_t*)t.w + row * rb, srow, c);
                 else
-                    ld_chunk<WF>(w[rl][j], t.w + row * rb, t.s + row * sb, c);
+                    ld_chunk<WF>(w[rl][j], t.w + row * rb, srow, c);
             }
         }
     };
@@ -1838,6 +1903,11 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     constexpr int XB = AF == MOE_FMT_F32 ? 4 : 2;
     constexpr int RTG = rt_gate<WF>();
     constexpr int RTD = rt_down<WF>();
+    // chunks per lane of a router row and of a token row (activation geometry, 64 lanes a row): NJ
+    // counts gate/up chunks, and an FP8 chunk holds twice the elements of a bf16 one
+    constexpr int NJR = WF == MOE_FMT_FP8 ? 2 * NJ : NJ;
+    static_assert(WF == MOE_FMT_FP8 || Geo<AF>::EPC * Geo<AF>::LPR_G == Geo<WF>::EPC * Geo<WF>::LPR_G,
+                  "router and gate/up rows cover the same elements per chunk column");
     LDS char* lds = (LDS char*)smem;
     LDS int* tab = (LDS int*)(lds + p.lds_tab);
     LDS char* xs = lds + p.lds_x;        // token rows; after phase C the staged SwiGLU rows
@@ -1869,12 +1939,12 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     if (!norm) async_rows_pitch((char*)xs, (const uint8_t*)p.x, M, H * XB, p.xpitch);
     const int e0 = (int)((int64_t)E * b / G), e1 = (int)((int64_t)E * (b + 1) / G);
     const int nrw = min(e1 - e0, kWaves);  // waves with router rows
-    Chunk rfirst[NJ];
+    Chunk rfirst[NJR];
     {
         const int e = e0 + wave_id(), lane = threadIdx.x & 63, nch = H / Geo<AF>::EPC;
         if (e < e1) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < NJR; ++j)
                 ld_chunk<AF>(rfirst[j], (const uint8_t*)p.wr + (int64_t)e * H * XB, nullptr, min(lane + 64 * j, nch - 1));
         }
     }
@@ -1896,7 +1966,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             async_dwords_to_lds((char*)sclw_sh, p.w.sh_down_s + (int64_t)h0 * (Is / 32), nown * (Is / 32));
     }
     if constexpr (AF == MOE_FMT_BF16)
-        if (norm) rms_norm_rows<NJ>(p, xs);  // the normed token rows replace x everywhere
+        if (norm) rms_norm_rows<NJR>(p, xs);  // the normed token rows replace x everywhere
     __builtin_amdgcn_s_waitcnt(0);  // token rows (and the slice's shared down rows) in LDS
     __syncthreads();
     MOE_TRACE(1);
@@ -1912,7 +1982,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         for (int l = threadIdx.x; l < kSetLines; l += kThreads) line(nxt, l)[0] = 0u;
     }
     // router rows (tagged logits: no arrival counter)
-    if (wave_id() < nrw) router_rows<AF, NJ>(p, xs, e0, e1, rfirst, call + 1u);
+    if (wave_id() < nrw) router_rows<AF, NJR>(p, xs, e0, e1, rfirst, call + 1u);
     MOE_TRACE(2);
     if (p.route_only && b != 0) {
         MOE_TRACE_FLUSH;
@@ -1960,8 +2030,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 const int64_t r0 = (int64_t)(qa + i) * RTG;
                 t.g = (const uint8_t*)p.w.sh_gate + r0 * row_bytes<WF>(H);
                 t.u = (const uint8_t*)p.w.sh_up + r0 * row_bytes<WF>(H);
-                t.gs = WF == MOE_FMT_MXFP4 ? p.w.sh_gate_s + r0 * (H / 32) : nullptr;
-                t.us = WF == MOE_FMT_MXFP4 ? p.w.sh_up_s + r0 * (H / 32) : nullptr;
+                t.gs = scale_row<WF>(p.w.sh_gate_s, r0, H);
+                t.us = scale_row<WF>(p.w.sh_up_s, r0, H);
                 t.mask = (1u << M) - 1u;
                 t.slot = (int)r0;
             },
@@ -2140,8 +2210,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     const int64_t r0 = f - (int64_t)u * I;
                     t.g = (const uint8_t*)p.w.gate + (e * I + r0) * rb;
                     t.u = (const uint8_t*)p.w.up + (e * I + r0) * rb;
-                    t.gs = WF == MOE_FMT_MXFP4 ? p.w.gate_s + (e * I + r0) * (H / 32) : nullptr;
-                    t.us = WF == MOE_FMT_MXFP4 ? p.w.up_s + (e * I + r0) * (H / 32) : nullptr;
+                    t.gs = scale_row<WF>(scale_mat<WF>(p.w.gate_s, e, I, H), r0, H);
+                    t.us = scale_row<WF>(scale_mat<WF>(p.w.up_s, e, I, H), r0, H);
                     t.mask = uni(s_mask[u]);
                     t.slot = (w * cap + s) * RTG;
                 },
@@ -2181,7 +2251,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     //      on the workgroups that finish gate/up last, is slower) ----
     //      (slice mode: in its down phase, before the wait for the routed units) ----
     auto shared_down = [&]() {
-        if constexpr (WF != MOE_FMT_F32 && NJD <= 3) {
+        if constexpr ((WF == MOE_FMT_BF16 || WF == MOE_FMT_MXFP4) && NJD <= 3) {
             if (has_sh && nown > 0 && mf_sh && !SLICE) {
                 wait_geq(line(set, kLineShared), (uint32_t)Is, fault);
                 const int apitch = 2 * p.act_stride + 16;  // rows 4 banks apart: no conflicts among the B columns
@@ -2205,8 +2275,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             wait_geq(line(set, kLineShared), (uint32_t)Is, fault);
             stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
             __syncthreads();
-            const uint8_t* dsb = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)h0 * (Is / 32) : nullptr;
-            down_run<WF, NJD, true>((const uint8_t*)shw, dsb, Is, nown, (const LDS float*)xs, M, wave_id(), []() {},
+            down_run<WF, NJD, true>((const uint8_t*)shw, p.w.sh_down_s, h0, Is, nown, (const LDS float*)xs, M, wave_id(),
+                                    []() {},
                                     [&](int row, int i, float v) { ysh[i * nown + row] = v; });
             __syncthreads();
         }
@@ -2240,14 +2310,16 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     t.lds = pidx >= ng ? 1 : 0;
                     t.w = t.lds ? (const uint8_t*)(dnw + ((int64_t)u * nown + r0) * rbI)
                                 : (const uint8_t*)p.w.down + (e * H + h0 + r0) * rbI;
-                    t.s = WF == MOE_FMT_MXFP4 ? p.w.down_s + (e * H + h0 + r0) * (I / 32) : nullptr;
+                    t.s = scale_mat<WF>(p.w.down_s, e, H, I);
+                    t.srow = h0 + r0;
                 } else {
                     t.prow = NP;
                     t.t = M;
                     t.K = Is;
                     t.lds = 1;
                     t.w = (const uint8_t*)(shw + (int64_t)r0 * rbIs);
-                    t.s = WF == MOE_FMT_MXFP4 ? p.w.sh_down_s + (int64_t)(h0 + r0) * (Is / 32) : nullptr;
+                    t.s = p.w.sh_down_s;
+                    t.srow = h0 + r0;
                 }
                 t.acts = (const LDS float*)xs + (int64_t)t.prow * astride;
             };
@@ -2259,7 +2331,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 __syncthreads();
                 MOE_TRACE(10);
             };
-            if constexpr (WF != MOE_FMT_F32 && NJD <= 3) {
+            if constexpr ((WF == MOE_FMT_BF16 || WF == MOE_FMT_MXFP4) && NJD <= 3) {
                 if (mf_slice) {
                     // matrix-core path: SwiGLU rows staged as bfloat16, one wave per unit
                     const int apitch = 2 * astride + 16;  // rows 4 banks apart: no conflicts among the B columns
@@ -2420,7 +2492,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 t.lds = r0 - ha < pre_rows[sg] ? 1 : 0;
                 t.w = t.lds ? (const uint8_t*)(dnw + pre_off[sg] + (int64_t)(r0 - ha) * rbI)
                             : (const uint8_t*)p.w.down + (e * H + r0) * rbI;
-                t.s = WF == MOE_FMT_MXFP4 ? p.w.down_s + (e * H + r0) * (I / 32) : nullptr;
+                t.s = scale_mat<WF>(p.w.down_s, e, H, I);
+                t.srow = r0;
                 t.acts = (const LDS float*)xs + aoff[sg];
             };
             auto ready = [&]() {
@@ -2472,15 +2545,15 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 // part from the LDS window: rows [pa, min(pb, ha + npre))
                 const int la = pa, lb = min(pb, ha + npre);
                 if (lb > la) {
-                    const uint8_t* dsb = WF == MOE_FMT_MXFP4 ? p.w.down_s + (e * H + la) * (I / 32) : nullptr;
-                    down_run<WF, NJD, true>((const uint8_t*)(dnw + pre_off[seg] + (int64_t)(la - ha) * rbI), dsb, I,
+                    down_run<WF, NJD, true>((const uint8_t*)(dnw + pre_off[seg] + (int64_t)(la - ha) * rbI),
+                                            scale_mat<WF>(p.w.down_s, e, H, I), la, I,
                                             lb - la, (const LDS float*)xs, t, wave_id(), ready,
                                             [&](int row, int i, float v) { out(row + la - pa, i, v); });
                 }
                 const int ga = max(pa, ha + npre), gb = pb;
                 if (gb > ga) {
-                    const uint8_t* dsb = WF == MOE_FMT_MXFP4 ? p.w.down_s + (e * H + ga) * (I / 32) : nullptr;
-                    down_run<WF, NJD, false>((const uint8_t*)p.w.down + (e * H + ga) * rbI, dsb, I, gb - ga,
+                    down_run<WF, NJD, false>((const uint8_t*)p.w.down + (e * H + ga) * rbI, scale_mat<WF>(p.w.down_s, e, H, I),
+                                             ga, I, gb - ga,
                                              (const LDS float*)xs, t, wave_id(), ready,
                                              [&](int row, int i, float v) { out(row + ga - pa, i, v); });
                 }
@@ -2570,7 +2643,8 @@ hipError_t plan_t(Params& p, int G) {
     constexpr int XB = AF == MOE_FMT_F32 ? 4 : 2;
     int nj, njd;
     chunks<WF>(p, &nj, &njd);
-    const bool fits = (nj <= 1 && njd <= 1) || (WF != MOE_FMT_F32 && nj <= 5 && njd <= 3);
+    const bool fits = (nj <= 1 && njd <= 1) || (WF == MOE_FMT_FP8 ? nj <= 3 && njd <= 3
+                                                                 : WF != MOE_FMT_F32 && nj <= 5 && njd <= 3);
     if (!fits) return hipErrorInvalidValue;  // no kernel instance for this shape
     const int M = p.M, H = p.H;
     const int64_t NP = (int64_t)p.k * M;
@@ -2587,7 +2661,7 @@ hipError_t plan_t(Params& p, int G) {
     p.route_delegate = (!p.route_only && M >= 3 && M <= G) ? 1 : 0;
     // slice mode on the matrix cores (bf16 and MXFP4 weights, up to 16 rows per workgroup, K <= 768):
     // bfloat16 SwiGLU rows, swizzled weight windows
-    p.sh_mfma = (WF != MOE_FMT_F32 && njd <= 3 && nown <= 16) ? 1 : 0;
+    p.sh_mfma = ((WF == MOE_FMT_BF16 || WF == MOE_FMT_MXFP4) && njd <= 3 && nown <= 16) ? 1 : 0;
     p.slice_mfma = (p.slice_mode && p.sh_mfma) ? 1 : 0;
     // staging area: routing scratch; routed SwiGLU results of one workgroup's tasks; down partials
     // (slice mode: [NP][nown]; unit-major: any size, larger means fewer passes)
@@ -2602,7 +2676,7 @@ hipError_t plan_t(Params& p, int G) {
     // whole-layer time: bf16 over 0, 1, 2, 3, 4 and 6 at 6 and 16 tokens (3 is fastest at both);
     // MXFP4 over 1, 3, 6, 9 and 14 at 16 tokens (6 is fastest: the vector path decodes every
     // code once per token)
-    p.cost_dn = WF == MOE_FMT_MXFP4 ? 6 : (WF == MOE_FMT_BF16 ? 3 : 0);
+    p.cost_dn = WF == MOE_FMT_MXFP4 ? 6 : (WF == MOE_FMT_BF16 ? 3 : (WF == MOE_FMT_FP8 ? 6 : 0));
     // gate/up staging: MXFP4 tiles of 8 rows dealt round robin (at most ceil(T / G) per workgroup);
     // otherwise per wave the static share plus up to twice the average dynamic share (the split
     // the kernel makes from the actual number of units, bounded here by its maximum)
@@ -2693,7 +2767,9 @@ hipError_t launch_fmt(const Params& p, int G, int dev, hipStream_t s) {
     int nj, njd;
     chunks<WF>(p, &nj, &njd);
     if (nj <= 1 && njd <= 1) return launch_t<AF, WF, 1, 1>(p, G, dev, s);
-    if constexpr (WF != MOE_FMT_F32)
+    if constexpr (WF == MOE_FMT_FP8)
+        if (nj <= 3 && njd <= 3) return launch_t<AF, WF, 3, 3>(p, G, dev, s);
+    if constexpr (WF == MOE_FMT_BF16 || WF == MOE_FMT_MXFP4)
         if (nj <= 5 && njd <= 3) return launch_t<AF, WF, 5, 3>(p, G, dev, s);
     return hipErrorInvalidValue;
 }
@@ -2710,6 +2786,7 @@ hipError_t plan_layer(Params& p, int G) {
     if (G < 1 || G > kMaxGrid) return hipErrorInvalidValue;
     if (p.act_fmt == MOE_FMT_F32) return plan_t<MOE_FMT_F32, MOE_FMT_F32>(p, G);
     if (p.w_fmt == MOE_FMT_BF16) return plan_t<MOE_FMT_BF16, MOE_FMT_BF16>(p, G);
+    if (p.w_fmt == MOE_FMT_FP8) return plan_t<MOE_FMT_BF16, MOE_FMT_FP8>(p, G);
     return plan_t<MOE_FMT_BF16, MOE_FMT_MXFP4>(p, G);
 }
 
@@ -2718,6 +2795,7 @@ hipError_t launch_layer(const Params& p, int G, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     if (p.act_fmt == MOE_FMT_F32) return launch_fmt<MOE_FMT_F32, MOE_FMT_F32>(p, G, dev, s);
     if (p.w_fmt == MOE_FMT_BF16) return launch_fmt<MOE_FMT_BF16, MOE_FMT_BF16>(p, G, dev, s);
+    if (p.w_fmt == MOE_FMT_FP8) return launch_fmt<MOE_FMT_BF16, MOE_FMT_FP8>(p, G, dev, s);
     return launch_fmt<MOE_FMT_BF16, MOE_FMT_MXFP4>(p, G, dev, s);
 }
 

@@ -16,8 +16,10 @@ from oracle import oracle as O
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 # max-abs(y_gpu - y_oracle) / rms(y_oracle) bars: bf16 and MXFP4 from the layer's accuracy target;
-# fp32 derived from fp32 accumulation over K <= 4096 terms (relative error well below 1e-5)
-TOL = {synth.F32: 1e-4, synth.BF16: 2e-2, synth.MXFP4: 5e-2}
+# FP8 weights take the bf16 bar (the oracle dequantises the same codes exactly, so only the bf16
+# rounding of the SwiGLU rows and of y remains, as for bf16 weights); fp32 derived from fp32
+# accumulation over K <= 4096 terms (relative error well below 1e-5)
+TOL = {synth.F32: 1e-4, synth.BF16: 2e-2, synth.MXFP4: 5e-2, synth.FP8: 2e-2}
 W_TOL = 1e-5  # routing weights, absolute
 
 

@@ -15,7 +15,7 @@ from tests import _gpu_common as G
 
 pytestmark = pytest.mark.gpu
 
-BF16, MXFP4, F32 = synth.BF16, synth.MXFP4, synth.F32
+BF16, MXFP4, F32, FP8 = synth.BF16, synth.MXFP4, synth.F32, synth.FP8
 
 
 def small(name, fmt=BF16, H=512, E=64, k=4, I=192, Is=128, lens=(5,), recipe="shared_base", norm=False, bias=False):
@@ -58,6 +58,16 @@ SMALL = [
     small("router_bias_k16", E=128, k=16, lens=(5,), bias=True),
     small("router_nb_mxfp4_m6", MXFP4, lens=(6,), norm=True, bias=True),
     small("router_nb_tail", H=520, I=200, Is=72, lens=(7,), norm=True, bias=True),
+    # FP8 (E4M3, one scale per 128 x 128 block): slice mode, unit-major, ragged chunk tails (H = 640:
+    # 40 chunks a row), down rows of several 128-row blocks per unit, and the router prologue
+    small("fp8_m1", FP8, I=256, lens=(1,), recipe="iid"),
+    small("fp8_m6", FP8, I=256, lens=(6,)),
+    small("fp8_m16", FP8, H=640, I=384, Is=256, lens=(9, 7)),
+    small("fp8_k8_m16", FP8, E=256, k=8, I=768, Is=128, lens=(16,)),
+    small("fp8_router_nb_m6", FP8, I=256, lens=(6,), norm=True, bias=True),
+    # router rows span twice the chunks of FP8 gate/up rows (bf16 activations)
+    small("fp8_h1024", FP8, H=1024, I=256, lens=(3,)),
+    small("fp8_h2560", FP8, H=2560, E=64, k=4, I=256, Is=128, lens=(2,), norm=True),
 ]
 
 
@@ -92,7 +102,8 @@ def test_tiny_f32_config():
 
 @pytest.mark.parametrize("name", ["ling_bf16_m1", "ling_bf16_m6", "ling_bf16_m16_ragged", "ling_mxfp4_m1",
                                   "ling_mxfp4_m6", "ling_mxfp4_m16_ragged", "ling_bf16_m1_router",
-                                  "ling_bf16_m6_router", "ling_bf16_m16_ragged_router", "ling_mxfp4_m6_router"])
+                                  "ling_bf16_m6_router", "ling_bf16_m16_ragged_router", "ling_mxfp4_m6_router",
+                                  "ling_fp8_m1", "ling_fp8_m6", "ling_fp8_m16_ragged"])
 def test_ling_configs(name):
     cfg = synth.CONFIGS[name]
     G.log("ling", name, "generating layer")
