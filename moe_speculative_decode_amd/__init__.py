@@ -14,7 +14,7 @@ from typing import Optional
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_decode.so")
 
-MOE_FMT_F32, MOE_FMT_BF16, MOE_FMT_MXFP4 = 0, 1, 2
+MOE_FMT_F32, MOE_FMT_BF16, MOE_FMT_MXFP4, MOE_FMT_FP8 = 0, 1, 2, 3
 MOE_OK = 0
 MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_FORMAT, MOE_ERR_WORKSPACE = -1, -2, -3, -4
 MOE_ERR_OFFSETS, MOE_ERR_HIP, MOE_ERR_ALIGN, MOE_ERR_TIMEOUT = -5, -6, -7, -8
@@ -23,7 +23,7 @@ MOE_NOALLOC_SCRATCH_BYTES = 2138112
 MOE_MAX_TOKENS, MOE_MAX_EXPERTS, MOE_MAX_TOPK = 16, 512, 16
 
 EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_decode_forward", "moe_decode_forward_noalloc",
-            "moe_read_status", "moe_status_string")
+            "moe_lm_head", "moe_read_status", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -41,6 +41,10 @@ class moe_desc_t(ctypes.Structure):
                 ("act_format", ctypes.c_int32), ("weight_format", ctypes.c_int32),
                 ("router_flags", ctypes.c_int32), ("norm_eps", ctypes.c_float),
                 ("norm_weight", ctypes.c_void_p), ("router_bias", ctypes.c_void_p)]
+
+
+class moe_lm_head_desc_t(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("vocab", ctypes.c_int32), ("weight_format", ctypes.c_int32)]
 
 
 class moe_weights_t(ctypes.Structure):
@@ -77,6 +81,8 @@ def lib():
         L.moe_decode_forward_noalloc.restype = ctypes.c_int
         L.moe_decode_forward_noalloc.argtypes = [ctypes.POINTER(moe_desc_t), i32, vp, vp, ctypes.POINTER(moe_weights_t),
                                                  vp, i32, vp, vp, vp, ctypes.POINTER(moe_dispatch_t), vp]
+        L.moe_lm_head.restype = ctypes.c_int
+        L.moe_lm_head.argtypes = [ctypes.POINTER(moe_lm_head_desc_t), i32, vp, vp, vp, vp, vp]
         L.moe_read_status.restype = ctypes.c_int
         L.moe_read_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -138,6 +144,11 @@ def moe_decode_forward_noalloc(desc, M, x, w_router, weights: moe_weights_t, y, 
                                           _ptr(req_offsets), R, _ptr(y), _ptr(topk_ids), _ptr(topk_w),
                                           ctypes.byref(disp) if disp is not None else None, _stream(stream))
     _check(st, "moe_decode_forward_noalloc")
+
+
+def moe_lm_head(desc: moe_lm_head_desc_t, M, x, w, logits, w_scale=None, stream=None):
+    st = lib().moe_lm_head(ctypes.byref(desc), M, _ptr(x), _ptr(w), _ptr(w_scale), _ptr(logits), _stream(stream))
+    _check(st, "moe_lm_head")
 
 
 def moe_read_status(ws, stream=None) -> int:

@@ -8,7 +8,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_decode.so")
-SOURCES = ["moe_layer.hip", "moe_api.hip"]
+SOURCES = ["moe_layer.hip", "moe_api.hip", "lm_head.hip"]
 BENCH_LIB = os.path.join(PKG, "libmoe_bench.so")
 BENCH_SOURCES = ["bench_stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -137,6 +137,24 @@ def test_noalloc_rejects_on_host():
                                         None) == mdl.MOE_ERR_NULL
 
 
+def test_lm_head_rejects_on_host():
+    L = mdl.lib()
+
+    def call(H=2560, V=157184, fmt=mdl.MOE_FMT_BF16, M=1, x=FAKE, w=FAKE, sc=None, out=FAKE):
+        d = mdl.moe_lm_head_desc_t(H, V, fmt)
+        return L.moe_lm_head(ctypes.byref(d), M, x, w, sc, out, None)
+    assert call(M=0) == mdl.MOE_ERR_SHAPE
+    assert call(M=17) == mdl.MOE_ERR_SHAPE
+    assert call(H=2568) == mdl.MOE_ERR_SHAPE
+    assert call(H=520, fmt=mdl.MOE_FMT_FP8, sc=FAKE) == mdl.MOE_ERR_SHAPE  # FP8 rows of whole 16-code chunks
+    assert call(V=0) == mdl.MOE_ERR_SHAPE
+    assert call(fmt=mdl.MOE_FMT_MXFP4) == mdl.MOE_ERR_FORMAT
+    assert call(fmt=mdl.MOE_FMT_FP8) == mdl.MOE_ERR_NULL  # no scales
+    assert call(x=None) == mdl.MOE_ERR_NULL
+    assert call(out=FAKE + 4) == mdl.MOE_ERR_ALIGN
+    assert L.moe_lm_head(None, 1, FAKE, FAKE, None, FAKE, None) == mdl.MOE_ERR_NULL
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert mdl.moe_status_string(s) and mdl.moe_status_string(s) != "unknown status"
