@@ -17,10 +17,12 @@ keep the counter pass separate from the timing):
     the same way: what one launch can read from HBM in that time on this GPU.
 
 Prints ONE JSON line.  The headline is the first workload (bf16, one token).  `workloads` holds
-every Ling configuration with its unique-expert count U, algorithmic bytes B_alg (router + each
-unique routed expert once + the shared expert + x in, y out + routing outputs), the roofline
-fraction B_alg / t / 8 TB/s and the HBM traffic the committed counter pass measured on the
-current kernel (null otherwise).  The CPU baseline is the fp64 oracle on the host's cores.
+every Ling configuration (bf16, MXFP4 and FP8 weights at M = 1, 6, 16) with its unique-expert count
+U, algorithmic bytes B_alg (router + each unique routed expert once + the shared expert + x in,
+y out + routing outputs), the roofline fraction B_alg / t / 8 TB/s and the HBM traffic the
+committed counter pass measured on the current kernel (null otherwise), and the LM head GEMV
+(157,184 x 2,560, bf16 and FP8 weights, M = 1 and 6) measured the same way.  The CPU baseline is
+the fp64 oracle on the host's cores.
 """
 import argparse
 import ctypes
@@ -251,6 +253,72 @@ def measure_format(torch, mdl, dev, synth, names, args, stream_ref):
     return results
 
 
+LM_HEAD_WORKLOADS = ["lm_head_bf16_m1", "lm_head_fp8_m1", "lm_head_bf16_m6", "lm_head_fp8_m6"]
+
+
+def lm_head_bytes(cfg) -> int:
+    """Bytes the LM head must move once: the weight (FP8: codes and one scale per row), the token
+    rows in and the fp32 logits out."""
+    from moe_speculative_decode_amd import synth
+    w = cfg.vocab * cfg.hidden * (1 if cfg.weight_fmt == synth.FP8 else 2)
+    if cfg.weight_fmt == synth.FP8:
+        w += 4 * cfg.vocab
+    return w + 2 * cfg.M * cfg.hidden + 4 * cfg.M * cfg.vocab
+
+
+def measure_lm_heads(torch, mdl, dev, synth, names, args, stream_ref):
+    """The LM head GEMV (moe_lm_head) per workload, timed like the layer: cold copies of the weight
+    rotated in a graph, hot, eager, and the streaming-read ceiling of the same bytes."""
+    results = []
+    cache = {}
+    for name in names:
+        cfg = synth.LM_HEADS[name]
+        key = (cfg.weight_fmt, cfg.hidden, cfg.vocab, cfg.seed)
+        if key not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            t0 = time.time()
+            w, sc = synth.lm_head_weights(cfg)
+            print("[bench] %s weight generated in %.1fs" % (name, time.time() - t0), file=sys.stderr, flush=True)
+            B1 = lm_head_bytes(cfg)
+            L = args.copies or max(1, -(-COLD_BYTES // B1))
+            wd = [dev.to_device(w)]
+            wd += [wd[0].clone() for _ in range(L - 1)]
+            scd = None if sc is None else [dev.to_device(sc)]
+            if scd is not None:
+                scd += [scd[0].clone() for _ in range(L - 1)]
+            cache[key] = (wd, scd, L)
+            del w, sc
+        wd, scd, L = cache[key]
+        x = dev.to_device(synth.lm_head_hidden(cfg, 1))
+        out = torch.empty((cfg.M, cfg.vocab), dtype=torch.float32, device="cuda")
+        desc = mdl.moe_lm_head_desc_t(cfg.hidden, cfg.vocab, cfg.weight_fmt)
+        B = lm_head_bytes(cfg)
+
+        def step(i, stream, rot=L):
+            j = i % rot
+            mdl.moe_lm_head(desc, cfg.M, x, wd[j], out, w_scale=None if scd is None else scd[j], stream=stream)
+
+        K, W, T = args.steps, args.warmup, args.trials
+        cold = graph_times(torch, step, K, T, W)
+        hot = graph_times(torch, lambda i, st: step(i, st, 1), K, T, W)
+        t = pct(cold, 0.5)
+        achieved = B / (t * 1e-6) / 1e9
+        r = {"workload": name, "M": cfg.M, "weights": synth.FORMAT_NAMES[cfg.weight_fmt], "vocab": cfg.vocab,
+             "hidden": cfg.hidden, "algorithmic_bytes": B, "cold_copies": L, "us_cold": summary(cold),
+             "us_hot": summary(hot), "tokens_per_s": round(cfg.M / (t * 1e-6), 1), "hbm_GBps": round(achieved, 1),
+             "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_from_profiles(name)}
+        if stream_ref is not None:
+            r["stream_ceiling"] = stream_ceiling(torch, stream_ref, B, K, T, W)
+            r["frac_of_stream"] = round(r["stream_ceiling"]["us_median"] / t, 4)
+        print("[bench] %s cold %.2f us (p10 %.2f, p90 %.2f) hot %.2f us  frac %.4f" %
+              (name, t, pct(cold, 0.1), pct(cold, 0.9), pct(hot, 0.5), r["frac"]), file=sys.stderr, flush=True)
+        results.append(r)
+    cache.clear()
+    torch.cuda.empty_cache()
+    return results
+
+
 def stream_ceiling(torch, ref, nbytes: int, K: int, T: int, W: int):
     """A plain streaming read of nbytes, cold (rotating over enough distinct buffers), graph-replayed
     like the layer."""
@@ -276,7 +344,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20, help="steps per graph replay (K)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--trials", type=int, default=20, help="graph replays timed per workload (>= 10)")
-    ap.add_argument("--config", default=None, help="measure only this workload")
+    ap.add_argument("--config", default=None, help="measure only these workloads (comma-separated names)")
     ap.add_argument("--copies", type=int, default=0, help="layer copies rotated (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=6.0, help="seconds per CPU-baseline timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -306,14 +374,20 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "dispatches": 5}))
         return
 
-    names = [args.config] if args.config else WORKLOADS
+    names = args.config.split(",") if args.config else WORKLOADS + LM_HEAD_WORKLOADS
+    layer_names = [n for n in names if n in synth.CONFIGS]
+    head_names = [n for n in names if n in synth.LM_HEADS]
     stream_ref = None if args.no_stream else StreamRef()
     by_fmt = {}
-    for n in names:
+    for n in layer_names:
         by_fmt.setdefault(synth.CONFIGS[n].weight_fmt, []).append(n)
     results = []
     for fmt, group in by_fmt.items():
         results += measure_format(torch, mdl, dev, synth, group, args, stream_ref)
+    lm_heads = measure_lm_heads(torch, mdl, dev, synth, head_names, args, stream_ref) if head_names else []
+    if not results:  # an LM-head run only
+        print(json.dumps({"metric": "LM head us/step", "workloads": lm_heads}), flush=True)
+        return
     head = next((r for r in results if r[0]["workload"] == HEADLINE), results[0])
     hr, hcfg, hlayer, hx = head
     t = hr["us_cold"]["median"]
@@ -333,7 +407,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": hr["hbm_GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": hr["frac"], "traffic": hr["traffic"]},
         "stream_ceiling": hr.get("stream_ceiling"),
-        "workloads": [r[0] for r in results],
+        "workloads": [r[0] for r in results] + lm_heads,
     }
     if not args.no_cpu_baseline:
         import numpy as np
