@@ -163,6 +163,7 @@ struct Geo<MOE_FMT_FP8> {
     static constexpr int EPC = 16, LPR_G = 64, RL_G = 1, LPR_D = 16, RL_D = 1;
 };
 constexpr int kFp8Block = 128;  // FP8 weights: one binary32 scale per 128 x 128 block
+constexpr int kFp8Stage = 10;   // FP8 matrix-core gate/up: chunk groups (64 elements each) per stage
 template <int WF>
 __host__ __device__ constexpr int rt_gate() { return Geo<WF>::RL_G * (64 / Geo<WF>::LPR_G); }
 template <int WF>
@@ -946,7 +947,32 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
     }
     __syncthreads();
     MOE_TRACE(13);
-    if (wave == 0) {
+    if (wave == 0 && M == 1) {
+        // one token: the units are its k experts in ascending id order and pair j is row rank(j);
+        // ties (only possible if a cut-short selection repeated an id) go by slot, so every unit
+        // slot is written once
+        const int id = lane < k ? sid[lane] : 0x7FFFFFFF;
+        int rank = 0;
+        for (int j = 0; j < k; ++j) {
+            const int o = __builtin_amdgcn_readlane(id, j);
+            rank += (o < id || (o == id && j < lane)) ? 1 : 0;
+        }
+        if (lane < k) {
+            s_mask[rank] = 1u;
+            s_off[rank] = rank;
+            s_exp[rank] = min(max(id, 0), E - 1);
+            s_pair[lane] = rank;
+            s_roww[rank] = sw[lane];
+        }
+        if (lane == 0) {
+            s_mask[k] = has_sh ? 1u : 0u;
+            s_off[k] = k;
+            s_off[k + 1] = k + (has_sh ? 1 : 0);
+            s_exp[k] = E;
+            tab[kTabMisc] = k;
+            s_roww[k] = 1.0f;
+        }
+    } else if (wave == 0) {
         // token bitmask of every expert (one wave: its LDS operations complete in order)
         for (int e = lane; e < kMaxExperts; e += 64) tokmask[e] = 0u;
         for (int q = lane; q < NP; q += 64) atomicOr((uint32_t*)&tokmask[sid[q]], 1u << (q / k));
@@ -1038,6 +1064,10 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
             if (!s_bad && p.disp.req_unique) {
                 for (int r = 0; r < p.R; ++r) {
                     const int a = p.req_off[r], b = p.req_off[r + 1];
+                    if (M == 1) {  // no token bitmasks: the one token's U experts, in the request holding it
+                        if (threadIdx.x == 0 && a == 0 && b >= 1) s_req_unique[r] = U;
+                        continue;
+                    }
                     const uint32_t rm = ((1u << b) - 1u) & ~((1u << a) - 1u);
                     for (int i = threadIdx.x; i < E; i += kThreads)
                         if (tokmask[i] & rm) atomicAdd(&s_req_unique[r], 1);
@@ -1371,6 +1401,161 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
             }
             acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             acc1 = acc0;
+        }
+    };
+    if (nsteps > 0) {
+        Stage sa, sb2;
+        load(sa, 0);
+        int t = 0;
+        while (true) {
+            load(sb2, t + 1);
+            compute(sa, t);
+            if (++t >= nsteps) break;
+            load(sa, t + 1);
+            compute(sb2, t);
+            if (++t >= nsteps) break;
+        }
+    }
+    if (ks) {  // sum each tile's stages in stage order, then silu(g) * v for the unit's tokens
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < nloc * 8 * M; idx += kThreads) {
+            const int i = idx / (8 * M), rem = idx - i * 8 * M;
+            const int jr = rem / M, n = rem - jr * M;
+            float g = 0.0f, v = 0.0f;
+            for (int sg = 0; sg < nstage; ++sg) {
+                const LDS float* pp = part + (int64_t)(i * nstage + sg) * 4 * M * 4;
+                g += pp[((jr >> 2) * M + n) * 4 + (jr & 3)];
+                v += pp[((2 + (jr >> 2)) * M + n) * 4 + (jr & 3)];
+            }
+            const uint32_t mk = row_mask(tile_row(i) + jr);
+            if ((mk >> n) & 1u) cst[(tile_slot(i) + jr) * M + __popc(mk & ((1u << n) - 1u))] = silu_mul(g, v);
+        }
+    }
+}
+
+// Routed (SH: shared) gate/up rows on the matrix cores for FP8 weights: the tiles, (tile, stage)
+// items, partial sums and outputs of gateup_mfma_mx.  Lane (r, kq) owns the 16-byte chunks 4q + kq
+// of its row (16 E4M3 codes: elements 16 (4q + kq) .. + 15), decoded exactly to bfloat16 pairs (scale
+// 1) and fed to two products: product h of group q takes elements 16 (4q + kq) + 8h .. + 7, and B
+// lane (n, kq) holds the same elements of token n's row.  Groups 2c and 2c + 1 lie in the 128-column
+// block c of the row, so their four products go to a fresh accumulator that joins the running sum
+// times the block's scale for the lane's D rows (rows 0..7: the gate rows' row block, 8..15: the up
+// rows'; the 8 rows of a tile lie in one 128-row block).  Every wave of the workgroup must call this.
+template <int NQ, bool SH = false>
+__device__ __forceinline__ void gateup_mfma_f8(const Params& p, const LDS char* xs, int nloc,
+                                               const LDS uint32_t* s_mask, const LDS int* s_exp, LDS float* cst,
+                                               LDS float* part) {
+    static_assert(NQ % 2 == 0, "stages of whole 128-column blocks");
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int r = lane & 15, kq = lane >> 4;
+    const int H = p.H, I = p.I, M = p.M, G = gridDim.x, b = blockIdx.x;
+    const int nch = H / 16, ngrp = nch / 4, nstage = (ngrp + NQ - 1) / NQ, nsb = H / kFp8Block;
+    const int64_t rb = H;
+    const int RI = SH ? p.Is : I;  // rows of one matrix
+    const bool ks = part != nullptr;
+    const int nsteps = ks ? n_strided(nloc * nstage, wave, kWaves) : n_strided(nloc, wave, kWaves) * nstage;
+    const uint8_t* mat = SH ? (r < 8 ? (const uint8_t*)p.w.sh_gate : (const uint8_t*)p.w.sh_up)
+                            : (r < 8 ? (const uint8_t*)p.w.gate : (const uint8_t*)p.w.up);
+    // the scales of this lane's D rows: gate for kq < 2 (rows 4 kq .. 4 kq + 3 < 8), up otherwise
+    const uint8_t* dsc = SH ? (kq < 2 ? p.w.sh_gate_s : p.w.sh_up_s) : (kq < 2 ? p.w.gate_s : p.w.up_s);
+    auto row_mask = [&](int64_t f) -> uint32_t { return SH ? (1u << M) - 1u : s_mask[(int)(f / I)]; };
+    const LDS char* xrow = xs + (int64_t)min(r, M - 1) * p.xpitch;  // columns past M are dropped
+    auto tile_of = [&](int t, int& i, int& sg) {
+        if (ks) {
+            const int kk = wave + kWaves * t;
+            i = kk / nstage;
+            sg = kk - i * nstage;
+        } else {
+            i = wave + kWaves * (t / nstage);
+            sg = t - (t / nstage) * nstage;
+        }
+    };
+    auto tile_row = [&](int i) { return (int64_t)(b + i * G) * 8; };
+    auto tile_slot = [&](int i) { return i * 8; };
+    // expert and row within it of flat row f
+    auto locate = [&](int64_t f, int64_t& e, int64_t& rl) {
+        if constexpr (SH) {
+            e = 0;
+            rl = f;
+        } else {
+            const int u = (int)(f / I);
+            e = s_exp[u];
+            rl = f - (int64_t)u * I;
+        }
+    };
+    struct Stage {
+        u32x4 c[NQ];
+        float s[NQ / 2];
+    };
+    // t == nsteps: the stand-in prefetch after the last stage (static loads in flight): the first
+    // chunk of the last tile's first row in every lane, one cache line
+    auto load = [&](Stage& st, int t) {
+        const bool dummy = t >= nsteps;
+        t = min(t, nsteps - 1);
+        int j, sg;
+        tile_of(t, j, sg);
+        const int64_t f0 = tile_row(j);
+        int64_t e, rl;
+        locate(f0, e, rl);
+        const uint8_t* w = (dummy ? (const uint8_t*)p.w.gate : mat) + ((e * RI + rl) + (dummy ? 0 : (r & 7))) * rb;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int c = dummy ? 0 : min(4 * (NQ * sg + q) + kq, nch - 1);
+            st.c[q] = __builtin_nontemporal_load((const u32x4*)(w + 16 * c));
+        }
+        const float* srow = (const float*)scale_row<MOE_FMT_FP8>(scale_mat<MOE_FMT_FP8>(dsc, e, RI, H), rl, H);
+#pragma unroll
+        for (int c = 0; c < NQ / 2; ++c) st.s[c] = srow[min((NQ * sg) / 2 + c, nsb - 1)];
+    };
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](Stage& st, int t) {
+        int j, sg;
+        tile_of(t, j, sg);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) asm volatile("" : "+v"(st.c[q]));
+#pragma unroll
+        for (int c = 0; c < NQ / 2; ++c) asm volatile("" : "+v"(st.s[c]));
+#pragma unroll
+        for (int c = 0; c < NQ / 2; ++c) {
+            f32x4 tmp = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int q = 2 * c + h2, qq = NQ * sg + q;
+                const bool valid = qq < ngrp;
+                const u32x4 code = valid ? st.c[q] : u32x4{0u, 0u, 0u, 0u};
+                const LDS char* xp = xrow + 32 * min(4 * qq + kq, nch - 1);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const bf16x8 bop = *(const LDS bf16x8*)(xp + 16 * h);
+                    const uint32_t d0 = code[2 * h], d1 = code[2 * h + 1];
+                    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+                    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+                    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+                    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+                    const bf16x8 aop = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                    tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, tmp, 0, 0, 0);
+                }
+            }
+            const float sc = (NQ * sg) / 2 + c < nsb ? st.s[c] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = fmaf(tmp[i], sc, acc[i]);
+        }
+        if (ks) {  // item done: its partial g (rows 0..7) and v (rows 8..15) of the M tokens to part
+            if (r < M) *(LDS f32x4*)(part + (((int64_t)(j * nstage + sg) * 4 + kq) * M + r) * 4) = acc;
+            acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        } else if (sg == nstage - 1) {  // tile j done: lanes kq < 2 hold g of rows 4 kq + i, lanes kq + 2 their v
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = __shfl_xor(acc[i], 32);
+            if (kq < 2 && r < M) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t mk = row_mask(tile_row(j) + 4 * kq + i);
+                    if ((mk >> r) & 1u)
+                        cst[(tile_slot(j) + 4 * kq + i) * M + __popc(mk & ((1u << r) - 1u))] = silu_mul(acc[i], v[i]);
+                }
+            }
+            acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
     };
     if (nsteps > 0) {
@@ -1994,13 +2179,16 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     int sh_rows = 0;
     int sh_waves = 0;  // waves kWaves - sh_waves .. kWaves - 1 have shared gate/up tasks
     bool sh_done = false;
-    if constexpr (WF == MOE_FMT_MXFP4) {
-        // MXFP4 from 8 tokens on: tiles of 8 shared rows on the matrix cores (on the vector ALU every
-        // code would be decoded once per token, and at 16 tokens one 4-row task outlasts the routing)
+    if constexpr (WF == MOE_FMT_MXFP4 || WF == MOE_FMT_FP8) {
+        // MXFP4 and FP8 from 8 tokens on: tiles of 8 shared rows on the matrix cores (on the vector
+        // ALU every code would be decoded once per token, and at 16 tokens one 4-row task outlasts
+        // the routing)
         if (has_sh && !p.route_only && p.sh_gu_mfma) {
             const int nloc = n_strided(Is / 8, b, G);
             if (nloc > 0) {
-                if ((H / 32) % 16 == 0)
+                if constexpr (WF == MOE_FMT_FP8)
+                    gateup_mfma_f8<kFp8Stage, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
+                else if ((H / 32) % 16 == 0)
                     gateup_mfma_mx<10, true, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
                 else
                     gateup_mfma_mx<10, false, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
@@ -2129,6 +2317,9 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     else
                         gateup_mfma_mx<10, false>(p, xs, nloc, s_mask, s_exp, cst, part);
                 }
+            if constexpr (WF == MOE_FMT_FP8)
+                if (nloc > 0)
+                    gateup_mfma_f8<kFp8Stage>(p, xs, nloc, s_mask, s_exp, cst, p.gu_ksplit ? cst + p.gu_part : nullptr);
             __syncthreads();
             MOE_TRACE(6);
             const int n = nloc * 8 * M;
@@ -2670,8 +2861,10 @@ hipError_t plan_t(Params& p, int G) {
     // decode of E2M1 codes makes MXFP4 rows four times denser in work
     // MXFP4 gate/up rows on the matrix cores: each code is decoded once for all tokens, so the
     // work per weight byte no longer grows with the unit's token count
-    p.gu_mfma = WF == MOE_FMT_MXFP4 ? 1 : 0;
-    p.sh_gu_mfma = WF == MOE_FMT_MXFP4 && M >= 8 && p.Is % 8 == 0 ? 1 : 0;  // the shared expert's too
+    // FP8 from 3 tokens on (at one token the vector path decodes each code once anyway, and 15 of
+    // the 16 token columns of a product would be empty: 34.0 against 31.8 us at Ling width)
+    p.gu_mfma = (WF == MOE_FMT_MXFP4 || (WF == MOE_FMT_FP8 && M >= 3)) ? 1 : 0;
+    p.sh_gu_mfma = (WF == MOE_FMT_MXFP4 || WF == MOE_FMT_FP8) && M >= 8 && p.Is % 8 == 0 ? 1 : 0;  // the shared expert's too
     // per-token cost of a down row (a row's bytes cost kCostBase = 8), from sweeps of the
     // whole-layer time: bf16 over 0, 1, 2, 3, 4 and 6 at 6 and 16 tokens (3 is fastest at both);
     // MXFP4 over 1, 3, 6, 9 and 14 at 16 tokens (6 is fastest: the vector path decodes every
@@ -2685,7 +2878,8 @@ hipError_t plan_t(Params& p, int G) {
     if (p.gu_mfma) {
         // tiles of 8 rows per workgroup; (tile, stage) items with partials in LDS while they fit
         const int64_t tiles = (units * p.I / 8 + G - 1) / G;
-        const int64_t nstage = ((H / 32 + 3) / 4 + 9) / 10;  // stages of 10 block groups
+        // stages of 10 block groups (MXFP4: 128 elements each; FP8: 64 elements each)
+        const int64_t nstage = WF == MOE_FMT_FP8 ? ((H / 64) + kFp8Stage - 1) / kFp8Stage : ((H / 32 + 3) / 4 + 9) / 10;
         const int64_t pbytes = tiles * nstage * 16 * M * 4;
         p.gu_ksplit = pbytes <= 16 * 1024 ? 1 : 0;
         p.gu_part = (int)(tiles * 8 * M);
