@@ -157,10 +157,13 @@ template <>
 struct Geo<MOE_FMT_MXFP4> {
     static constexpr int EPC = 32, LPR_G = 16, RL_G = 1, LPR_D = 8, RL_D = 1;
 };
-// FP8: 16 E4M3 codes per chunk, all in one 128-column scale block
+// FP8: 16 E4M3 codes per chunk, all in one 128-column scale block.  32 lanes per gate/up row (two
+// rows of 2,560 codes per wave and 10 KB per task, the bytes of a bf16 task) and two rows per lane
+// group of a down task (8 rows, 6 KB): a task's loads are what one wave keeps in flight, so tasks
+// of half a bf16 task's bytes streamed at half its rate
 template <>
 struct Geo<MOE_FMT_FP8> {
-    static constexpr int EPC = 16, LPR_G = 64, RL_G = 1, LPR_D = 16, RL_D = 1;
+    static constexpr int EPC = 16, LPR_G = 32, RL_G = 1, LPR_D = 16, RL_D = 2;
 };
 constexpr int kFp8Block = 128;  // FP8 weights: one binary32 scale per 128 x 128 block
 constexpr int kFp8Stage = 10;   // FP8 matrix-core gate/up: chunk groups (64 elements each) per stage
@@ -1126,7 +1129,8 @@ __device__ __forceinline__ void router_rows(const Params& p, const LDS char* xs,
 struct GUTask {
     const uint8_t* g;
     const uint8_t* u;
-    const uint8_t* gs;  // block scales of those rows (scale_row of the first row; FP8 tasks are one row)
+    const uint8_t* gs;  // block scales of those rows (scale_row of the first row; the rows of an FP8
+                        // task lie in one 128-row block and share it)
     const uint8_t* us;
     uint32_t mask;      // the unit's tokens
     int slot;           // staging row of the task's first row
@@ -1147,7 +1151,7 @@ __device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, N
     const int H = p.H;
     const int nch = H / Geo<WF>::EPC;
     const int64_t rb = row_bytes<WF>(H), sb = H / 32;
-    static_assert(WF != MOE_FMT_FP8 || rt_gate<WF>() == 1, "an FP8 gate/up task is one row (one scale row)");
+    static_assert(WF != MOE_FMT_FP8 || kFp8Block % rt_gate<WF>() == 0, "an FP8 gate/up task lies in one row block");
     int q = next(0);
     if (q < 0) return 0;
     Chunk ga[RL][NJ], ua[RL][NJ], gb[RL][NJ], ub[RL][NJ];
@@ -1159,8 +1163,8 @@ __device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, N
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int c = t.dummy ? 0 : min(sl + LPR * j, nch - 1);
-                ld_chunk<WF>(g[rl][j], t.g + ro * rb, t.gs + ro * sb, c);
-                ld_chunk<WF>(u[rl][j], t.u + ro * rb, t.us + ro * sb, c);
+                ld_chunk<WF>(g[rl][j], t.g + ro * rb, WF == MOE_FMT_FP8 ? t.gs : t.gs + ro * sb, c);
+                ld_chunk<WF>(u[rl][j], t.u + ro * rb, WF == MOE_FMT_FP8 ? t.us : t.us + ro * sb, c);
             }
         }
     };
@@ -2088,10 +2092,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     constexpr int XB = AF == MOE_FMT_F32 ? 4 : 2;
     constexpr int RTG = rt_gate<WF>();
     constexpr int RTD = rt_down<WF>();
-    // chunks per lane of a router row and of a token row (activation geometry, 64 lanes a row): NJ
-    // counts gate/up chunks, and an FP8 chunk holds twice the elements of a bf16 one
-    constexpr int NJR = WF == MOE_FMT_FP8 ? 2 * NJ : NJ;
-    static_assert(WF == MOE_FMT_FP8 || Geo<AF>::EPC * Geo<AF>::LPR_G == Geo<WF>::EPC * Geo<WF>::LPR_G,
+    // NJ is also the chunks per lane of a router row and of a token row (64 lanes a row)
+    static_assert(Geo<AF>::EPC * Geo<AF>::LPR_G == Geo<WF>::EPC * Geo<WF>::LPR_G,
                   "router and gate/up rows cover the same elements per chunk column");
     LDS char* lds = (LDS char*)smem;
     LDS int* tab = (LDS int*)(lds + p.lds_tab);
@@ -2124,12 +2126,12 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     if (!norm) async_rows_pitch((char*)xs, (const uint8_t*)p.x, M, H * XB, p.xpitch);
     const int e0 = (int)((int64_t)E * b / G), e1 = (int)((int64_t)E * (b + 1) / G);
     const int nrw = min(e1 - e0, kWaves);  // waves with router rows
-    Chunk rfirst[NJR];
+    Chunk rfirst[NJ];
     {
         const int e = e0 + wave_id(), lane = threadIdx.x & 63, nch = H / Geo<AF>::EPC;
         if (e < e1) {
 #pragma unroll
-            for (int j = 0; j < NJR; ++j)
+            for (int j = 0; j < NJ; ++j)
                 ld_chunk<AF>(rfirst[j], (const uint8_t*)p.wr + (int64_t)e * H * XB, nullptr, min(lane + 64 * j, nch - 1));
         }
     }
@@ -2151,7 +2153,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             async_dwords_to_lds((char*)sclw_sh, p.w.sh_down_s + (int64_t)h0 * (Is / 32), nown * (Is / 32));
     }
     if constexpr (AF == MOE_FMT_BF16)
-        if (norm) rms_norm_rows<NJR>(p, xs);  // the normed token rows replace x everywhere
+        if (norm) rms_norm_rows<NJ>(p, xs);  // the normed token rows replace x everywhere
     __builtin_amdgcn_s_waitcnt(0);  // token rows (and the slice's shared down rows) in LDS
     __syncthreads();
     MOE_TRACE(1);
@@ -2167,7 +2169,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         for (int l = threadIdx.x; l < kSetLines; l += kThreads) line(nxt, l)[0] = 0u;
     }
     // router rows (tagged logits: no arrival counter)
-    if (wave_id() < nrw) router_rows<AF, NJR>(p, xs, e0, e1, rfirst, call + 1u);
+    if (wave_id() < nrw) router_rows<AF, NJ>(p, xs, e0, e1, rfirst, call + 1u);
     MOE_TRACE(2);
     if (p.route_only && b != 0) {
         MOE_TRACE_FLUSH;
@@ -2834,8 +2836,7 @@ hipError_t plan_t(Params& p, int G) {
     constexpr int XB = AF == MOE_FMT_F32 ? 4 : 2;
     int nj, njd;
     chunks<WF>(p, &nj, &njd);
-    const bool fits = (nj <= 1 && njd <= 1) || (WF == MOE_FMT_FP8 ? nj <= 3 && njd <= 3
-                                                                 : WF != MOE_FMT_F32 && nj <= 5 && njd <= 3);
+    const bool fits = (nj <= 1 && njd <= 1) || (WF != MOE_FMT_F32 && nj <= 5 && njd <= 3);
     if (!fits) return hipErrorInvalidValue;  // no kernel instance for this shape
     const int M = p.M, H = p.H;
     const int64_t NP = (int64_t)p.k * M;
@@ -2961,9 +2962,7 @@ hipError_t launch_fmt(const Params& p, int G, int dev, hipStream_t s) {
     int nj, njd;
     chunks<WF>(p, &nj, &njd);
     if (nj <= 1 && njd <= 1) return launch_t<AF, WF, 1, 1>(p, G, dev, s);
-    if constexpr (WF == MOE_FMT_FP8)
-        if (nj <= 3 && njd <= 3) return launch_t<AF, WF, 3, 3>(p, G, dev, s);
-    if constexpr (WF == MOE_FMT_BF16 || WF == MOE_FMT_MXFP4)
+    if constexpr (WF != MOE_FMT_F32)
         if (nj <= 5 && njd <= 3) return launch_t<AF, WF, 5, 3>(p, G, dev, s);
     return hipErrorInvalidValue;
 }
