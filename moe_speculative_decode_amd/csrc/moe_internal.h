@@ -64,7 +64,7 @@ struct Params {
     // LDS layout, byte offsets from the dynamic LDS base (filled by launch_layer)
     int lds_tab, lds_x, lds_cst, lds_sh, lds_ysh, lds_dn, lds_total;
     int cst_bytes;    // staging area (routing scratch, SwiGLU results, down partials)
-    int dn_bytes;     // routed down-row window
+    int dn_bytes;     // slice mode: routed down-row window
     int slice_mode;   // 1: every workgroup computes its y slice of every routed unit (small M*k)
     int slice_mfma;   // 1: slice mode on the matrix cores (bfloat16 SwiGLU rows, swizzled windows)
     int sh_mfma;      // 1: the shared expert's down rows on the matrix cores (swizzled window)

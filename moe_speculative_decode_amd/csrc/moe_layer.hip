@@ -383,7 +383,7 @@ constexpr int kTabWords = (kTabMisc + 8 + 3) / 4 * 4;
 // routing scratch (token masks, expert row offsets, per-token ids / weights / logits), in the
 // staging area
 constexpr int kSelBytes = (2 * kMaxExperts + 3 * kMaxTokens * kMaxTopK) * 4;
-constexpr int kMaxPre = 4;  // routed down-row segments prefetched into LDS per workgroup (unit-major)
+constexpr int kMaxSeg = 4;  // unit-major: segments (one per unit) of a workgroup's down rows in one flat task list
 
 constexpr int kCostBase = 8;  // cost of one weight row's bytes in cost_split units
 constexpr int kSpinLimit = 1 << 20;  // ~1 s of polling; normal waits are microseconds
@@ -1219,12 +1219,14 @@ __device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, N
     info(q, 0, ta);
     ta.dummy = 0;
     load(ga, ua, ta);
+    MOE_TRACE(16);
     while (true) {
         const int qb = next(s + 1);
         info(qb >= 0 ? qb : q, s + 1, tb);
         tb.dummy = qb < 0;
         load(gb, ub, tb);
         settle_all(ga, ua);
+        if (s == 0) MOE_TRACE(17);
         compute(ga, ua, ta);
         ++s;
         if (qb < 0) break;
@@ -1233,11 +1235,13 @@ __device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, N
         ta.dummy = qa < 0;
         load(ga, ua, ta);
         settle_all(gb, ub);
+        if (s == 1) MOE_TRACE(18);
         compute(gb, ub, tb);
         ++s;
         if (qa < 0) break;
         q = qa;
     }
+    MOE_TRACE(19);
     return s;
 }
 
@@ -1354,6 +1358,8 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
         tile_of(t, j, sg);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) asm volatile("" : "+v"(st.c[q]));
+        if (t == 0) MOE_TRACE(17);
+        if (t == 1) MOE_TRACE(18);
 #pragma unroll
         for (int i = 0; i < (WIDE ? 4 * NS : NQ); ++i) asm volatile("" : "+v"(st.s[i]));
         const int sh = (NQ * sg) & 3;
@@ -1410,6 +1416,7 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
     if (nsteps > 0) {
         Stage sa, sb2;
         load(sa, 0);
+        MOE_TRACE(16);
         int t = 0;
         while (true) {
             load(sb2, t + 1);
@@ -1420,6 +1427,7 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
             if (++t >= nsteps) break;
         }
     }
+    MOE_TRACE(19);
     if (ks) {  // sum each tile's stages in stage order, then silu(g) * v for the unit's tokens
         __syncthreads();
         for (int idx = threadIdx.x; idx < nloc * 8 * M; idx += kThreads) {
@@ -1519,6 +1527,8 @@ __device__ __forceinline__ void gateup_mfma_f8(const Params& p, const LDS char* 
         for (int q = 0; q < NQ; ++q) asm volatile("" : "+v"(st.c[q]));
 #pragma unroll
         for (int c = 0; c < NQ / 2; ++c) asm volatile("" : "+v"(st.s[c]));
+        if (t == 0) MOE_TRACE(17);
+        if (t == 1) MOE_TRACE(18);
 #pragma unroll
         for (int c = 0; c < NQ / 2; ++c) {
             f32x4 tmp = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1565,6 +1575,7 @@ __device__ __forceinline__ void gateup_mfma_f8(const Params& p, const LDS char* 
     if (nsteps > 0) {
         Stage sa, sb2;
         load(sa, 0);
+        MOE_TRACE(16);
         int t = 0;
         while (true) {
             load(sb2, t + 1);
@@ -1575,6 +1586,7 @@ __device__ __forceinline__ void gateup_mfma_f8(const Params& p, const LDS char* 
             if (++t >= nsteps) break;
         }
     }
+    MOE_TRACE(19);
     if (ks) {  // sum each tile's stages in stage order, then silu(g) * v for the unit's tokens
         __syncthreads();
         for (int idx = threadIdx.x; idx < nloc * 8 * M; idx += kThreads) {
@@ -2248,6 +2260,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         publish();
         if (threadIdx.x == 0) add_dev(line(set, kLineShared), (uint32_t)sh_rows);
     }
+    MOE_TRACE(20);
     const LDS uint32_t* s_mask = (const LDS uint32_t*)tab + kTabMask;
     const LDS int* s_off = tab + kTabOff;
     const LDS int* s_exp = tab + kTabExp;
@@ -2256,15 +2269,15 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     //      slice mode: rows [h0, h1) of every unit; otherwise an equal share of all units' rows ----
     int64_t d0 = 0, d1 = 0;  // unit-major: this workgroup's (unit, row) range, split by cost
     if constexpr (!SLICE) cost_split(s_mask, U, H, kCostBase, p.cost_dn, G, b, &d0, &d1);
-    int pre_rows[kMaxPre];
-    int pre_off[kMaxPre];
     int nfit = 0;  // slice mode: units whose slice rows are in the window
-    // slice mode on the matrix cores: the window streams in after this workgroup's gate/up rows
-    // have been published (during the wait for the other workgroups): issued before them, it would
-    // sit ahead of the gate/up loads in every wave's in-order memory counter and delay the whole
-    // phase (bf16: -0.8 us at one token; the 4-bit MXFP4 window is small and gains nothing).  The
-    // vector slice path loads its first window task before its wait, so its window is issued here,
-    // before C.
+    // The window streams in after this workgroup's gate/up rows have been published (during the
+    // wait for the other workgroups) for bf16 and FP8 weights: issued before them, it would sit
+    // ahead of the gate/up loads in every wave's in-order memory counter and delay the whole phase
+    // (bf16 at one token: 0.8 us; FP8: 1.3 us).  The 4-bit MXFP4 window is small, and its matrix-
+    // core down rows are fast enough that waiting for a late window costs more (2.3 us at one
+    // token, 2.9 at six): it is issued here, before C.  Unit-major down rows stream from global
+    // memory inside the down phase (an LDS prefetch of them issued here cost ~1 us at six tokens).
+    const bool late_window = WF == MOE_FMT_FP8 || (mf_slice && WF == MOE_FMT_BF16);
     auto slice_window = [&]() {
         if (nown > 0) {
             for (int u = 0; u < nfit; ++u) {
@@ -2282,26 +2295,9 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     };
     if constexpr (SLICE) {
         if (nown > 0) nfit = min(U, (int)(p.dn_bytes / (nown * rbI)));
-        if (!mf_slice || WF != MOE_FMT_BF16) slice_window();
-    } else {
-        int64_t room = p.dn_bytes;
-        int seg = 0;
-        for (int64_t q = d0; q < d1 && seg < kMaxPre; ++seg) {
-            const int u = (int)(q / H);
-            const int ha = (int)(q - (int64_t)u * H);
-            const int hb = (int)min<int64_t>(H, ha + (d1 - q));
-            q += hb - ha;
-            int n = (int)min<int64_t>(hb - ha, room / rbI);
-            if (n < hb - ha) n = n / RTD * RTD;  // whole down tasks only
-            pre_rows[seg] = n;
-            pre_off[seg] = (int)(p.dn_bytes - room);
-            if (n > 0)
-                async_to_lds((char*)(dnw + pre_off[seg]), (const uint8_t*)p.w.down + ((int64_t)s_exp[u] * H + ha) * rbI,
-                             (int)(n * rbI));
-            room -= n * rbI;
-        }
-        for (; seg < kMaxPre; ++seg) pre_rows[seg] = pre_off[seg] = 0;
+        if (!late_window) slice_window();
     }
+    MOE_TRACE(21);
 
     // ---- C: routed gate/up over the flattened (unit, row) list.  Results are staged in LDS,
     //      written at the end, and counted on one counter ----
@@ -2311,6 +2307,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         if (p.gu_mfma) {
             // tiles of 8 rows dealt to the workgroups round robin
             const int nloc = n_strided((int)(nrows / 8), b, G);
+            MOE_TRACE(22);
             if constexpr (WF == MOE_FMT_MXFP4)
                 if (nloc > 0) {
                     LDS float* part = p.gu_ksplit ? cst + p.gu_part : nullptr;
@@ -2371,6 +2368,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             uint32_t pend = 0;
             if (has_pend && lane == 0) pend = add_dev(pctr, 1u);
             int cstart = 0;
+            MOE_TRACE(22);
             const int n = gateup_seq<AF, WF, NJ>(
                 p, xs,
                 [&](int s) -> int {
@@ -2437,7 +2435,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         if (my_rows > 0 && threadIdx.x == 0) add_dev(line(set, kLineRouted + b % kRoutedStripes), (uint32_t)my_rows);
     }
     if constexpr (SLICE)
-        if (mf_slice && WF == MOE_FMT_BF16) slice_window();
+        if (late_window) slice_window();
 
     // ---- B': the shared expert's down rows of this slice (weights in LDS) -> ysh [M][nown], while
     //      the routed units' counters complete (measured: doing it after the down rows instead,
@@ -2476,6 +2474,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     };
     if constexpr (!SLICE)
         if (has_sh && nown > 0) shared_down();
+    if (SLICE && late_window && !mf_slice) {  // the vector path reads window rows before its wait
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
     MOE_TRACE(8);
 
     if constexpr (SLICE) {
@@ -2638,7 +2640,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         // area together and the partials fit at once, the whole range is one task list: one wait,
         // one staging pass, and the next task's loads stay in flight across segment boundaries.
         int nseg = 0;
-        int sg_u[kMaxPre], sg_ha[kMaxPre], sg_hb[kMaxPre];
+        int sg_u[kMaxSeg], sg_ha[kMaxSeg], sg_hb[kMaxSeg];
         bool flat = once;
         {
             int64_t abytes = 0;
@@ -2647,7 +2649,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 const int ha = (int)(q - (int64_t)u * H);
                 const int hb = (int)min<int64_t>(H, ha + (d1 - q));
                 q += hb - ha;
-                if (nseg == kMaxPre) {
+                if (nseg == kMaxSeg) {
                     flat = false;
                     break;
                 }
@@ -2660,7 +2662,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             if (abytes > p.lds_cst - p.lds_x) flat = false;
         }
         if (flat && nseg > 0) {
-            int toff[kMaxPre + 1], aoff[kMaxPre], poff[kMaxPre];
+            int toff[kMaxSeg + 1], aoff[kMaxSeg], poff[kMaxSeg];
             toff[0] = 0;
             int ao = 0, po = 0;
             for (int sg = 0; sg < nseg; ++sg) {
@@ -2682,9 +2684,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 t.K = I;
                 t.orow = r0 - ha;
                 t.prow = poff[sg];
-                t.lds = r0 - ha < pre_rows[sg] ? 1 : 0;
-                t.w = t.lds ? (const uint8_t*)(dnw + pre_off[sg] + (int64_t)(r0 - ha) * rbI)
-                            : (const uint8_t*)p.w.down + (e * H + r0) * rbI;
+                t.lds = 0;
+                t.w = (const uint8_t*)p.w.down + (e * H + r0) * rbI;
                 t.s = scale_mat<WF>(p.w.down_s, e, H, I);
                 t.srow = r0;
                 t.acts = (const LDS float*)xs + aoff[sg];
@@ -2716,7 +2717,6 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             const int t = __popc(s_mask[u]);
             const int row0 = s_off[u];
             const int64_t e = s_exp[u];
-            const int npre = seg < kMaxPre ? pre_rows[seg] : 0;
             const int rows_per_pass = once ? hb - ha : max(RTD, (cap / t) / RTD * RTD);
             bool staged = false;
             // rows [ha, hb) in passes that fit the partial staging area
@@ -2735,21 +2735,9 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 };
                 LDS float* pout = pst + pbase;
                 auto out = [&](int row, int i, float v) { pout[row * t + i] = v; };
-                // part from the LDS window: rows [pa, min(pb, ha + npre))
-                const int la = pa, lb = min(pb, ha + npre);
-                if (lb > la) {
-                    down_run<WF, NJD, true>((const uint8_t*)(dnw + pre_off[seg] + (int64_t)(la - ha) * rbI),
-                                            scale_mat<WF>(p.w.down_s, e, H, I), la, I,
-                                            lb - la, (const LDS float*)xs, t, wave_id(), ready,
-                                            [&](int row, int i, float v) { out(row + la - pa, i, v); });
-                }
-                const int ga = max(pa, ha + npre), gb = pb;
-                if (gb > ga) {
-                    down_run<WF, NJD, false>((const uint8_t*)p.w.down + (e * H + ga) * rbI, scale_mat<WF>(p.w.down_s, e, H, I),
-                                             ga, I, gb - ga,
-                                             (const LDS float*)xs, t, wave_id(), ready,
-                                             [&](int row, int i, float v) { out(row + ga - pa, i, v); });
-                }
+                down_run<WF, NJD, false>((const uint8_t*)p.w.down + (e * H + pa) * rbI, scale_mat<WF>(p.w.down_s, e, H, I),
+                                         pa, I, pb - pa, (const LDS float*)xs, t, wave_id(), ready,
+                                         [&](int row, int i, float v) { out(row, i, v); });
                 __syncthreads();
                 if (once) {
                     pbase += (pb - pa) * t;
@@ -2916,7 +2904,9 @@ hipError_t plan_t(Params& p, int G) {
     }
     p.lds_dn = p.lds_scl + p.scl_sh + p.scl_rt;
     const int budget = kLdsBudget;
-    p.dn_bytes = p.route_only ? 0 : std::max(0, (budget - p.lds_dn) / 16 * 16);
+    // slice mode: the rest of LDS is the window its routed down rows stream into (unit-major down
+    // rows stream from global memory)
+    p.dn_bytes = (p.route_only || !p.slice_mode) ? 0 : std::max(0, (budget - p.lds_dn) / 16 * 16);
     p.lds_total = p.lds_dn + p.dn_bytes;
     if (p.lds_total > budget) return hipErrorInvalidValue;
     return hipSuccess;
