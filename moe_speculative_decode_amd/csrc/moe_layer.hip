@@ -519,9 +519,12 @@ __device__ __forceinline__ void wait_units(uint32_t* set, uint32_t target, uint3
 
 // Starts an asynchronous copy of n bytes (a multiple of 16) from global memory to LDS with every
 // wave of the workgroup.  The data is usable after the issuing waves' next s_waitcnt vmcnt(0) and
-// a workgroup barrier.
-__device__ __forceinline__ void async_to_lds(char* lds, const uint8_t* src, int n) {
-    const int lane = threadIdx.x & 63, wave = wave_id();
+// a workgroup barrier.  Instruction i (i KB in) is issued by wave (i + rot) mod 8: a caller that
+// copies many small pieces passes the number of instructions issued so far, so the pieces do not
+// all start on wave 0.
+__device__ __forceinline__ int rot_wave(int rot) { return (wave_id() + kWaves - rot % kWaves) % kWaves; }
+__device__ __forceinline__ void async_to_lds(char* lds, const uint8_t* src, int n, int rot = 0) {
+    const int lane = threadIdx.x & 63, wave = rot_wave(rot);
     constexpr int chunk = 64 * 16;
     for (int base = wave * chunk; base < n; base += kWaves * chunk) {
         if (base + lane * 16 < n) {
@@ -532,8 +535,8 @@ __device__ __forceinline__ void async_to_lds(char* lds, const uint8_t* src, int 
 }
 
 // The same with 4-byte pieces, for n bytes (a multiple of 4) from a 4-byte aligned source.
-__device__ __forceinline__ void async_dwords_to_lds(char* lds, const uint8_t* src, int n) {
-    const int lane = threadIdx.x & 63, wave = wave_id();
+__device__ __forceinline__ void async_dwords_to_lds(char* lds, const uint8_t* src, int n, int rot = 0) {
+    const int lane = threadIdx.x & 63, wave = rot_wave(rot);
     constexpr int chunk = 64 * 4;
     for (int base = wave * chunk; base < n; base += kWaves * chunk) {
         if (base + lane * 4 < n) {
@@ -565,8 +568,8 @@ __device__ __forceinline__ void async_rows_pitch(char* lds, const uint8_t* src, 
 __host__ __device__ __forceinline__ int chunk_swz(int row, int64_t rb) {
     return (rb & 255) == 0 ? (row & 15) : ((rb & 127) == 0 ? (row & 7) : 0);
 }
-__device__ __forceinline__ void async_rows_to_lds(char* lds, const uint8_t* src, int n, int rb) {
-    const int lane = threadIdx.x & 63, wave = wave_id();
+__device__ __forceinline__ void async_rows_to_lds(char* lds, const uint8_t* src, int n, int rb, int rot = 0) {
+    const int lane = threadIdx.x & 63, wave = rot_wave(rot);
     constexpr int chunk = 64 * 16;
     for (int base = wave * chunk; base < n; base += kWaves * chunk) {
         const int o = base + lane * 16;
@@ -2280,17 +2283,23 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     const bool late_window = WF == MOE_FMT_FP8 || (mf_slice && WF == MOE_FMT_BF16);
     auto slice_window = [&]() {
         if (nown > 0) {
+            // a unit's slice is a few instructions: each unit starts on the wave after the last
+            // one's, so every wave issues its share
+            const int per = (int)((nown * rbI + 1023) / 1024);
             for (int u = 0; u < nfit; ++u) {
                 const uint8_t* src = (const uint8_t*)p.w.down + ((int64_t)s_exp[u] * H + h0) * rbI;
                 if (mf_slice)
-                    async_rows_to_lds((char*)(dnw + (int64_t)u * nown * rbI), src, (int)(nown * rbI), (int)rbI);
+                    async_rows_to_lds((char*)(dnw + (int64_t)u * nown * rbI), src, (int)(nown * rbI), (int)rbI, u * per);
                 else
-                    async_to_lds((char*)(dnw + (int64_t)u * nown * rbI), src, (int)(nown * rbI));
+                    async_to_lds((char*)(dnw + (int64_t)u * nown * rbI), src, (int)(nown * rbI), u * per);
             }
-            if (sclw)
+            if (sclw) {
+                const int pers = (nown * (I / 32) + 255) / 256;
                 for (int u = 0; u < U; ++u)
                     async_dwords_to_lds((char*)(sclw + (int64_t)u * nown * (I / 32)),
-                                        p.w.down_s + ((int64_t)s_exp[u] * H + h0) * (I / 32), nown * (I / 32));
+                                        p.w.down_s + ((int64_t)s_exp[u] * H + h0) * (I / 32), nown * (I / 32),
+                                        nfit * per + u * pers);
+            }
         }
     };
     if constexpr (SLICE) {

@@ -1,11 +1,18 @@
 """GPU parity of the LM head (moe_lm_head) against the fp64 oracle, through the C ABI.
 
 Bar: max |logit_gpu - logit_oracle| <= 1e-4 * rms(logits_oracle).  Derivation: every product of
-a bf16 activation and a bf16 weight (or an E4M3 code, 4 significant bits) is exact in fp32; a lane
-sums its 40 products in four chains of 10, the chains are added pairwise and the lanes of a row by
-a 6-level tree, so the rounding error is at most about 20 * 2^-24 * sum_h |x_h w_h| (one more
-rounding for the FP8 row scale).  With w ~ N(0, 0.02^2), x ~ N(0, 1) and H = 2,560 that sum is about
-33 and rms(logits) about 1: a bound near 4e-5 * rms.  Results are also bit-identical run to run."""
+a bf16 activation and a bf16 weight (or an E4M3 code, 4 significant bits) is exact in fp32.  One
+token (the vector form): a lane sums its 40 products in four chains of 10, the chains are added
+pairwise and the lanes of a row by a 6-level tree, so the rounding error is at most about
+20 * 2^-24 * sum_h |x_h w_h| (one more rounding for the FP8 row scale).  Verify windows on the
+matrix cores: one fixed chain of H / 32 products of 32 elements per logit in fp32; at most
+log2(32) + 1 = 6 roundings per product, each at most 2^-24 times a partial sum of the logit
+(|partial| <= 5 rms for these inputs), so about 480 roundings at H = 2,560.  With w ~ N(0, 0.02^2),
+x ~ N(0, 1) and H = 2,560, sum_h |x_h w_h| is about 33 and rms(logits) about 1: the one-token bound
+is near 4e-5 * rms; the matrix-core roundings are independent and of either sign, so they add like
+a random walk, sqrt(480) * 2^-24 * 5 rms ~ 7e-6 rms, with a worst case of 1.4e-4 only if every
+rounding took one sign at the largest partial.  1e-4 * rms holds both with a wide margin.  Results
+are also bit-identical run to run."""
 import numpy as np
 import pytest
 import torch
@@ -56,6 +63,14 @@ SMALL = [
     synth.LMHeadConfig("fp8_h2560_m16", 2560, 4096, synth.FP8, 16),
     synth.LMHeadConfig("bf16_v7_m2", 64, 7, synth.BF16, 2),   # fewer rows than waves
     synth.LMHeadConfig("fp8_v3_m1", 128, 3, synth.FP8, 1),
+    # matrix-core form (2..16 tokens, whole 256-byte stages): ragged row ranges, partial tiles,
+    # waves without rows, one stage per row, columns past M
+    synth.LMHeadConfig("bf16_mf_v5003_m2", 256, 5003, synth.BF16, 2),
+    synth.LMHeadConfig("bf16_mf_v33_m4", 128, 33, synth.BF16, 4),
+    synth.LMHeadConfig("bf16_mf_h2560_m16", 2560, 20011, synth.BF16, 16),
+    synth.LMHeadConfig("fp8_mf_v4099_m9", 512, 4099, synth.FP8, 9),
+    synth.LMHeadConfig("fp8_mf_v17_m2", 256, 17, synth.FP8, 2),
+    synth.LMHeadConfig("fp8_mf_h2560_m6", 2560, 30001, synth.FP8, 6),
 ]
 
 
