@@ -63,12 +63,13 @@ struct Params {
     int route_delegate;  // 1: workgroup m selects token m's experts and publishes them
     // LDS layout, byte offsets from the dynamic LDS base (filled by launch_layer)
     int lds_tab, lds_x, lds_cst, lds_sh, lds_ysh, lds_dn, lds_total;
+    int lds_tr;       // matrix-core gate/up: kWaves transpose buffers of 4 KB
     int cst_bytes;    // staging area (routing scratch, SwiGLU results, down partials)
     int dn_bytes;     // slice mode: routed down-row window
     int slice_mode;   // 1: every workgroup computes its y slice of every routed unit (small M*k)
     int slice_mfma;   // 1: slice mode on the matrix cores (bfloat16 SwiGLU rows, swizzled windows)
     int sh_mfma;      // 1: the shared expert's down rows on the matrix cores (swizzled window)
-    int gu_mfma;      // 1: routed gate/up rows on the matrix cores (MXFP4 weights)
+    int gu_mfma;      // 1: routed gate/up rows on the matrix cores (MXFP4, FP8 from 3 tokens)
     int gu_cap;       // gate/up tasks one wave may stage (static share plus the chunks it takes)
     int xpitch;       // bytes between consecutive token rows staged in LDS (padded)
     int cost_dn;      // per-token cost of a down row relative to its weight bytes (8 units): work
@@ -85,8 +86,8 @@ struct Params {
     Workspace ws;
     int lds_scl;         // MXFP4: LDS scale windows (shared expert, then routed units) at this offset,
     int scl_sh, scl_rt;  // of these sizes in bytes (0: none)
-    int gu_ksplit;       // MXFP4 gate/up: (tile, stage) items, partials in the staging area at
-    int gu_part;         // this float offset
+    int gu_ksplit;       // MXFP4 slice mode: (tile, stage) items with partials in the staging area
+    int gu_part;         // matrix-core gate/up: float offset of the partials in the staging area (-1: none)
     int sh_gu_mfma;      // MXFP4: the shared expert's gate/up rows on the matrix cores too
     int router_flags;    // MOE_ROUTER_NORM | MOE_ROUTER_BIAS
     float norm_eps;

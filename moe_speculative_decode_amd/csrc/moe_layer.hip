@@ -166,7 +166,6 @@ struct Geo<MOE_FMT_FP8> {
     static constexpr int EPC = 16, LPR_G = 32, RL_G = 1, LPR_D = 16, RL_D = 2;
 };
 constexpr int kFp8Block = 128;  // FP8 weights: one binary32 scale per 128 x 128 block
-constexpr int kFp8Stage = 10;   // FP8 matrix-core gate/up: chunk groups (64 elements each) per stage
 template <int WF>
 __host__ __device__ constexpr int rt_gate() { return Geo<WF>::RL_G * (64 / Geo<WF>::LPR_G); }
 template <int WF>
@@ -1256,7 +1255,9 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
         [&](int i, int, GUTask& t) { info(i, t); }, out);
 }
 
-// Routed gate/up rows on the matrix cores, for MXFP4 weights.  The workgroup's tasks are nloc
+// Routed gate/up rows on the matrix cores, for MXFP4 weights in slice mode (one or a few tokens:
+// a wave has one or two (tile, stage) items, and whole 10 KB items issued at once beat the
+// line-wise stages of gateup_mfma below there).  The workgroup's tasks are nloc
 // tiles of 8 consecutive rows of the flattened (unit, row) list (local tile i = rows 8 (b + i G) ..
 // + 7), dealt to its waves round robin.  A tile is one 16-row A operand: the 8 gate rows (A rows
 // 0..7) and the same 8 up rows (A rows 8..15).
@@ -1448,48 +1449,80 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
     }
 }
 
-// Routed (SH: shared) gate/up rows on the matrix cores for FP8 weights: the tiles, (tile, stage)
-// items, partial sums and outputs of gateup_mfma_mx.  Lane (r, kq) owns the 16-byte chunks 4q + kq
-// of its row (16 E4M3 codes: elements 16 (4q + kq) .. + 15), decoded exactly to bfloat16 pairs (scale
-// 1) and fed to two products: product h of group q takes elements 16 (4q + kq) + 8h .. + 7, and B
-// lane (n, kq) holds the same elements of token n's row.  Groups 2c and 2c + 1 lie in the 128-column
-// block c of the row, so their four products go to a fresh accumulator that joins the running sum
-// times the block's scale for the lane's D rows (rows 0..7: the gate rows' row block, 8..15: the up
-// rows'; the 8 rows of a tile lie in one 128-row block).  Every wave of the workgroup must call this.
-template <int NQ, bool SH = false>
-__device__ __forceinline__ void gateup_mfma_f8(const Params& p, const LDS char* xs, int nloc,
-                                               const LDS uint32_t* s_mask, const LDS int* s_exp, LDS float* cst,
-                                               LDS float* part) {
-    static_assert(NQ % 2 == 0, "stages of whole 128-column blocks");
+// Routed (SH: shared) gate/up rows on the matrix cores, for MXFP4 and FP8 weights.  The
+// workgroup's tasks are nloc tiles of 8 consecutive rows of the flattened (unit, row) list (local
+// tile i = rows 8 (b + i G) .. + 7).  A tile is one 16-row A operand: the 8 gate rows (A rows 0..7)
+// and the same 8 up rows (A rows 8..15).  B holds the rows x of all M tokens (column n = token n,
+// whichever unit the row belongs to), so a chain of v_mfma_f32_16x16x32_bf16 gives g and v of the
+// 8 rows for every token and each code is decoded once, not once per token.  Operand layout of
+// the instruction: lane l holds A[l % 16][8 (l / 16) + 0..7], B[8 (l / 16) + 0..7][l % 16] and
+// D[4 (l / 16) + 0..3][l % 16].
+//
+// A tile streams in stages of 256 bytes per row.  A stage is four loads, each lane 16 bytes, four A
+// rows of 256 contiguous bytes per instruction (the operand layout itself, 16 rows of 64 bytes per
+// instruction, streamed at 2.5-3.5 TB/s here).  It goes through a 4 KB LDS buffer of the wave's
+// own: chunk c of A row a is stored at slot c ^ a, and lane (r, kq) reads chunks 4 j + kq (j =
+// 0..3) of A row r (the 16 lanes of one chunk position hit 16 different bank groups).  R - 1 stages
+// are in flight while one is computed.
+//   MXFP4: a chunk is one MX block (32 codes) and its E8M0 scale byte, decoded with
+// v_cvt_scalef32_pk_bf16_fp4; elements 8 m .. 8 m + 7 feed product m, and B lane (n, kq) holds the
+// same elements of token n's row.
+//   FP8: a chunk is 16 E4M3 codes, decoded exactly to bfloat16 (scale 1) and fed to two products
+// (elements 8 h .. 8 h + 7).  Chunks j = 0, 1 and j = 2, 3 of a stage lie in its two 128-column
+// blocks: each pair's products go to a fresh accumulator that joins the running sum times the
+// block's scale for the lane's D rows (rows 0..7: the gate rows' 128-row block, 8..15: the up
+// rows'; the 8 rows of a tile lie in one 128-row block).
+// Chunks past the end of a row are loaded from the row's last chunk and zeroed.
+//
+// With `part` the workgroup's nloc * nstage (tile, stage) steps are split into 8 contiguous ranges,
+// one per wave, so the waves carry the same bytes to within one stage.  A tile inside one wave's
+// range is finished there; a tile cut by range boundaries leaves a partial sum per wave (at most the
+// first and the last tile of a range: `part`, 2 * M * 64 bytes per wave), added in wave (= stage)
+// order after a barrier.  Without it (no LDS to spare: many tokens and tiles) whole tiles go to the
+// waves round robin.  silu(g) * v of row 8 (b + i G) + s of local tile i and the unit's n-th token
+// goes to cst[(8 i + s) * M + n].  trb: kWaves LDS buffers of 4 KB.  Every wave of the workgroup
+// must call this.
+template <int WF>
+__device__ __forceinline__ void gateup_mfma(const Params& p, bool SH, const LDS char* xs, int nloc,
+                                            const LDS uint32_t* s_mask, const LDS int* s_exp, LDS float* cst,
+                                            LDS float* part, LDS char* trb) {
+    static_assert(WF == MOE_FMT_MXFP4 || WF == MOE_FMT_FP8, "4- and 8-bit weights");
+    constexpr bool MX = WF == MOE_FMT_MXFP4;
+    constexpr int R = 4;  // stages in flight per wave (VGPR ring)
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r = lane & 15, kq = lane >> 4;
     const int H = p.H, I = p.I, M = p.M, G = gridDim.x, b = blockIdx.x;
-    const int nch = H / 16, ngrp = nch / 4, nstage = (ngrp + NQ - 1) / NQ, nsb = H / kFp8Block;
-    const int64_t rb = H;
-    const int RI = SH ? p.Is : I;  // rows of one matrix
-    const bool ks = part != nullptr;
-    const int nsteps = ks ? n_strided(nloc * nstage, wave, kWaves) : n_strided(nloc, wave, kWaves) * nstage;
-    const uint8_t* mat = SH ? (r < 8 ? (const uint8_t*)p.w.sh_gate : (const uint8_t*)p.w.sh_up)
-                            : (r < 8 ? (const uint8_t*)p.w.gate : (const uint8_t*)p.w.up);
-    // the scales of this lane's D rows: gate for kq < 2 (rows 4 kq .. 4 kq + 3 < 8), up otherwise
-    const uint8_t* dsc = SH ? (kq < 2 ? p.w.sh_gate_s : p.w.sh_up_s) : (kq < 2 ? p.w.gate_s : p.w.up_s);
-    auto row_mask = [&](int64_t f) -> uint32_t { return SH ? (1u << M) - 1u : s_mask[(int)(f / I)]; };
-    const LDS char* xrow = xs + (int64_t)min(r, M - 1) * p.xpitch;  // columns past M are dropped
-    auto tile_of = [&](int t, int& i, int& sg) {
-        if (ks) {
-            const int kk = wave + kWaves * t;
-            i = kk / nstage;
-            sg = kk - i * nstage;
+    const int RI = SH ? p.Is : I;                // rows of one matrix
+    const int64_t rb = MX ? H / 2 : H;           // bytes of a row
+    const int nch = (int)(rb / 16);              // 16-byte chunks of a row
+    const int nstage = (nch + 15) / 16;          // stages of 16 chunks
+    const int64_t sb = H / 32;                   // MXFP4: scale bytes of a row
+    const bool WIDE = sb % 16 == 0;              // MXFP4: a stage's scale bytes are one aligned 16-byte load
+    const int nsb = H / kFp8Block;               // FP8: column blocks of a row
+    const bool split = part != nullptr;
+    const int T = nloc * nstage;
+    // this wave's steps: [a0, a0 + nsteps) of the workgroup's, or all stages of tiles wave, wave + 8, ...
+    const int a0 = split ? T * wave / kWaves : 0;
+    const int nsteps = split ? T * (wave + 1) / kWaves - a0 : n_strided(nloc, wave, kWaves) * nstage;
+    auto step_of = [&](int t, int& i, int& sg) {
+        if (split) {
+            const int g = a0 + t;
+            i = g / nstage;
+            sg = g - i * nstage;
         } else {
             i = wave + kWaves * (t / nstage);
             sg = t - (t / nstage) * nstage;
         }
     };
-    auto tile_row = [&](int i) { return (int64_t)(b + i * G) * 8; };
-    auto tile_slot = [&](int i) { return i * 8; };
+    LDS char* tb = trb + wave * 4096;
+    const uint8_t* gmat = (const uint8_t*)(SH ? p.w.sh_gate : p.w.gate);
+    const uint8_t* umat = (const uint8_t*)(SH ? p.w.sh_up : p.w.up);
+    const uint8_t* gsc = SH ? p.w.sh_gate_s : p.w.gate_s;
+    const uint8_t* usc = SH ? p.w.sh_up_s : p.w.up_s;
+    auto row_mask = [&](int64_t f) -> uint32_t { return SH ? (1u << M) - 1u : s_mask[(int)(f / I)]; };
     // expert and row within it of flat row f
     auto locate = [&](int64_t f, int64_t& e, int64_t& rl) {
-        if constexpr (SH) {
+        if (SH) {
             e = 0;
             rl = f;
         } else {
@@ -1498,112 +1531,192 @@ __device__ __forceinline__ void gateup_mfma_f8(const Params& p, const LDS char* 
             rl = f - (int64_t)u * I;
         }
     };
+    const LDS char* xrow = xs + (int64_t)min(r, M - 1) * p.xpitch;  // columns past M are dropped
+    auto tile_row = [&](int i) { return (int64_t)(b + i * G) * 8; };
+    auto tile_slot = [&](int i) { return i * 8; };
     struct Stage {
-        u32x4 c[NQ];
-        float s[NQ / 2];
+        u32x4 c[4];  // instruction i: A row 4 i + kq, chunk 16 sg + r
+        u32x4 s;     // MXFP4: scale bytes of blocks 16 sg .. + 15 of A row r (WIDE; else the bytes of
+                     // blocks 16 sg + 4 j + kq in s[j]); FP8: s[0], s[1] = the stage's two block
+                     // scales for the lane's D rows
     };
-    // t == nsteps: the stand-in prefetch after the last stage (static loads in flight): the first
-    // chunk of the last tile's first row in every lane, one cache line
+    // t >= nsteps: the stand-in prefetch after the last step (a static number of loads in flight):
+    // every lane reads the first chunk of the last step's first row, one cache line
     auto load = [&](Stage& st, int t) {
         const bool dummy = t >= nsteps;
-        t = min(t, nsteps - 1);
-        int j, sg;
-        tile_of(t, j, sg);
-        const int64_t f0 = tile_row(j);
-        int64_t e, rl;
-        locate(f0, e, rl);
-        const uint8_t* w = (dummy ? (const uint8_t*)p.w.gate : mat) + ((e * RI + rl) + (dummy ? 0 : (r & 7))) * rb;
+        int i, sg;
+        step_of(min(t, nsteps - 1), i, sg);
+        const int64_t f0 = tile_row(i);
+        const int ch = dummy ? 0 : min(16 * sg + r, nch - 1);
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int c = dummy ? 0 : min(4 * (NQ * sg + q) + kq, nch - 1);
-            st.c[q] = __builtin_nontemporal_load((const u32x4*)(w + 16 * c));
+        for (int q = 0; q < 4; ++q) {
+            const int a = dummy ? 0 : 4 * q + kq;
+            int64_t e, rl;
+            locate(f0 + (a & 7), e, rl);
+            st.c[q] = __builtin_nontemporal_load((const u32x4*)((a < 8 ? gmat : umat) + (e * RI + rl) * rb + 16 * ch));
         }
-        const float* srow = (const float*)scale_row<MOE_FMT_FP8>(scale_mat<MOE_FMT_FP8>(dsc, e, RI, H), rl, H);
+        int64_t e, rl;
+        if constexpr (MX) {
+            locate(f0 + (dummy ? 0 : (r & 7)), e, rl);
+            const uint8_t* sc = (r < 8 || dummy ? gsc : usc) + (e * RI + rl) * sb;
+            if (WIDE) {
+                st.s = __builtin_nontemporal_load((const u32x4*)(sc + (dummy ? 0 : 16 * sg)));
+            } else {
 #pragma unroll
-        for (int c = 0; c < NQ / 2; ++c) st.s[c] = srow[min((NQ * sg) / 2 + c, nsb - 1)];
+                for (int q = 0; q < 4; ++q) st.s[q] = sc[dummy ? 0 : min(16 * sg + 4 * q + kq, (int)sb - 1)];
+            }
+        } else {
+            locate(f0, e, rl);
+            const float* srow = (const float*)scale_row<WF>(scale_mat<WF>(kq < 2 || dummy ? gsc : usc, e, RI, H), rl, H);
+            st.s[0] = __float_as_uint(srow[dummy ? 0 : min(2 * sg, nsb - 1)]);
+            st.s[1] = __float_as_uint(srow[dummy ? 0 : min(2 * sg + 1, nsb - 1)]);
+            st.s[2] = st.s[3] = 0u;
+        }
     };
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+    const int i0 = a0 / nstage;  // the first tile of this wave's range
     auto compute = [&](Stage& st, int t) {
-        int j, sg;
-        tile_of(t, j, sg);
+        int i, sg;
+        step_of(t, i, sg);
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) asm volatile("" : "+v"(st.c[q]));
-#pragma unroll
-        for (int c = 0; c < NQ / 2; ++c) asm volatile("" : "+v"(st.s[c]));
+        for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(st.c[q]));
+        asm volatile("" : "+v"(st.s));
         if (t == 0) MOE_TRACE(17);
         if (t == 1) MOE_TRACE(18);
+        // the stage into the operand layout, through this wave's LDS buffer
 #pragma unroll
-        for (int c = 0; c < NQ / 2; ++c) {
-            f32x4 tmp = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int q = 2 * c + h2, qq = NQ * sg + q;
-                const bool valid = qq < ngrp;
-                const u32x4 code = valid ? st.c[q] : u32x4{0u, 0u, 0u, 0u};
-                const LDS char* xp = xrow + 32 * min(4 * qq + kq, nch - 1);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const bf16x8 bop = *(const LDS bf16x8*)(xp + 16 * h);
-                    const uint32_t d0 = code[2 * h], d1 = code[2 * h + 1];
-                    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
-                    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
-                    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
-                    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
-                    const bf16x8 aop = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-                    tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, tmp, 0, 0, 0);
-                }
-            }
-            const float sc = (NQ * sg) / 2 + c < nsb ? st.s[c] : 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = fmaf(tmp[i], sc, acc[i]);
+        for (int q = 0; q < 4; ++q) {
+            const int a = 4 * q + kq;
+            *(LDS u32x4*)(tb + a * 256 + 16 * (r ^ a)) = st.c[q];
         }
-        if (ks) {  // item done: its partial g (rows 0..7) and v (rows 8..15) of the M tokens to part
-            if (r < M) *(LDS f32x4*)(part + (((int64_t)(j * nstage + sg) * 4 + kq) * M + r) * 4) = acc;
-            acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        } else if (sg == nstage - 1) {  // tile j done: lanes kq < 2 hold g of rows 4 kq + i, lanes kq + 2 their v
-            f32x4 v;
+        asm volatile("" ::: "memory");  // a wave's LDS operations complete in order
+        u32x4 av[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = __shfl_xor(acc[i], 32);
-            if (kq < 2 && r < M) {
+        for (int q = 0; q < 4; ++q) av[q] = *(const LDS u32x4*)(tb + r * 256 + 16 * ((4 * q + kq) ^ r));
+        asm volatile("" ::: "memory");
+        if constexpr (MX) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t mk = row_mask(tile_row(j) + 4 * kq + i);
-                    if ((mk >> r) & 1u)
-                        cst[(tile_slot(j) + 4 * kq + i) * M + __popc(mk & ((1u << r) - 1u))] = silu_mul(acc[i], v[i]);
+            for (int q = 0; q < 4; ++q) {
+                const int blk = 16 * sg + 4 * q + kq;  // MX block of the row
+                const bool valid = blk < nch;
+                const uint32_t sbyte = WIDE ? (st.s[q] >> (8 * kq)) & 0xFFu : st.s[q];
+                const float sc = e8m0_to_f32(valid ? sbyte : 127u);
+                const u32x4 c = valid ? av[q] : u32x4{0u, 0u, 0u, 0u};
+                const LDS char* xp = xrow + 64 * min(blk, nch - 1);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const bf16x8 bop = *(const LDS bf16x8*)(xp + 16 * m);
+                    const uint32_t wd = c[m];
+                    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 0);
+                    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 1);
+                    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 2);
+                    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 3);
+                    const bf16x8 aop = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                    if (m & 1)
+                        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc1, 0, 0, 0);
+                    else
+                        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc0, 0, 0, 0);
                 }
             }
-            acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        } else {
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {  // column block 2 sg + hb: chunks q = 2 hb, 2 hb + 1
+                f32x4 tmp = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq) {
+                    const int q = 2 * hb + qq;
+                    const int ch = 16 * sg + 4 * q + kq;  // chunk of the row
+                    const bool valid = ch < nch;
+                    const u32x4 code = valid ? av[q] : u32x4{0u, 0u, 0u, 0u};
+                    const LDS char* xp = xrow + 32 * min(ch, nch - 1);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const bf16x8 bop = *(const LDS bf16x8*)(xp + 16 * h);
+                        const uint32_t d0 = code[2 * h], d1 = code[2 * h + 1];
+                        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+                        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+                        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+                        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+                        const bf16x8 aop = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                        tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, tmp, 0, 0, 0);
+                    }
+                }
+                const float sc = 2 * sg + hb < nsb ? __uint_as_float(st.s[hb]) : 0.0f;
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) acc0[k2] = fmaf(tmp[k2], sc, acc0[k2]);
+            }
+        }
+        if (sg == nstage - 1 || (split && t == nsteps - 1)) {  // the end of a tile, or of this wave's range
+            const f32x4 d = acc0 + acc1;
+            if (!split || (i * nstage >= a0 && sg == nstage - 1)) {
+                // the whole tile in this range: lanes kq < 2 hold g of rows 4 kq + k2, lanes kq + 2 their v
+                f32x4 v;
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) v[k2] = __shfl_xor(d[k2], 32);
+                if (kq < 2 && r < M) {
+#pragma unroll
+                    for (int k2 = 0; k2 < 4; ++k2) {
+                        const uint32_t mk = row_mask(tile_row(i) + 4 * kq + k2);
+                        if ((mk >> r) & 1u)
+                            cst[(tile_slot(i) + 4 * kq + k2) * M + __popc(mk & ((1u << r) - 1u))] = silu_mul(d[k2], v[k2]);
+                    }
+                }
+            } else if (r < M) {  // a partial sum: slot 0 for the range's first tile, 1 for its last
+                *(LDS f32x4*)(part + ((((wave * 2 + (i == i0 ? 0 : 1)) * M) + r) * 4 + kq) * 4) = d;
+            }
+            acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            acc1 = acc0;
         }
     };
-    if (nsteps > 0) {
-        Stage sa, sb2;
-        load(sa, 0);
+    Stage st[R];
+    if (nsteps <= R) {
+        // a short range: every load at once, no stand-in loads (a load queued behind a saturated
+        // memory path holds its wave at issue)
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+            if (q < nsteps) load(st[q], q);
         MOE_TRACE(16);
-        int t = 0;
-        while (true) {
-            load(sb2, t + 1);
-            compute(sa, t);
-            if (++t >= nsteps) break;
-            load(sa, t + 1);
-            compute(sb2, t);
-            if (++t >= nsteps) break;
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+            if (q < nsteps) compute(st[q], q);
+    } else {
+        // R stages in flight; the loads are unconditional (past the end: stand-ins) so the number
+        // in flight is static and each stage waits for its own loads only
+#pragma unroll
+        for (int q = 0; q < R; ++q) load(st[q], q);
+        MOE_TRACE(16);
+        for (int t0 = 0; t0 < nsteps; t0 += R) {
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                if (t0 + q < nsteps) compute(st[q], t0 + q);
+                load(st[q], t0 + q + R);
+            }
         }
     }
     MOE_TRACE(19);
-    if (ks) {  // sum each tile's stages in stage order, then silu(g) * v for the unit's tokens
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < nloc * 8 * M; idx += kThreads) {
-            const int i = idx / (8 * M), rem = idx - i * 8 * M;
-            const int jr = rem / M, n = rem - jr * M;
-            float g = 0.0f, v = 0.0f;
-            for (int sg = 0; sg < nstage; ++sg) {
-                const LDS float* pp = part + (int64_t)(i * nstage + sg) * 4 * M * 4;
-                g += pp[((jr >> 2) * M + n) * 4 + (jr & 3)];
-                v += pp[((2 + (jr >> 2)) * M + n) * 4 + (jr & 3)];
-            }
-            const uint32_t mk = row_mask(tile_row(i) + jr);
-            if ((mk >> n) & 1u) cst[(tile_slot(i) + jr) * M + __popc(mk & ((1u << n) - 1u))] = silu_mul(g, v);
+    if (!split) return;
+    __syncthreads();
+    // tiles cut by range boundaries: the partial sums of the waves that share them, in wave order
+    for (int idx = threadIdx.x; idx < nloc * 8 * M; idx += kThreads) {
+        const int i = idx / (8 * M), rem = idx - i * 8 * M;
+        const int jr = rem / M, n = rem - jr * M;
+        int wf = 0, wl = 0;  // the waves whose ranges hold the tile's first and last step
+        for (int w = 0; w < kWaves; ++w) {
+            const int lo = T * w / kWaves, hi = T * (w + 1) / kWaves;
+            if (lo <= i * nstage && i * nstage < hi) wf = w;
+            if (lo <= (i + 1) * nstage - 1 && (i + 1) * nstage - 1 < hi) wl = w;
         }
+        if (wf == wl) continue;  // finished inside one range
+        float g = 0.0f, v = 0.0f;
+        for (int w = wf; w <= wl; ++w) {
+            const int lo = T * w / kWaves, hi = T * (w + 1) / kWaves;
+            if (lo == hi) continue;  // an empty range
+            const LDS float* pp = part + (int64_t)((w * 2 + (i == lo / nstage ? 0 : 1)) * M + n) * 16;
+            g += pp[(jr >> 2) * 4 + (jr & 3)];
+            v += pp[(2 + (jr >> 2)) * 4 + (jr & 3)];
+        }
+        const uint32_t mk = row_mask(tile_row(i) + jr);
+        if ((mk >> n) & 1u) cst[(tile_slot(i) + jr) * M + __popc(mk & ((1u << n) - 1u))] = silu_mul(g, v);
     }
 }
 
@@ -2071,17 +2184,36 @@ __device__ __forceinline__ void down_slice_mfma_mx(int nun, int npre, int nown, 
 // computes the same scalar result.
 __device__ __forceinline__ void cost_split(const LDS uint32_t* s_mask, int U, int n, int c0, int c1, int G, int b,
                                            int64_t* lo, int64_t* hi) {
-    int64_t total = 0;
-    for (int u = 0; u < U; ++u) total += (int64_t)n * (c0 + c1 * __popc(s_mask[u]));
-    auto at = [&](int64_t x) -> int64_t {  // flat index of the first item whose cost interval ends after x
+    // lane l holds units 4 l .. 4 l + 3 (U <= 256), so the unit costs come from LDS in one round
+    // trip and their running sum is one wave scan (a loop over the units, one dependent LDS read
+    // each, took 11 us at 77 units).  A unit's cost n * c is at most 2,560 * (8 + 6 * 16): the
+    // total fits in 32 bits.
+    const int lane = threadIdx.x & 63;
+    int c[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int u = 4 * lane + q;
+        c[q] = u < U ? c0 + c1 * __popc(s_mask[u]) : 0;
+        sum += n * c[q];
+    }
+    const int incl = wave_incl_scan(sum);
+    const int64_t total = __builtin_amdgcn_readlane(incl, 63);
+    const int first = incl - sum;  // the cost of units before 4 l
+    // flat index of the first item whose cost interval ends after x (the unit holding x is unique)
+    auto at = [&](int64_t x) -> int64_t {
         if (x >= total) return (int64_t)U * n;
-        int64_t acc = 0;
-        for (int u = 0; u < U; ++u) {
-            const int64_t c = c0 + c1 * __popc(s_mask[u]);
-            if (acc + n * c > x) return (int64_t)u * n + (x - acc + c - 1) / c;
-            acc += n * c;
+        int64_t r = -1;
+        int64_t acc = first;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t w = (int64_t)n * c[q];
+            if (acc <= x && x < acc + w) r = (int64_t)(4 * lane + q) * n + (x - acc + c[q] - 1) / c[q];
+            acc += w;
         }
-        return (int64_t)U * n;
+        const uint64_t ball = __ballot(r >= 0);
+        const int src = __ffsll((unsigned long long)ball) - 1;
+        const int rl = __builtin_amdgcn_readlane((int)(uint32_t)r, src), rh = __builtin_amdgcn_readlane((int)(r >> 32), src);
+        return (int64_t)(((uint64_t)(uint32_t)rh << 32) | (uint32_t)rl);
     };
     *lo = at(total * b / G);
     *hi = at(total * (b + 1) / G);
@@ -2117,6 +2249,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     LDS char* shw = lds + p.lds_sh;
     LDS float* ysh = (LDS float*)(lds + p.lds_ysh);
     LDS char* dnw = lds + p.lds_dn;
+    LDS char* trb = lds + p.lds_tr;     // the waves' transpose buffers of the matrix-core gate/up
     // MXFP4 scales of the slice rows in LDS (the shared expert's, and the routed units' in slice
     // mode), or null
     const LDS uint8_t* sclw_sh = WF == MOE_FMT_MXFP4 && p.scl_sh ? (const LDS uint8_t*)(lds + p.lds_scl) : nullptr;
@@ -2203,12 +2336,15 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         if (has_sh && !p.route_only && p.sh_gu_mfma) {
             const int nloc = n_strided(Is / 8, b, G);
             if (nloc > 0) {
-                if constexpr (WF == MOE_FMT_FP8)
-                    gateup_mfma_f8<kFp8Stage, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
-                else if ((H / 32) % 16 == 0)
-                    gateup_mfma_mx<10, true, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
-                else
-                    gateup_mfma_mx<10, false, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
+                if constexpr (WF == MOE_FMT_MXFP4 && SLICE) {
+                    if ((H / 32) % 16 == 0)
+                        gateup_mfma_mx<10, true, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
+                    else
+                        gateup_mfma_mx<10, false, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
+                } else {
+                    gateup_mfma<WF>(p, true, xs, nloc, nullptr, nullptr, cst, p.gu_part >= 0 ? cst + p.gu_part : nullptr,
+                                    trb);
+                }
             }
             __syncthreads();
             for (int i = threadIdx.x; i < nloc * 8 * M; i += kThreads) {
@@ -2278,8 +2414,9 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     // ahead of the gate/up loads in every wave's in-order memory counter and delay the whole phase
     // (bf16 at one token: 0.8 us; FP8: 1.3 us).  The 4-bit MXFP4 window is small, and its matrix-
     // core down rows are fast enough that waiting for a late window costs more (2.3 us at one
-    // token, 2.9 at six): it is issued here, before C.  Unit-major down rows stream from global
-    // memory inside the down phase (an LDS prefetch of them issued here cost ~1 us at six tokens).
+    // token, 2.9 at six): it is issued here, before C (issued behind the first gate/up stages
+    // instead: +1 us at one token).  Unit-major down rows stream from global memory inside the down
+    // phase (an LDS prefetch of them issued here cost ~1 us at six tokens).
     const bool late_window = WF == MOE_FMT_FP8 || (mf_slice && WF == MOE_FMT_BF16);
     auto slice_window = [&]() {
         if (nown > 0) {
@@ -2317,7 +2454,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             // tiles of 8 rows dealt to the workgroups round robin
             const int nloc = n_strided((int)(nrows / 8), b, G);
             MOE_TRACE(22);
-            if constexpr (WF == MOE_FMT_MXFP4)
+            if constexpr (WF == MOE_FMT_MXFP4 && SLICE) {
                 if (nloc > 0) {
                     LDS float* part = p.gu_ksplit ? cst + p.gu_part : nullptr;
                     if ((H / 32) % 16 == 0)
@@ -2325,9 +2462,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     else
                         gateup_mfma_mx<10, false>(p, xs, nloc, s_mask, s_exp, cst, part);
                 }
-            if constexpr (WF == MOE_FMT_FP8)
+            } else if constexpr (WF == MOE_FMT_MXFP4 || WF == MOE_FMT_FP8) {
                 if (nloc > 0)
-                    gateup_mfma_f8<kFp8Stage>(p, xs, nloc, s_mask, s_exp, cst, p.gu_ksplit ? cst + p.gu_part : nullptr);
+                    gateup_mfma<WF>(p, false, xs, nloc, s_mask, s_exp, cst, p.gu_part >= 0 ? cst + p.gu_part : nullptr, trb);
+            }
             __syncthreads();
             MOE_TRACE(6);
             const int n = nloc * 8 * M;
@@ -2716,9 +2854,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             __syncthreads();
         }
         int pbase = 0;
-        int seg = 0;
         bool first = true;
-        for (int64_t q = flat ? d1 : d0; q < d1; ++seg) {
+        for (int64_t q = flat ? d1 : d0; q < d1;) {
             const int u = (int)(q / H);
             const int ha = (int)(q - (int64_t)u * H);
             const int hb = (int)min<int64_t>(H, ha + (d1 - q));
@@ -2872,16 +3009,30 @@ hipError_t plan_t(Params& p, int G) {
     // otherwise per wave the static share plus up to twice the average dynamic share (the split
     // the kernel makes from the actual number of units, bounded here by its maximum)
     const int64_t units = std::min<int64_t>(NP, p.E);
-    int64_t cst;
-    if (p.gu_mfma) {
-        // tiles of 8 rows per workgroup; (tile, stage) items with partials in LDS while they fit
+    int64_t cst, cst_nopart = -1;
+    p.gu_part = -1;
+    // MXFP4 slice mode keeps its gate/up rows in whole-item form (gateup_mfma_mx); the other
+    // matrix-core gate/up runs through the line-wise form with its transpose buffers
+    const bool mx_items = WF == MOE_FMT_MXFP4 && p.slice_mode;
+    p.gu_ksplit = 0;
+    if (p.gu_mfma && mx_items) {
+        // tiles of 8 rows dealt round robin; (tile, stage) items with partials in LDS while they fit
         const int64_t tiles = (units * p.I / 8 + G - 1) / G;
-        // stages of 10 block groups (MXFP4: 128 elements each; FP8: 64 elements each)
-        const int64_t nstage = WF == MOE_FMT_FP8 ? ((H / 64) + kFp8Stage - 1) / kFp8Stage : ((H / 32 + 3) / 4 + 9) / 10;
+        const int64_t nstage = ((H / 32 + 3) / 4 + 9) / 10;  // stages of 10 groups of 4 MX blocks
         const int64_t pbytes = tiles * nstage * 16 * M * 4;
         p.gu_ksplit = pbytes <= 16 * 1024 ? 1 : 0;
         p.gu_part = (int)(tiles * 8 * M);
         cst = std::max<int64_t>(kSelBytes, tiles * 8 * M * 4 + (p.gu_ksplit ? pbytes : 0));
+        p.gu_cap = 0;
+    } else if (p.gu_mfma) {
+        // tiles of 8 rows per workgroup; (tile, stage) steps split into contiguous ranges per wave
+        const int64_t tiles = (units * p.I / 8 + G - 1) / G;
+        // outputs [tiles * 8][M], then two partial tiles per wave [kWaves][2][M][16] (the shared
+        // expert's gate/up, at most one tile per workgroup, uses the same areas); dropped below if
+        // the LDS budget has no room for them
+        p.gu_part = (int)(tiles * 8 * M);
+        cst = std::max<int64_t>(kSelBytes, tiles * 8 * M * 4 + (int64_t)kWaves * 2 * M * 64);
+        cst_nopart = std::max<int64_t>(kSelBytes, tiles * 8 * M * 4);
         p.gu_cap = 0;
     } else {
         const int64_t rtg = rt_gate<WF>();
@@ -2891,7 +3042,8 @@ hipError_t plan_t(Params& p, int G) {
         p.gu_cap = (int)(Rs + 2 * ((dyn + kWaves * G - 1) / (kWaves * G)) + 2 * ch + 5);
         cst = std::max<int64_t>(kSelBytes, (int64_t)kWaves * p.gu_cap * (rtg * M * 4 + 4) + kWaves * 4);
     }
-    cst = std::max<int64_t>(cst, p.slice_mode ? (NP + M) * nown * 4 : 16 * 1024);
+    const int64_t cst_min = p.slice_mode ? (NP + M) * nown * 4 : 16 * 1024;
+    cst = std::max<int64_t>(cst, cst_min);
     // token rows 16 bytes further apart than their size: the 16 token columns of a matrix-core B
     // operand then start in 16 different bank groups
     p.xpitch = H * XB + 16;
@@ -2900,19 +3052,30 @@ hipError_t plan_t(Params& p, int G) {
     p.lds_tab = 0;
     p.lds_x = round16(kTabWords * 4);
     p.lds_cst = p.lds_x + round16(xb);
-    p.cst_bytes = round16(cst);
-    p.lds_sh = p.lds_cst + p.cst_bytes;
-    p.lds_ysh = p.lds_sh + round16(p.Is > 0 ? nown * row_bytes<WF>(p.Is) : 0);
-    p.lds_scl = p.lds_ysh + round16((int64_t)M * nown * 4);
-    // MXFP4 scales of the slice rows in LDS (copied in 4-byte pieces: whole dwords per row block):
-    // the shared expert's when its down rows run on the matrix cores, the routed units' in slice mode
-    p.scl_sh = p.scl_rt = 0;
-    if constexpr (WF == MOE_FMT_MXFP4) if (!p.route_only) {
-        if (p.sh_mfma && p.Is > 0 && (p.Is / 32) % 4 == 0) p.scl_sh = (int)round16((int64_t)nown * (p.Is / 32));
-        if (p.slice_mfma && (p.I / 32) % 4 == 0) p.scl_rt = (int)round16(units * nown * (p.I / 32));
-    }
-    p.lds_dn = p.lds_scl + p.scl_sh + p.scl_rt;
     const int budget = kLdsBudget;
+    p.cst_bytes = round16(cst);
+    // the fixed regions; a second pass without the partial tiles if they do not fit
+    for (int pass = 0;; ++pass) {
+        p.lds_sh = p.lds_cst + p.cst_bytes;
+        p.lds_ysh = p.lds_sh + round16(p.Is > 0 ? nown * row_bytes<WF>(p.Is) : 0);
+        p.lds_scl = p.lds_ysh + round16((int64_t)M * nown * 4);
+        // MXFP4 scales of the slice rows in LDS (copied in 4-byte pieces: whole dwords per row
+        // block): the shared expert's when its down rows run on the matrix cores, the routed units'
+        // in slice mode
+        p.scl_sh = p.scl_rt = 0;
+        if constexpr (WF == MOE_FMT_MXFP4) if (!p.route_only) {
+            if (p.sh_mfma && p.Is > 0 && (p.Is / 32) % 4 == 0) p.scl_sh = (int)round16((int64_t)nown * (p.Is / 32));
+            if (p.slice_mfma && (p.I / 32) % 4 == 0) p.scl_rt = (int)round16(units * nown * (p.I / 32));
+        }
+        p.lds_tr = p.lds_scl + p.scl_sh + p.scl_rt;
+        p.lds_dn = p.lds_tr + ((p.gu_mfma || p.sh_gu_mfma) && !mx_items && !p.route_only ? kWaves * 4096 : 0);
+        if (pass == 0 && p.lds_dn > budget && cst_nopart >= 0) {  // no room for the partial tiles
+            p.gu_part = -1;
+            p.cst_bytes = round16(std::max<int64_t>(cst_nopart, cst_min));
+            continue;
+        }
+        break;
+    }
     // slice mode: the rest of LDS is the window its routed down rows stream into (unit-major down
     // rows stream from global memory)
     p.dn_bytes = (p.route_only || !p.slice_mode) ? 0 : std::max(0, (budget - p.lds_dn) / 16 * 16);
