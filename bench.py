@@ -37,7 +37,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer µs/step + achieved HBM GB/s (% of peak), Ling shapes, M=1/6/16"
 PEAK_HBM_GBPS = 8000.0
-KERNEL_SOURCES = ["moe_speculative_decode_amd/csrc/moe_layer.hip", "moe_speculative_decode_amd/csrc/moe_internal.h"]
+# the sources of each kernel: counter summaries taken on other sources are stale
+KERNEL_SOURCES = {"k_layer": ["moe_speculative_decode_amd/csrc/moe_layer.hip",
+                              "moe_speculative_decode_amd/csrc/moe_internal.h"],
+                  "k_lm_head": ["moe_speculative_decode_amd/csrc/lm_head.hip"]}
 HEADLINE = "ling_bf16_m1"
 WORKLOADS = ["ling_bf16_m1", "ling_bf16_m6", "ling_bf16_m16_ragged", "ling_mxfp4_m1", "ling_mxfp4_m6",
              "ling_mxfp4_m16_ragged", "ling_fp8_m1", "ling_fp8_m6", "ling_fp8_m16_ragged"]
@@ -63,9 +66,13 @@ def algorithmic_bytes(cfg, U: int) -> int:
     return E * H * ab + U * expert + shared + 2 * M * H * ab + 8 * M * k
 
 
-def kernel_hash() -> str:
+def kernel_of(workload: str) -> str:
+    return "k_lm_head" if workload.startswith("lm_head") else "k_layer"
+
+
+def kernel_hash(kernel: str = "k_layer") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
@@ -77,7 +84,7 @@ def traffic_from_profiles(workload: str):
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("kernel_hash") != kernel_hash():
+    if d.get("kernel_hash") != kernel_hash(kernel_of(workload)):
         return None
     return d.get("bytes_per_step")
 
