@@ -792,6 +792,7 @@ __device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, ui
         __builtin_amdgcn_s_sleep(1);
         asm volatile("" ::: "memory");  // the next iteration reads memory again
     }
+    MOE_TRACE(23);
     // selection keys: the logit, or the logit plus the expert's bias
     float key[8];
 #pragma unroll
@@ -830,6 +831,7 @@ __device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, ui
             local_max(lm, li);
         }
     }
+    MOE_TRACE(24);
     // weights: softmax over the k selected logits (lanes 0..k-1 of row 0; k <= 16); without a bias
     // the first selected logit is the largest
     float top;
@@ -1293,7 +1295,7 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
                             : (r < 8 ? (const uint8_t*)p.w.gate : (const uint8_t*)p.w.up);
     const uint8_t* mats = SH ? (r < 8 ? p.w.sh_gate_s : p.w.sh_up_s) : (r < 8 ? p.w.gate_s : p.w.up_s);
     // the token mask of a flat row: the unit's, or every token for the shared expert
-    auto row_mask = [&](int64_t f) -> uint32_t { return SH ? (1u << M) - 1u : s_mask[(int)(f / I)]; };
+    auto row_mask = [&](int64_t f) -> uint32_t { return SH ? (1u << M) - 1u : s_mask[(int)f / I]; };
     const LDS char* xrow = xs + (int64_t)min(r, M - 1) * p.xpitch;  // columns past M are dropped
     // local tile and stage of this wave's step t; a local tile's first flat row and staging slot
     auto tile_of = [&](int t, int& i, int& sg) {
@@ -1327,7 +1329,7 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
         const int64_t f = tile_row(j) + (dummy ? 0 : (r & 7));
         int64_t row = f;  // the shared expert's rows are the flat rows
         if constexpr (!SH) {
-            const int u = (int)(f / I);
+            const int u = (int)f / I;
             row = (int64_t)s_exp[u] * I + (f - (int64_t)u * I);
         }
         const uint8_t* w = (dummy ? (const uint8_t*)p.w.gate : mat) + row * rb;
@@ -1519,14 +1521,14 @@ __device__ __forceinline__ void gateup_mfma(const Params& p, bool SH, const LDS 
     const uint8_t* umat = (const uint8_t*)(SH ? p.w.sh_up : p.w.up);
     const uint8_t* gsc = SH ? p.w.sh_gate_s : p.w.gate_s;
     const uint8_t* usc = SH ? p.w.sh_up_s : p.w.up_s;
-    auto row_mask = [&](int64_t f) -> uint32_t { return SH ? (1u << M) - 1u : s_mask[(int)(f / I)]; };
+    auto row_mask = [&](int64_t f) -> uint32_t { return SH ? (1u << M) - 1u : s_mask[(int)f / I]; };
     // expert and row within it of flat row f
     auto locate = [&](int64_t f, int64_t& e, int64_t& rl) {
         if (SH) {
             e = 0;
             rl = f;
         } else {
-            const int u = (int)(f / I);
+            const int u = (int)f / I;
             e = s_exp[u];
             rl = f - (int64_t)u * I;
         }
@@ -1548,17 +1550,16 @@ __device__ __forceinline__ void gateup_mfma(const Params& p, bool SH, const LDS 
         step_of(min(t, nsteps - 1), i, sg);
         const int64_t f0 = tile_row(i);
         const int ch = dummy ? 0 : min(16 * sg + r, nch - 1);
+        int64_t e, rl;  // the tile's 8 rows lie in one unit: rows rl .. rl + 7 of expert e
+        locate(f0, e, rl);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int a = dummy ? 0 : 4 * q + kq;
-            int64_t e, rl;
-            locate(f0 + (a & 7), e, rl);
-            st.c[q] = __builtin_nontemporal_load((const u32x4*)((a < 8 ? gmat : umat) + (e * RI + rl) * rb + 16 * ch));
+            st.c[q] = __builtin_nontemporal_load(
+                (const u32x4*)((a < 8 ? gmat : umat) + (e * RI + rl + (a & 7)) * rb + 16 * ch));
         }
-        int64_t e, rl;
         if constexpr (MX) {
-            locate(f0 + (dummy ? 0 : (r & 7)), e, rl);
-            const uint8_t* sc = (r < 8 || dummy ? gsc : usc) + (e * RI + rl) * sb;
+            const uint8_t* sc = (r < 8 || dummy ? gsc : usc) + (e * RI + rl + (dummy ? 0 : (r & 7))) * sb;
             if (WIDE) {
                 st.s = __builtin_nontemporal_load((const u32x4*)(sc + (dummy ? 0 : 16 * sg)));
             } else {
@@ -1566,7 +1567,6 @@ __device__ __forceinline__ void gateup_mfma(const Params& p, bool SH, const LDS 
                 for (int q = 0; q < 4; ++q) st.s[q] = sc[dummy ? 0 : min(16 * sg + 4 * q + kq, (int)sb - 1)];
             }
         } else {
-            locate(f0, e, rl);
             const float* srow = (const float*)scale_row<WF>(scale_mat<WF>(kq < 2 || dummy ? gsc : usc, e, RI, H), rl, H);
             st.s[0] = __float_as_uint(srow[dummy ? 0 : min(2 * sg, nsb - 1)]);
             st.s[1] = __float_as_uint(srow[dummy ? 0 : min(2 * sg + 1, nsb - 1)]);
@@ -2207,7 +2207,7 @@ __device__ __forceinline__ void cost_split(const LDS uint32_t* s_mask, int U, in
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int64_t w = (int64_t)n * c[q];
-            if (acc <= x && x < acc + w) r = (int64_t)(4 * lane + q) * n + (x - acc + c[q] - 1) / c[q];
+            if (acc <= x && x < acc + w) r = (int64_t)(4 * lane + q) * n + (int)(x - acc + c[q] - 1) / c[q];
             acc += w;
         }
         const uint64_t ball = __ballot(r >= 0);
@@ -2215,12 +2215,14 @@ __device__ __forceinline__ void cost_split(const LDS uint32_t* s_mask, int U, in
         const int rl = __builtin_amdgcn_readlane((int)(uint32_t)r, src), rh = __builtin_amdgcn_readlane((int)(r >> 32), src);
         return (int64_t)(((uint64_t)(uint32_t)rh << 32) | (uint32_t)rl);
     };
-    *lo = at(total * b / G);
-    *hi = at(total * (b + 1) / G);
+    // total * b / G without 64-bit division (total < 2^27)
+    auto share = [&](int bb) { return (int64_t)((int)total / G) * bb + (int)((int)total % G) * bb / G; };
+    *lo = at(share(b));
+    *hi = at(share(b + 1));
 }
 
 // First row of workgroup o's slice of y's columns: [slice0(o), slice0(o + 1)).
-__device__ __forceinline__ int slice0(int H, int G, int o) { return (int)((int64_t)H * o / G); }
+__device__ __forceinline__ int slice0(int H, int G, int o) { return H * o / G; }  // H * G < 2^31
 
 // ------------------------------------------------------------------------------------------
 // the layer kernel
@@ -2272,7 +2274,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     }
     const bool norm = AF == MOE_FMT_BF16 && (p.router_flags & MOE_ROUTER_NORM) != 0;
     if (!norm) async_rows_pitch((char*)xs, (const uint8_t*)p.x, M, H * XB, p.xpitch);
-    const int e0 = (int)((int64_t)E * b / G), e1 = (int)((int64_t)E * (b + 1) / G);
+    const int e0 = E * b / G, e1 = E * (b + 1) / G;
     const int nrw = min(e1 - e0, kWaves);  // waves with router rows
     Chunk rfirst[NJ];
     {
@@ -2362,7 +2364,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     }
     if (has_sh && !p.route_only && !sh_done) {
         const int T = Is / RTG;  // a contiguous range of tasks per workgroup
-        const int qa = (int)((int64_t)T * b / G), qb = (int)((int64_t)T * (b + 1) / G);
+        const int qa = T * b / G, qb = T * (b + 1) / G;
         sh_rows = (qb - qa) * RTG;
         sh_waves = min(qb - qa, kWaves);
         gateup_run<AF, WF, NJ>(
@@ -2472,7 +2474,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             for (int i = threadIdx.x; i < n; i += kThreads) {
                 const int sl = i / M, m = i - sl * M;
                 const int64_t f = (int64_t)(b + (sl / 8) * G) * 8 + sl % 8;
-                const int u = (int)(f / I);
+                const int u = (int)f / I;
                 if (m < __popc(s_mask[u]))
                 {
                     const int64_t o = (int64_t)(s_off[u] + m) * p.act_stride + (f - (int64_t)u * I);
@@ -2499,14 +2501,14 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             const int P0 = dyn ? kWaves * G * Rs : T;
             // this workgroup's static tasks: a contiguous range of the static part, dealt to its
             // waves round robin (consecutive rows: whole DRAM pages, contiguous write-out)
-            const int sa = (int)((int64_t)P0 * b / G), sbnd = (int)((int64_t)P0 * (b + 1) / G);
+            const int sa = P0 * b / G, sbnd = P0 * (b + 1) / G;  // task counts * G < 2^31: 32-bit divisions
             const int ns = n_strided(sbnd - sa, w, kWaves);  // static positions of this wave
             // consecutive workgroups sit on different XCDs (round robin), so pool b mod npool
             // gathers workgroups of one XCD (measured: stealing across XCDs costs more than it
             // evens out)
             const int npool = max(1, G / 8), pool = b % npool;
-            const int pa = P0 + (int)((int64_t)(T - P0) * pool / npool);
-            const int pb = P0 + (int)((int64_t)(T - P0) * (pool + 1) / npool);
+            const int pa = P0 + (T - P0) * pool / npool;
+            const int pb = P0 + (T - P0) * (pool + 1) / npool;
             const int64_t rb = row_bytes<WF>(H);
             const int ch = max(1, (int)(20480 / (2 * RTG * rb)));
             const int nch = (pb - pa + ch - 1) / ch;
@@ -2543,7 +2545,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 },
                 [&](int q, int s, GUTask& t) {
                     const int64_t f = (int64_t)q * RTG;  // the task's first flat row
-                    const int u = uni((int)(f / I));
+                    const int u = uni((int)f / I);
                     const int64_t e = uni(s_exp[u]);
                     const int64_t r0 = f - (int64_t)u * I;
                     t.g = (const uint8_t*)p.w.gate + (e * I + r0) * rb;
@@ -2564,7 +2566,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 const int sp = sl / RTG;
                 if (sp < nwv[wv]) {
                     const int64_t f = (int64_t)qlog[wv * cap + sp] * RTG + sl % RTG;
-                    const int u = (int)(f / I);
+                    const int u = (int)f / I;
                     if (m < __popc(s_mask[u]))
                     {
                     const int64_t o = (int64_t)(s_off[u] + m) * p.act_stride + (f - (int64_t)u * I);
@@ -2776,7 +2778,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         const int cap = p.cst_bytes / 4;
         int64_t need = 0;
         for (int64_t q = d0; q < d1;) {
-            const int u = (int)(q / H);
+            const int u = (int)q / H;
             const int ha = (int)(q - (int64_t)u * H);
             const int hb = (int)min<int64_t>(H, ha + (d1 - q));
             q += hb - ha;
@@ -2792,7 +2794,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         {
             int64_t abytes = 0;
             for (int64_t q = d0; q < d1;) {
-                const int u = (int)(q / H);
+                const int u = (int)q / H;
                 const int ha = (int)(q - (int64_t)u * H);
                 const int hb = (int)min<int64_t>(H, ha + (d1 - q));
                 q += hb - ha;
@@ -2856,7 +2858,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         int pbase = 0;
         bool first = true;
         for (int64_t q = flat ? d1 : d0; q < d1;) {
-            const int u = (int)(q / H);
+            const int u = (int)q / H;
             const int ha = (int)(q - (int64_t)u * H);
             const int hb = (int)min<int64_t>(H, ha + (d1 - q));
             q += hb - ha;
@@ -2900,7 +2902,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         if (once) {  // every partial of the range, in the order it was staged
             int base = 0;
             for (int64_t q = d0; q < d1;) {
-                const int u = (int)(q / H);
+                const int u = (int)q / H;
                 const int ha = (int)(q - (int64_t)u * H);
                 const int hb = (int)min<int64_t>(H, ha + (d1 - q));
                 q += hb - ha;
