@@ -112,6 +112,23 @@ __device__ __forceinline__ float wave_max_bcast(float v) {
     v = fmaxf(v, __builtin_bit_cast(float, dpp_rows<0x143, 0xC>(b, b)));  // row_bcast:31 into rows 2, 3
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+// Maximum of an unsigned value over the wave, in every lane (0 is the identity).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    auto step = [](uint32_t x, int y) { return max(x, (uint32_t)y); };
+    int b = (int)v;
+    v = step(v, __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+    b = (int)v;
+    v = step(v, __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+    b = (int)v;
+    v = step(v, __builtin_amdgcn_update_dpp(0, b, 0x141, 0xF, 0xF, true));  // row_half_mirror
+    b = (int)v;
+    v = step(v, __builtin_amdgcn_update_dpp(0, b, 0x140, 0xF, 0xF, true));  // row_mirror
+    b = (int)v;
+    v = step(v, __builtin_amdgcn_update_dpp(0, b, 0x142, 0xA, 0xF, false));  // row_bcast:15 into rows 1, 3
+    b = (int)v;
+    v = step(v, __builtin_amdgcn_update_dpp(0, b, 0x143, 0xC, 0xF, false));  // row_bcast:31 into rows 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
 // The wave's index in the workgroup, as a scalar the compiler knows to be wave-uniform.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -793,43 +810,75 @@ __device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, ui
         asm volatile("" ::: "memory");  // the next iteration reads memory again
     }
     MOE_TRACE(23);
-    // selection keys: the logit, or the logit plus the expert's bias
-    float key[8];
+    // Selection.  Each lane sorts its 8 entries once, descending, as 64-bit words (selection key as
+    // an order-preserving integer << 32 | 7 - index: larger key first, then the lower index), so a
+    // round is one wave maximum of the lanes' heads and a shift in the winning lane (recomputing the
+    // winner's maximum instead was a chain of 21 dependent instructions per round).  Equal heads:
+    // the lowest lane holds the lowest ids.  Past E: 0, below every real key.  With a bias the raw
+    // logits travel with their keys (the weights use them).
+    uint64_t c[8];
+    float rv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) key[i] = 8 * lane + i >= E ? -INFINITY : v[i] + bv[i];
-    auto local_max = [&](float& m, int& mi) {
-        m = key[0];
-        mi = 0;
-#pragma unroll
-        for (int i = 1; i < 8; ++i) {
-            const bool gt = key[i] > m;
-            m = gt ? key[i] : m;
-            mi = gt ? i : mi;
-        }
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t u = __float_as_uint(v[i] + bv[i]);
+        const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        c[i] = 8 * lane + i >= E ? 0ull : ((uint64_t)key << 32) | (uint32_t)(7 - i);
+        rv[i] = v[i];
+    }
+    auto sort8 = [&](auto with_raw) {
+        auto ce = [&](int i, int j) {  // c[i] >= c[j] afterwards
+            const uint64_t a = c[i], bb = c[j];
+            const bool sw = bb > a;
+            c[i] = sw ? bb : a;
+            c[j] = sw ? a : bb;
+            if constexpr (decltype(with_raw)::value) {
+                const float ra = rv[i], rb = rv[j];
+                rv[i] = sw ? rb : ra;
+                rv[j] = sw ? ra : rb;
+            }
+        };
+        ce(0, 2), ce(1, 3), ce(4, 6), ce(5, 7);
+        ce(0, 4), ce(1, 5), ce(2, 6), ce(3, 7);
+        ce(0, 1), ce(2, 3), ce(4, 5), ce(6, 7);
+        ce(2, 4), ce(3, 5);
+        ce(1, 4), ce(3, 6);
+        ce(1, 2), ce(3, 4), ce(5, 6);
     };
-    float lm;
-    int li;
-    local_max(lm, li);
-    float my_v = -INFINITY;  // lane r < k: the logit of the r-th selected expert
+    if (bias)
+        sort8(std::true_type{});
+    else
+        sort8(std::false_type{});
+    uint32_t my_key = 0u;  // lane r < k: the selection key of the r-th selected expert
+    float my_raw = 0.0f;   // with a bias: its raw logit
     int my_id = 0;
     for (int r = 0; r < k; ++r) {
-        const float mx = wave_max_bcast(lm);
-        const uint64_t ball = __ballot(lm == mx);
-        const int wl = ball ? __ffsll((unsigned long long)ball) - 1 : 0;  // no match only for NaN inputs
-        const int wi = __builtin_amdgcn_readlane(li, wl);
-        float raw = v[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) raw = i == wi ? v[i] : raw;
-        raw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, raw), wl));
+        const uint32_t head = (uint32_t)(c[0] >> 32);
+        const uint32_t K = wave_max_u32(head);
+        const uint64_t ball = __ballot(head == K);
+        const int wl = __builtin_amdgcn_readfirstlane(ball ? __ffsll((unsigned long long)ball) - 1 : 0);
+        const int wi = 7 - __builtin_amdgcn_readlane((int)(uint32_t)c[0], wl);
+        const float wr = bias ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rv[0]), wl)) : 0.0f;
         if (lane == r) {
-            my_v = raw;
+            my_key = K;
+            my_raw = wr;
             my_id = min(8 * wl + wi, E - 1);
         }
         if (lane == wl) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) key[i] = i == wi ? -INFINITY : key[i];
-            local_max(lm, li);
+            for (int i = 0; i < 7; ++i) c[i] = c[i + 1];
+            c[7] = 0ull;
+            if (bias) {
+#pragma unroll
+                for (int i = 0; i < 7; ++i) rv[i] = rv[i + 1];
+            }
         }
+    }
+    float my_v;
+    if (bias) {
+        my_v = lane < k ? my_raw : -INFINITY;
+    } else {  // the key is the logit itself
+        const uint32_t u = (my_key & 0x80000000u) ? (my_key & 0x7FFFFFFFu) : ~my_key;
+        my_v = lane < k ? __uint_as_float(u) : -INFINITY;
     }
     MOE_TRACE(24);
     // weights: softmax over the k selected logits (lanes 0..k-1 of row 0; k <= 16); without a bias
