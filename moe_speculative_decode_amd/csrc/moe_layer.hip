@@ -168,7 +168,7 @@ struct Geo<MOE_FMT_F32> {
 };
 template <>
 struct Geo<MOE_FMT_BF16> {
-    static constexpr int EPC = 8, LPR_G = 64, RL_G = 1, LPR_D = 32, RL_D = 2;
+    static constexpr int EPC = 8, LPR_G = 64, RL_G = 1, LPR_D = 32, RL_D = 4;
 };
 template <>
 struct Geo<MOE_FMT_MXFP4> {
