@@ -68,6 +68,11 @@ SMALL = [
     # router rows span twice the chunks of FP8 gate/up rows (bf16 activations)
     small("fp8_h1024", FP8, H=1024, I=256, lens=(3,)),
     small("fp8_h2560", FP8, H=2560, E=64, k=4, I=256, Is=128, lens=(2,), norm=True),
+    # matrix-core gate/up in slice mode (FP8 from three tokens, M * k <= 16)
+    small("fp8_slice_mfma_m4", FP8, I=256, lens=(4,)),
+    # the line-form matrix-core gate/up for MXFP4 (unit-major): scale rows not a multiple of 16
+    # bytes (H = 544: 17 blocks, a last stage of one block) and the shared expert's tiles from 8 tokens
+    small("mxfp4_um_tail", MXFP4, H=544, E=64, k=4, I=768, Is=96, lens=(16,)),
 ]
 
 
@@ -124,8 +129,11 @@ def test_ling_configs(name):
     assert mdl.moe_read_status(case.ws) == mdl.MOE_OK
 
 
-def test_deterministic_and_permutation_equivariant():
-    cfg = small("perm", lens=(11,))
+@pytest.mark.parametrize("fmt", [BF16, MXFP4, FP8], ids=["bf16", "mxfp4", "fp8"])
+def test_deterministic_and_permutation_equivariant(fmt):
+    """Unit-major down rows (and the matrix-core gate/up with its per-wave step ranges for MXFP4
+    and FP8): bit-identical across runs and token orders."""
+    cfg = small("perm", fmt, I=256 if fmt == FP8 else 192, lens=(11,))
     case = G.Case(cfg)
     y1, ids1, w1 = case.run()
     y2, ids2, w2 = case.run()
@@ -139,11 +147,12 @@ def test_deterministic_and_permutation_equivariant():
         assert set(idsp[m].tolist()) == set(ids1[perm[m]].tolist())
 
 
-@pytest.mark.parametrize("fmt", [BF16, MXFP4], ids=["bf16", "mxfp4"])
+@pytest.mark.parametrize("fmt", [BF16, MXFP4, FP8], ids=["bf16", "mxfp4", "fp8"])
 def test_permutation_equivariant_slice_mode(fmt):
-    """Few pair rows: every workgroup computes its own columns of every unit on the matrix cores.
-    The result is bit-identical across token orders (fixed operand order per token column)."""
-    cfg = small("perm_slice", fmt, k=4, lens=(4,))
+    """Few pair rows: every workgroup computes its own columns of every unit (bf16 and MXFP4 on the
+    matrix cores, FP8 on the vector path after a matrix-core gate/up).  The result is
+    bit-identical across token orders (fixed operand order per token column)."""
+    cfg = small("perm_slice", fmt, k=4, I=256 if fmt == FP8 else 192, lens=(4,))
     case = G.Case(cfg)
     y1, ids1, _ = case.run()
     perm = torch.tensor([2, 0, 3, 1], device="cuda")
