@@ -88,7 +88,6 @@ struct Params {
     int scl_sh, scl_rt;  // of these sizes in bytes (0: none)
     int gu_ksplit;       // MXFP4 slice mode: (tile, stage) items with partials in the staging area
     int gu_part;         // matrix-core gate/up: float offset of the partials in the staging area (-1: none)
-    int sh_gu_mfma;      // MXFP4: the shared expert's gate/up rows on the matrix cores too
     int router_flags;    // MOE_ROUTER_NORM | MOE_ROUTER_BIAS
     float norm_eps;
     const void* norm_w;  // [H] activation format

@@ -1327,7 +1327,7 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
 // workgroup has few tiles (9 tiles of 2 stages on 8 waves: 3 stages at most per wave, not 4).  Each
 // item's partial g and v go to `part`; after a barrier the stages of a tile are summed in stage
 // order and silu(g) * v is staged as above.  Every wave of the workgroup must call this.
-template <int NQ, bool WIDE, bool SH = false>
+template <int NQ, bool WIDE>
 __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* xs, int nloc,
                                                const LDS uint32_t* s_mask, const LDS int* s_exp, LDS float* cst,
                                                LDS float* part) {
@@ -1340,11 +1340,9 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
     // this wave's steps: items wave, wave + kWaves, ... (split), or all stages of tiles wave,
     // wave + kWaves, ...
     const int nsteps = ks ? n_strided(nloc * nstage, wave, kWaves) : n_strided(nloc, wave, kWaves) * nstage;
-    const uint8_t* mat = SH ? (r < 8 ? (const uint8_t*)p.w.sh_gate : (const uint8_t*)p.w.sh_up)
-                            : (r < 8 ? (const uint8_t*)p.w.gate : (const uint8_t*)p.w.up);
-    const uint8_t* mats = SH ? (r < 8 ? p.w.sh_gate_s : p.w.sh_up_s) : (r < 8 ? p.w.gate_s : p.w.up_s);
-    // the token mask of a flat row: the unit's, or every token for the shared expert
-    auto row_mask = [&](int64_t f) -> uint32_t { return SH ? (1u << M) - 1u : s_mask[(int)f / I]; };
+    const uint8_t* mat = r < 8 ? (const uint8_t*)p.w.gate : (const uint8_t*)p.w.up;
+    const uint8_t* mats = r < 8 ? p.w.gate_s : p.w.up_s;
+    auto row_mask = [&](int64_t f) -> uint32_t { return s_mask[(int)f / I]; };  // the unit's tokens
     const LDS char* xrow = xs + (int64_t)min(r, M - 1) * p.xpitch;  // columns past M are dropped
     // local tile and stage of this wave's step t; a local tile's first flat row and staging slot
     auto tile_of = [&](int t, int& i, int& sg) {
@@ -1376,11 +1374,8 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
         int j, sg;
         tile_of(t, j, sg);
         const int64_t f = tile_row(j) + (dummy ? 0 : (r & 7));
-        int64_t row = f;  // the shared expert's rows are the flat rows
-        if constexpr (!SH) {
-            const int u = (int)f / I;
-            row = (int64_t)s_exp[u] * I + (f - (int64_t)u * I);
-        }
+        const int u = (int)f / I;
+        const int64_t row = (int64_t)s_exp[u] * I + (f - (int64_t)u * I);
         const uint8_t* w = (dummy ? (const uint8_t*)p.w.gate : mat) + row * rb;
         const uint8_t* sc = (dummy ? p.w.gate_s : mats) + row * sb;
 #pragma unroll
@@ -1500,7 +1495,7 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
     }
 }
 
-// Routed (SH: shared) gate/up rows on the matrix cores, for MXFP4 and FP8 weights.  The
+// Routed gate/up rows on the matrix cores, for MXFP4 and FP8 weights.  The
 // workgroup's tasks are nloc tiles of 8 consecutive rows of the flattened (unit, row) list (local
 // tile i = rows 8 (b + i G) .. + 7).  A tile is one 16-row A operand: the 8 gate rows (A rows 0..7)
 // and the same 8 up rows (A rows 8..15).  B holds the rows x of all M tokens (column n = token n,
@@ -1534,7 +1529,7 @@ __device__ __forceinline__ void gateup_mfma_mx(const Params& p, const LDS char* 
 // goes to cst[(8 i + s) * M + n].  trb: kWaves LDS buffers of 4 KB.  Every wave of the workgroup
 // must call this.
 template <int WF>
-__device__ __forceinline__ void gateup_mfma(const Params& p, bool SH, const LDS char* xs, int nloc,
+__device__ __forceinline__ void gateup_mfma(const Params& p, const LDS char* xs, int nloc,
                                             const LDS uint32_t* s_mask, const LDS int* s_exp, LDS float* cst,
                                             LDS float* part, LDS char* trb) {
     static_assert(WF == MOE_FMT_MXFP4 || WF == MOE_FMT_FP8, "4- and 8-bit weights");
@@ -1543,7 +1538,6 @@ __device__ __forceinline__ void gateup_mfma(const Params& p, bool SH, const LDS 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r = lane & 15, kq = lane >> 4;
     const int H = p.H, I = p.I, M = p.M, G = gridDim.x, b = blockIdx.x;
-    const int RI = SH ? p.Is : I;                // rows of one matrix
     const int64_t rb = MX ? H / 2 : H;           // bytes of a row
     const int nch = (int)(rb / 16);              // 16-byte chunks of a row
     const int nstage = (nch + 15) / 16;          // stages of 16 chunks
@@ -1566,21 +1560,16 @@ __device__ __forceinline__ void gateup_mfma(const Params& p, bool SH, const LDS 
         }
     };
     LDS char* tb = trb + wave * 4096;
-    const uint8_t* gmat = (const uint8_t*)(SH ? p.w.sh_gate : p.w.gate);
-    const uint8_t* umat = (const uint8_t*)(SH ? p.w.sh_up : p.w.up);
-    const uint8_t* gsc = SH ? p.w.sh_gate_s : p.w.gate_s;
-    const uint8_t* usc = SH ? p.w.sh_up_s : p.w.up_s;
-    auto row_mask = [&](int64_t f) -> uint32_t { return SH ? (1u << M) - 1u : s_mask[(int)f / I]; };
+    const uint8_t* gmat = (const uint8_t*)p.w.gate;
+    const uint8_t* umat = (const uint8_t*)p.w.up;
+    const uint8_t* gsc = p.w.gate_s;
+    const uint8_t* usc = p.w.up_s;
+    auto row_mask = [&](int64_t f) -> uint32_t { return s_mask[(int)f / I]; };  // the unit's tokens
     // expert and row within it of flat row f
     auto locate = [&](int64_t f, int64_t& e, int64_t& rl) {
-        if (SH) {
-            e = 0;
-            rl = f;
-        } else {
-            const int u = (int)f / I;
-            e = s_exp[u];
-            rl = f - (int64_t)u * I;
-        }
+        const int u = (int)f / I;
+        e = s_exp[u];
+        rl = f - (int64_t)u * I;
     };
     const LDS char* xrow = xs + (int64_t)min(r, M - 1) * p.xpitch;  // columns past M are dropped
     auto tile_row = [&](int i) { return (int64_t)(b + i * G) * 8; };
@@ -1605,10 +1594,10 @@ __device__ __forceinline__ void gateup_mfma(const Params& p, bool SH, const LDS 
         for (int q = 0; q < 4; ++q) {
             const int a = dummy ? 0 : 4 * q + kq;
             st.c[q] = __builtin_nontemporal_load(
-                (const u32x4*)((a < 8 ? gmat : umat) + (e * RI + rl + (a & 7)) * rb + 16 * ch));
+                (const u32x4*)((a < 8 ? gmat : umat) + (e * I + rl + (a & 7)) * rb + 16 * ch));
         }
         if constexpr (MX) {
-            const uint8_t* sc = (r < 8 || dummy ? gsc : usc) + (e * RI + rl + (dummy ? 0 : (r & 7))) * sb;
+            const uint8_t* sc = (r < 8 || dummy ? gsc : usc) + (e * I + rl + (dummy ? 0 : (r & 7))) * sb;
             if (WIDE) {
                 st.s = __builtin_nontemporal_load((const u32x4*)(sc + (dummy ? 0 : 16 * sg)));
             } else {
@@ -1616,7 +1605,7 @@ __device__ __forceinline__ void gateup_mfma(const Params& p, bool SH, const LDS 
                 for (int q = 0; q < 4; ++q) st.s[q] = sc[dummy ? 0 : min(16 * sg + 4 * q + kq, (int)sb - 1)];
             }
         } else {
-            const float* srow = (const float*)scale_row<WF>(scale_mat<WF>(kq < 2 || dummy ? gsc : usc, e, RI, H), rl, H);
+            const float* srow = (const float*)scale_row<WF>(scale_mat<WF>(kq < 2 || dummy ? gsc : usc, e, I, H), rl, H);
             st.s[0] = __float_as_uint(srow[dummy ? 0 : min(2 * sg, nsb - 1)]);
             st.s[1] = __float_as_uint(srow[dummy ? 0 : min(2 * sg + 1, nsb - 1)]);
             st.s[2] = st.s[3] = 0u;
@@ -2379,39 +2368,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     //      results go straight to the workspace and are counted after the routing barrier ----
     int sh_rows = 0;
     int sh_waves = 0;  // waves kWaves - sh_waves .. kWaves - 1 have shared gate/up tasks
-    bool sh_done = false;
-    if constexpr (WF == MOE_FMT_MXFP4 || WF == MOE_FMT_FP8) {
-        // MXFP4 and FP8 from 8 tokens on: tiles of 8 shared rows on the matrix cores (on the vector
-        // ALU every code would be decoded once per token, and at 16 tokens one 4-row task outlasts
-        // the routing)
-        if (has_sh && !p.route_only && p.sh_gu_mfma) {
-            const int nloc = n_strided(Is / 8, b, G);
-            if (nloc > 0) {
-                if constexpr (WF == MOE_FMT_MXFP4 && SLICE) {
-                    if ((H / 32) % 16 == 0)
-                        gateup_mfma_mx<10, true, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
-                    else
-                        gateup_mfma_mx<10, false, true>(p, xs, nloc, nullptr, nullptr, cst, nullptr);
-                } else {
-                    gateup_mfma<WF>(p, true, xs, nloc, nullptr, nullptr, cst, p.gu_part >= 0 ? cst + p.gu_part : nullptr,
-                                    trb);
-                }
-            }
-            __syncthreads();
-            for (int i = threadIdx.x; i < nloc * 8 * M; i += kThreads) {
-                const int sl = i / M, m = i - sl * M;
-                const int64_t o = (int64_t)(NP + m) * p.act_stride + (int64_t)(b + (sl / 8) * G) * 8 + sl % 8;
-                if (bf_act)
-                    st_dev_bf16(act_rs, (uint32_t)(o * 2), cst[i]);
-                else
-                    st_dev(p.ws.act + o, cst[i]);
-            }
-            __syncthreads();  // the staging area is the routing scratch next
-            sh_rows = nloc * 8;
-            sh_done = true;
-        }
-    }
-    if (has_sh && !p.route_only && !sh_done) {
+    if (has_sh && !p.route_only) {
         const int T = Is / RTG;  // a contiguous range of tasks per workgroup
         const int qa = T * b / G, qb = T * (b + 1) / G;
         sh_rows = (qb - qa) * RTG;
@@ -2515,7 +2472,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 }
             } else if constexpr (WF == MOE_FMT_MXFP4 || WF == MOE_FMT_FP8) {
                 if (nloc > 0)
-                    gateup_mfma<WF>(p, false, xs, nloc, s_mask, s_exp, cst, p.gu_part >= 0 ? cst + p.gu_part : nullptr, trb);
+                    gateup_mfma<WF>(p, xs, nloc, s_mask, s_exp, cst, p.gu_part >= 0 ? cst + p.gu_part : nullptr, trb);
             }
             __syncthreads();
             MOE_TRACE(6);
@@ -3050,7 +3007,9 @@ hipError_t plan_t(Params& p, int G) {
     // FP8 from 3 tokens on (at one token the vector path decodes each code once anyway, and 15 of
     // the 16 token columns of a product would be empty: 34.0 against 31.8 us at Ling width)
     p.gu_mfma = (WF == MOE_FMT_MXFP4 || (WF == MOE_FMT_FP8 && M >= 3)) ? 1 : 0;
-    p.sh_gu_mfma = (WF == MOE_FMT_MXFP4 || WF == MOE_FMT_FP8) && M >= 8 && p.Is % 8 == 0 ? 1 : 0;  // the shared expert's too
+    // The shared expert's gate/up stays on the vector path at every token count: its rows run while
+    // the routing is still pending, and on the matrix cores at 16 tokens the layer took longer
+    // (FP8 136.0 against 129.7 us, MXFP4 106.3 against 103.9 us)
     // per-token cost of a down row (a row's bytes cost kCostBase = 8), from sweeps of the
     // whole-layer time: bf16 over 0, 1, 2, 3, 4 and 6 at 6 and 16 tokens (3 is fastest at both);
     // MXFP4 over 1, 3, 6, 9 and 14 at 16 tokens (6 is fastest: the vector path decodes every
@@ -3119,7 +3078,7 @@ hipError_t plan_t(Params& p, int G) {
             if (p.slice_mfma && (p.I / 32) % 4 == 0) p.scl_rt = (int)round16(units * nown * (p.I / 32));
         }
         p.lds_tr = p.lds_scl + p.scl_sh + p.scl_rt;
-        p.lds_dn = p.lds_tr + ((p.gu_mfma || p.sh_gu_mfma) && !mx_items && !p.route_only ? kWaves * 4096 : 0);
+        p.lds_dn = p.lds_tr + (p.gu_mfma && !mx_items && !p.route_only ? kWaves * 4096 : 0);
         if (pass == 0 && p.lds_dn > budget && cst_nopart >= 0) {  // no room for the partial tiles
             p.gu_part = -1;
             p.cst_bytes = round16(std::max<int64_t>(cst_nopart, cst_min));
