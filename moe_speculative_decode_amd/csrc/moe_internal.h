@@ -64,7 +64,8 @@ struct Params {
     // LDS layout, byte offsets from the dynamic LDS base (filled by launch_layer)
     int lds_tab, lds_x, lds_cst, lds_sh, lds_ysh, lds_dn, lds_total;
     int lds_tr;       // matrix-core gate/up: kWaves transpose buffers of 4 KB
-    int cst_bytes;    // staging area (routing scratch, SwiGLU results, down partials)
+    int lds_sel;      // routing scratch (the head of the slice-mode down window while it is empty, else cst)
+    int cst_bytes;    // staging area (SwiGLU results, down partials; the routing scratch unless lds_sel is elsewhere)
     int dn_bytes;     // slice mode: routed down-row window
     int slice_mode;   // 1: every workgroup computes its y slice of every routed unit (small M*k)
     int slice_mfma;   // 1: slice mode on the matrix cores (bfloat16 SwiGLU rows, swizzled windows)

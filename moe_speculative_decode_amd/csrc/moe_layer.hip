@@ -2396,7 +2396,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     // ---- B: routing barrier, top-k and compaction in every workgroup ----
     // the published expert pairs are polled by the highest wave without shared gate/up tasks (those
     // run on the vector ALU and, at 16 tokens with E2M1 decode, would hold the poll back by µs)
-    const int U = route_and_compact(p, tab, (LDS char*)cst, b == 0, call + 1u,
+    const int U = route_and_compact(p, tab, lds + p.lds_sel, b == 0, call + 1u,
                                     sh_waves >= kWaves ? kWaves - 1 : kWaves - 1 - sh_waves, fault);
     MOE_TRACE(5);
     if (p.route_only) {
@@ -3032,7 +3032,7 @@ hipError_t plan_t(Params& p, int G) {
         const int64_t pbytes = tiles * nstage * 16 * M * 4;
         p.gu_ksplit = pbytes <= 16 * 1024 ? 1 : 0;
         p.gu_part = (int)(tiles * 8 * M);
-        cst = std::max<int64_t>(kSelBytes, tiles * 8 * M * 4 + (p.gu_ksplit ? pbytes : 0));
+        cst = tiles * 8 * M * 4 + (p.gu_ksplit ? pbytes : 0);
         p.gu_cap = 0;
     } else if (p.gu_mfma) {
         // tiles of 8 rows per workgroup; (tile, stage) steps split into contiguous ranges per wave
@@ -3041,8 +3041,8 @@ hipError_t plan_t(Params& p, int G) {
         // expert's gate/up, at most one tile per workgroup, uses the same areas); dropped below if
         // the LDS budget has no room for them
         p.gu_part = (int)(tiles * 8 * M);
-        cst = std::max<int64_t>(kSelBytes, tiles * 8 * M * 4 + (int64_t)kWaves * 2 * M * 64);
-        cst_nopart = std::max<int64_t>(kSelBytes, tiles * 8 * M * 4);
+        cst = tiles * 8 * M * 4 + (int64_t)kWaves * 2 * M * 64;
+        cst_nopart = tiles * 8 * M * 4;
         p.gu_cap = 0;
     } else {
         const int64_t rtg = rt_gate<WF>();
@@ -3050,10 +3050,9 @@ hipError_t plan_t(Params& p, int G) {
         const int64_t Rs = 7 * T / (80 * (int64_t)G), dyn = T - (int64_t)kWaves * G * Rs;
         const int64_t ch = std::max<int64_t>(1, 20480 / (2 * rtg * row_bytes<WF>(H)));
         p.gu_cap = (int)(Rs + 2 * ((dyn + kWaves * G - 1) / (kWaves * G)) + 2 * ch + 5);
-        cst = std::max<int64_t>(kSelBytes, (int64_t)kWaves * p.gu_cap * (rtg * M * 4 + 4) + kWaves * 4);
+        cst = (int64_t)kWaves * p.gu_cap * (rtg * M * 4 + 4) + kWaves * 4;
     }
     const int64_t cst_min = p.slice_mode ? (NP + M) * nown * 4 : 16 * 1024;
-    cst = std::max<int64_t>(cst, cst_min);
     // token rows 16 bytes further apart than their size: the 16 token columns of a matrix-core B
     // operand then start in 16 different bank groups
     p.xpitch = H * XB + 16;
@@ -3063,32 +3062,43 @@ hipError_t plan_t(Params& p, int G) {
     p.lds_x = round16(kTabWords * 4);
     p.lds_cst = p.lds_x + round16(xb);
     const int budget = kLdsBudget;
-    p.cst_bytes = round16(cst);
-    // the fixed regions; a second pass without the partial tiles if they do not fit
-    for (int pass = 0;; ++pass) {
-        p.lds_sh = p.lds_cst + p.cst_bytes;
-        p.lds_ysh = p.lds_sh + round16(p.Is > 0 ? nown * row_bytes<WF>(p.Is) : 0);
-        p.lds_scl = p.lds_ysh + round16((int64_t)M * nown * 4);
-        // MXFP4 scales of the slice rows in LDS (copied in 4-byte pieces: whole dwords per row
-        // block): the shared expert's when its down rows run on the matrix cores, the routed units'
-        // in slice mode
-        p.scl_sh = p.scl_rt = 0;
-        if constexpr (WF == MOE_FMT_MXFP4) if (!p.route_only) {
-            if (p.sh_mfma && p.Is > 0 && (p.Is / 32) % 4 == 0) p.scl_sh = (int)round16((int64_t)nown * (p.Is / 32));
-            if (p.slice_mfma && (p.I / 32) % 4 == 0) p.scl_rt = (int)round16(units * nown * (p.I / 32));
+    const int gu_part0 = p.gu_part;
+    // The routing scratch sits at the head of the slice-mode down window, which stays empty until
+    // the routing has finished (at one bf16 token the window then holds all eight units' slices,
+    // not seven); without a window, or one too small for it, it is part of the staging area.
+    for (int sel_win = p.slice_mode && !p.route_only ? 1 : 0;; sel_win = 0) {
+        const int64_t floor = std::max<int64_t>(cst_min, sel_win ? 0 : kSelBytes);
+        p.gu_part = gu_part0;
+        p.cst_bytes = round16(std::max<int64_t>(cst, floor));
+        // the fixed regions; a second pass without the partial tiles if they do not fit
+        for (int pass = 0;; ++pass) {
+            p.lds_sh = p.lds_cst + p.cst_bytes;
+            p.lds_ysh = p.lds_sh + round16(p.Is > 0 ? nown * row_bytes<WF>(p.Is) : 0);
+            p.lds_scl = p.lds_ysh + round16((int64_t)M * nown * 4);
+            // MXFP4 scales of the slice rows in LDS (copied in 4-byte pieces: whole dwords per row
+            // block): the shared expert's when its down rows run on the matrix cores, the routed
+            // units' in slice mode
+            p.scl_sh = p.scl_rt = 0;
+            if constexpr (WF == MOE_FMT_MXFP4) if (!p.route_only) {
+                if (p.sh_mfma && p.Is > 0 && (p.Is / 32) % 4 == 0) p.scl_sh = (int)round16((int64_t)nown * (p.Is / 32));
+                if (p.slice_mfma && (p.I / 32) % 4 == 0) p.scl_rt = (int)round16(units * nown * (p.I / 32));
+            }
+            p.lds_tr = p.lds_scl + p.scl_sh + p.scl_rt;
+            p.lds_dn = p.lds_tr + (p.gu_mfma && !mx_items && !p.route_only ? kWaves * 4096 : 0);
+            if (pass == 0 && p.lds_dn > budget && cst_nopart >= 0) {  // no room for the partial tiles
+                p.gu_part = -1;
+                p.cst_bytes = round16(std::max<int64_t>(cst_nopart, floor));
+                continue;
+            }
+            break;
         }
-        p.lds_tr = p.lds_scl + p.scl_sh + p.scl_rt;
-        p.lds_dn = p.lds_tr + (p.gu_mfma && !mx_items && !p.route_only ? kWaves * 4096 : 0);
-        if (pass == 0 && p.lds_dn > budget && cst_nopart >= 0) {  // no room for the partial tiles
-            p.gu_part = -1;
-            p.cst_bytes = round16(std::max<int64_t>(cst_nopart, cst_min));
-            continue;
-        }
+        // slice mode: the rest of LDS is the window its routed down rows stream into (unit-major
+        // down rows stream from global memory)
+        p.dn_bytes = (p.route_only || !p.slice_mode) ? 0 : std::max(0, (budget - p.lds_dn) / 16 * 16);
+        if (sel_win && p.dn_bytes < kSelBytes) continue;
+        p.lds_sel = sel_win ? p.lds_dn : p.lds_cst;
         break;
     }
-    // slice mode: the rest of LDS is the window its routed down rows stream into (unit-major down
-    // rows stream from global memory)
-    p.dn_bytes = (p.route_only || !p.slice_mode) ? 0 : std::max(0, (budget - p.lds_dn) / 16 * 16);
     p.lds_total = p.lds_dn + p.dn_bytes;
     if (p.lds_total > budget) return hipErrorInvalidValue;
     return hipSuccess;
