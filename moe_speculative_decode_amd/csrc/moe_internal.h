@@ -85,8 +85,8 @@ struct Params {
     float* topk_w;
     moe_dispatch_t disp;
     Workspace ws;
-    int lds_scl;         // MXFP4: LDS scale windows (shared expert, then routed units) at this offset,
-    int scl_sh, scl_rt;  // of these sizes in bytes (0: none)
+    int lds_scl;         // MXFP4: LDS scale window of the shared expert's slice rows at this offset,
+    int scl_sh;          // of this size in bytes (0: none)
     int gu_ksplit;       // MXFP4 slice mode: (tile, stage) items with partials in the staging area
     int gu_part;         // matrix-core gate/up: float offset of the partials in the staging area (-1: none)
     int router_flags;    // MOE_ROUTER_NORM | MOE_ROUTER_BIAS

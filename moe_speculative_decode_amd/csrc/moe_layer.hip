@@ -2290,10 +2290,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     LDS float* ysh = (LDS float*)(lds + p.lds_ysh);
     LDS char* dnw = lds + p.lds_dn;
     LDS char* trb = lds + p.lds_tr;     // the waves' transpose buffers of the matrix-core gate/up
-    // MXFP4 scales of the slice rows in LDS (the shared expert's, and the routed units' in slice
-    // mode), or null
+    // MXFP4 scale bytes of the shared expert's slice rows in LDS, or null
     const LDS uint8_t* sclw_sh = WF == MOE_FMT_MXFP4 && p.scl_sh ? (const LDS uint8_t*)(lds + p.lds_scl) : nullptr;
-    const LDS uint8_t* sclw = WF == MOE_FMT_MXFP4 && p.scl_rt ? (const LDS uint8_t*)(lds + p.lds_scl) + p.scl_sh : nullptr;
     __shared__ uint32_t s_call, s_spin;
     MOE_TRACE_INIT;
     MOE_TRACE(0);
@@ -2417,15 +2415,13 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     int64_t d0 = 0, d1 = 0;  // unit-major: this workgroup's (unit, row) range, split by cost
     if constexpr (!SLICE) cost_split(s_mask, U, H, kCostBase, p.cost_dn, G, b, &d0, &d1);
     int nfit = 0;  // slice mode: units whose slice rows are in the window
-    // The window streams in after this workgroup's gate/up rows have been published (during the
-    // wait for the other workgroups) for bf16 and FP8 weights: issued before them, it would sit
-    // ahead of the gate/up loads in every wave's in-order memory counter and delay the whole phase
-    // (bf16 at one token: 0.8 us; FP8: 1.3 us).  The 4-bit MXFP4 window is small, and its matrix-
-    // core down rows are fast enough that waiting for a late window costs more (2.3 us at one
-    // token, 2.9 at six): it is issued here, before C (issued behind the first gate/up stages
-    // instead: +1 us at one token).  Unit-major down rows stream from global memory inside the down
-    // phase (an LDS prefetch of them issued here cost ~1 us at six tokens).
-    const bool late_window = WF == MOE_FMT_FP8 || (mf_slice && WF == MOE_FMT_BF16);
+    // Slice mode keeps an LDS window of down rows for bf16 (and f32) weights only.  With bf16 on
+    // the matrix cores the window streams in after this workgroup's gate/up rows have been
+    // published (during the wait for the other workgroups): issued before them, it would sit ahead
+    // of the gate/up loads in every wave's in-order memory counter and delay the whole phase (0.8 us
+    // at one token).  Unit-major down rows stream from global memory inside the down phase (an LDS
+    // prefetch of them issued here cost ~1 us at six tokens).
+    const bool late_window = WF == MOE_FMT_BF16 && mf_slice;
     auto slice_window = [&]() {
         if (nown > 0) {
             // a unit's slice is a few instructions: each unit starts on the wave after the last
@@ -2437,13 +2433,6 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     async_rows_to_lds((char*)(dnw + (int64_t)u * nown * rbI), src, (int)(nown * rbI), (int)rbI, u * per);
                 else
                     async_to_lds((char*)(dnw + (int64_t)u * nown * rbI), src, (int)(nown * rbI), u * per);
-            }
-            if (sclw) {
-                const int pers = (nown * (I / 32) + 255) / 256;
-                for (int u = 0; u < U; ++u)
-                    async_dwords_to_lds((char*)(sclw + (int64_t)u * nown * (I / 32)),
-                                        p.w.down_s + ((int64_t)s_exp[u] * H + h0) * (I / 32), nown * (I / 32),
-                                        nfit * per + u * pers);
             }
         }
     };
@@ -2629,10 +2618,6 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     };
     if constexpr (!SLICE)
         if (has_sh && nown > 0) shared_down();
-    if (SLICE && late_window && !mf_slice) {  // the vector path reads window rows before its wait
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
     MOE_TRACE(8);
 
     if constexpr (SLICE) {
@@ -2704,7 +2689,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                             t.w = t.lds ? (const uint8_t*)(dnw + (int64_t)u * nown * rbI)
                                         : (const uint8_t*)p.w.down + (e * H + h0) * rbI;
                             t.s = WF == MOE_FMT_MXFP4 ? p.w.down_s + (e * H + h0) * (I / 32) : nullptr;
-                            if constexpr (WF == MOE_FMT_MXFP4) t.sl = sclw ? sclw + (int64_t)u * nown * (I / 32) : nullptr;
+                            if constexpr (WF == MOE_FMT_MXFP4) t.sl = nullptr;  // routed scale bytes from global memory
                         } else {
                             t.prow = NP;
                             t.t = M;
@@ -3066,7 +3051,13 @@ hipError_t plan_t(Params& p, int G) {
     // The routing scratch sits at the head of the slice-mode down window, which stays empty until
     // the routing has finished (at one bf16 token the window then holds all eight units' slices,
     // not seven); without a window, or one too small for it, it is part of the staging area.
-    for (int sel_win = p.slice_mode && !p.route_only ? 1 : 0;; sel_win = 0) {
+    // slice mode keeps an LDS window of routed down rows for bf16 and f32 weights; MXFP4 and FP8
+    // slice rows are read from global memory in the down phase (their windows were copied one unit
+    // at a time, each copy waiting for the last, and the MXFP4 gate/up waited for the whole window:
+    // without them MXFP4 took 24.2 against 26.0 us at one token and 44.5 against 45.8 at six, FP8
+    // 28.0 against 28.4 at one token)
+    const bool win = p.slice_mode && !p.route_only && (WF == MOE_FMT_BF16 || WF == MOE_FMT_F32);
+    for (int sel_win = win ? 1 : 0;; sel_win = 0) {
         const int64_t floor = std::max<int64_t>(cst_min, sel_win ? 0 : kSelBytes);
         p.gu_part = gu_part0;
         p.cst_bytes = round16(std::max<int64_t>(cst, floor));
@@ -3075,15 +3066,13 @@ hipError_t plan_t(Params& p, int G) {
             p.lds_sh = p.lds_cst + p.cst_bytes;
             p.lds_ysh = p.lds_sh + round16(p.Is > 0 ? nown * row_bytes<WF>(p.Is) : 0);
             p.lds_scl = p.lds_ysh + round16((int64_t)M * nown * 4);
-            // MXFP4 scales of the slice rows in LDS (copied in 4-byte pieces: whole dwords per row
-            // block): the shared expert's when its down rows run on the matrix cores, the routed
-            // units' in slice mode
-            p.scl_sh = p.scl_rt = 0;
-            if constexpr (WF == MOE_FMT_MXFP4) if (!p.route_only) {
-                if (p.sh_mfma && p.Is > 0 && (p.Is / 32) % 4 == 0) p.scl_sh = (int)round16((int64_t)nown * (p.Is / 32));
-                if (p.slice_mfma && (p.I / 32) % 4 == 0) p.scl_rt = (int)round16(units * nown * (p.I / 32));
-            }
-            p.lds_tr = p.lds_scl + p.scl_sh + p.scl_rt;
+            // MXFP4 scale bytes of the shared expert's slice rows in LDS when its down rows run on
+            // the matrix cores (copied in 4-byte pieces: whole dwords per row block)
+            p.scl_sh = 0;
+            if constexpr (WF == MOE_FMT_MXFP4)
+                if (!p.route_only && p.sh_mfma && p.Is > 0 && (p.Is / 32) % 4 == 0)
+                    p.scl_sh = (int)round16((int64_t)nown * (p.Is / 32));
+            p.lds_tr = p.lds_scl + p.scl_sh;
             p.lds_dn = p.lds_tr + (p.gu_mfma && !mx_items && !p.route_only ? kWaves * 4096 : 0);
             if (pass == 0 && p.lds_dn > budget && cst_nopart >= 0) {  // no room for the partial tiles
                 p.gu_part = -1;
@@ -3094,7 +3083,7 @@ hipError_t plan_t(Params& p, int G) {
         }
         // slice mode: the rest of LDS is the window its routed down rows stream into (unit-major
         // down rows stream from global memory)
-        p.dn_bytes = (p.route_only || !p.slice_mode) ? 0 : std::max(0, (budget - p.lds_dn) / 16 * 16);
+        p.dn_bytes = win ? std::max(0, (budget - p.lds_dn) / 16 * 16) : 0;
         if (sel_win && p.dn_bytes < kSelBytes) continue;
         p.lds_sel = sel_win ? p.lds_dn : p.lds_cst;
         break;

@@ -34,7 +34,7 @@ SMALL = [
     small("mxfp4_m16", MXFP4, H=544, I=224, Is=96, lens=(9, 7)),
     # all pair rows do not fit in LDS as bf16 -> unit-major down rows for MXFP4 (vector path)
     small("mxfp4_m16_unit_major", MXFP4, H=512, E=256, k=8, I=768, Is=128, lens=(16,)),
-    # MXFP4 slice mode with the scale windows in LDS (I / 32 a multiple of 4) and two requests
+    # MXFP4 slice mode with the shared expert's scale bytes in LDS (Is / 32 a multiple of 4) and two requests
     small("mxfp4_m6_scale_window", MXFP4, H=512, E=128, k=8, I=256, Is=128, lens=(2, 4)),
     small("f32_m3", F32, H=256, E=32, k=3, I=96, Is=64, lens=(3,)),
     small("bf16_no_shared", Is=0, lens=(4,)),
