@@ -88,6 +88,7 @@ struct Params {
     int lds_scl;         // MXFP4: LDS scale window of the shared expert's slice rows at this offset,
     int scl_sh;          // of this size in bytes (0: none)
     int gu_ksplit;       // MXFP4 slice mode: (tile, stage) items with partials in the staging area
+    int gu_items;        // MXFP4 slice mode: the whole-item matrix-core gate/up (else the line form)
     int gu_part;         // matrix-core gate/up: float offset of the partials in the staging area (-1: none)
     int router_flags;    // MOE_ROUTER_NORM | MOE_ROUTER_BIAS
     float norm_eps;

@@ -1306,9 +1306,9 @@ __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, 
         [&](int i, int, GUTask& t) { info(i, t); }, out);
 }
 
-// Routed gate/up rows on the matrix cores, for MXFP4 weights in slice mode (one or a few tokens:
-// a wave has one or two (tile, stage) items, and whole 10 KB items issued at once beat the
-// line-wise stages of gateup_mfma below there).  The workgroup's tasks are nloc
+// Routed gate/up rows on the matrix cores, for MXFP4 weights in slice mode from three tokens on (a
+// wave has a few (tile, stage) items, and whole 10 KB items issued at once beat the line-wise
+// stages of gateup_mfma below there; at one token the line-wise form is faster).  The workgroup's tasks are nloc
 // tiles of 8 consecutive rows of the flattened (unit, row) list (local tile i = rows 8 (b + i G) ..
 // + 7), dealt to its waves round robin.  A tile is one 16-row A operand: the 8 gate rows (A rows
 // 0..7) and the same 8 up rows (A rows 8..15).
@@ -2451,7 +2451,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             // tiles of 8 rows dealt to the workgroups round robin
             const int nloc = n_strided((int)(nrows / 8), b, G);
             MOE_TRACE(22);
-            if constexpr (WF == MOE_FMT_MXFP4 && SLICE) {
+            if (WF == MOE_FMT_MXFP4 && SLICE && p.gu_items) {
                 if (nloc > 0) {
                     LDS float* part = p.gu_ksplit ? cst + p.gu_part : nullptr;
                     if ((H / 32) % 16 == 0)
@@ -3006,9 +3006,12 @@ hipError_t plan_t(Params& p, int G) {
     const int64_t units = std::min<int64_t>(NP, p.E);
     int64_t cst, cst_nopart = -1;
     p.gu_part = -1;
-    // MXFP4 slice mode keeps its gate/up rows in whole-item form (gateup_mfma_mx); the other
-    // matrix-core gate/up runs through the line-wise form with its transpose buffers
-    const bool mx_items = WF == MOE_FMT_MXFP4 && p.slice_mode;
+    // MXFP4 slice mode from three tokens on keeps its gate/up rows in whole-item form
+    // (gateup_mfma_mx); the other matrix-core gate/up runs through the line-wise form with its
+    // transpose buffers (MXFP4 at one token: 23.0 against 24.2 us; at six tokens the item form is
+    // faster, 43.4 against 44.2 us)
+    const bool mx_items = WF == MOE_FMT_MXFP4 && p.slice_mode && M >= 3;
+    p.gu_items = mx_items ? 1 : 0;
     p.gu_ksplit = 0;
     if (p.gu_mfma && mx_items) {
         // tiles of 8 rows dealt round robin; (tile, stage) items with partials in LDS while they fit

@@ -30,6 +30,7 @@ SMALL = [
     small("bf16_m16_ragged", lens=(3, 1, 7, 5)),
     small("bf16_tail", H=520, I=200, Is=72, lens=(6,)),
     small("mxfp4_m1", MXFP4, lens=(1,), recipe="iid"),
+    small("mxfp4_m2", MXFP4, lens=(2,)),  # slice mode, line-form matrix-core gate/up (below three tokens)
     small("mxfp4_m6", MXFP4, lens=(6,)),
     small("mxfp4_m16", MXFP4, H=544, I=224, Is=96, lens=(9, 7)),
     # all pair rows do not fit in LDS as bf16 -> unit-major down rows for MXFP4 (vector path)
