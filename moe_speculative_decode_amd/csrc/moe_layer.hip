@@ -1850,10 +1850,12 @@ struct DNTask {
 };
 
 // This wave's tasks n = wslot, wslot + kWaves, ... < ntask of a flattened down-row list described by
-// info(n, task); the source of each task (LDS or HBM) is its own.  Same pipelining as down_run:
-// the first task is loaded before ready(), and the next task's loads are in flight during the
-// current task's compute.  out(task, row, i, v) receives row `row` of the task for token i.
-template <int WF, int NJD, typename Info, typename Ready, typename Out>
+// info(n, task); the source of each task (LDS or HBM) is its own.  The first task (PRE2: the first
+// two) is loaded before ready(), and the next task's loads are in flight during the current task's
+// compute.  out(task, row, i, v) receives row `row` of the task for token i.  Two tasks ahead of the
+// wait pay where the wait is long against the tasks (slice mode: FP8 at one token 27.2 against
+// 28.5 us) and cost where the tasks are many (unit-major FP8: +0.4 us at six tokens, +1.4 at 16).
+template <int WF, int NJD, bool PRE2, typename Info, typename Ready, typename Out>
 __device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Info info, Ready ready, Out out) {
     constexpr int LPR = Geo<WF>::LPR_D, RL = Geo<WF>::RL_D;
     const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
@@ -1908,25 +1910,53 @@ __device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Inf
             }
         }
     };
-    if (n < ntask) {
-        info(n, ta);
-        load(wa, ta);
-    }
-    ready();
-    if (n >= ntask) return;
-    while (true) {
-        info(min(n + kWaves, ntask - 1), tb);
-        load(wb, tb);
-        settle_all(wa, ta);
-        compute(wa, ta);
-        n += kWaves;
-        if (n >= ntask) break;
-        info(min(n + kWaves, ntask - 1), ta);
-        load(wa, ta);
-        settle_all(wb, tb);
-        compute(wb, tb);
-        n += kWaves;
-        if (n >= ntask) break;
+    if constexpr (PRE2) {
+        // the first two tasks load before ready() (past the list: the last task again, so the
+        // number of loads in flight stays static); then each task's loads go out right after the
+        // compute of the task before the one in flight
+        if (n < ntask) {
+            info(n, ta);
+            load(wa, ta);
+            info(min(n + kWaves, ntask - 1), tb);
+            load(wb, tb);
+        }
+        ready();
+        if (n >= ntask) return;
+        while (true) {
+            settle_all(wa, ta);
+            compute(wa, ta);
+            n += kWaves;
+            if (n >= ntask) break;
+            info(min(n + kWaves, ntask - 1), ta);
+            load(wa, ta);
+            settle_all(wb, tb);
+            compute(wb, tb);
+            n += kWaves;
+            if (n >= ntask) break;
+            info(min(n + kWaves, ntask - 1), tb);
+            load(wb, tb);
+        }
+    } else {
+        if (n < ntask) {
+            info(n, ta);
+            load(wa, ta);
+        }
+        ready();
+        if (n >= ntask) return;
+        while (true) {
+            info(min(n + kWaves, ntask - 1), tb);
+            load(wb, tb);
+            settle_all(wa, ta);
+            compute(wa, ta);
+            n += kWaves;
+            if (n >= ntask) break;
+            info(min(n + kWaves, ntask - 1), ta);
+            load(wa, ta);
+            settle_all(wb, tb);
+            compute(wb, tb);
+            n += kWaves;
+            if (n >= ntask) break;
+        }
     }
 }
 
@@ -2734,7 +2764,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     return;
                 }
             }
-            down_flat<WF, NJD>(nun * nblk, astride, wave_id(), info, ready,
+            down_flat<WF, NJD, true>(nun * nblk, astride, wave_id(), info, ready,
                                [&](const DNTask& t, int row, int i, float v) { pst[(t.prow + i) * nown + t.orow + row] = v; });
             __syncthreads();
             MOE_TRACE(11);
@@ -2841,7 +2871,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 __syncthreads();
                 MOE_TRACE(10);
             };
-            down_flat<WF, NJD>(toff[nseg], I, wave_id(), info, ready, [&](const DNTask& t, int row, int i, float v) {
+            down_flat<WF, NJD, false>(toff[nseg], I, wave_id(), info, ready, [&](const DNTask& t, int row, int i, float v) {
                 pst[t.prow + (t.orow + row) * t.t + i] = v;
             });
             __syncthreads();
