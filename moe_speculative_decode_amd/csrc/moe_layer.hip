@@ -1761,12 +1761,13 @@ __device__ __forceinline__ void gateup_mfma(const Params& p, const LDS char* xs,
 // Down rows [0, nrows) of one unit (row 0 at wbase, in LDS when FROM_LDS; its block scales are those of
 // absolute row srow0 of the scale matrix smat) with K inputs,
 // for the unit's t tokens whose fp32 activations are at acts ([t][K], LDS).  Tasks of RT rows go
-// to the waves round robin, task 0 to the wave whose slot is 0.  `ready()` is called by every wave after its first loads are issued
-// and before any compute (it may contain workgroup barriers).  out(row, i, value) receives each
-// result in the row's last lane.
+// to the waves round robin (every `step`-th task from task `wslot` on; step 1: all of them).
+// `ready()` is called by every wave after its first loads are issued and before any compute (it
+// may contain workgroup barriers).  out(row, i, value) receives each result in the row's last lane.
 template <int WF, int NJD, bool FROM_LDS, typename Ready, typename Out>
 __device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* smat, int64_t srow0, int K, int nrows,
-                                         const LDS float* acts, int t, int wslot, Ready ready, Out out) {
+                                         const LDS float* acts, int t, int wslot, Ready ready, Out out,
+                                         int step = kWaves) {
     constexpr int LPR = Geo<WF>::LPR_D, RL = Geo<WF>::RL_D, RT = rt_down<WF>();
     const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
     const int nch = K / Geo<WF>::EPC;
@@ -1822,15 +1823,15 @@ __device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* sm
     ready();
     if (n >= ntask) return;
     while (true) {
-        load(wb, min(n + kWaves, ntask - 1));
+        load(wb, min(n + step, ntask - 1));
         settle_all(wa);
         compute(wa, n);
-        n += kWaves;
+        n += step;
         if (n >= ntask) break;
-        load(wa, min(n + kWaves, ntask - 1));
+        load(wa, min(n + step, ntask - 1));
         settle_all(wb);
         compute(wb, n);
-        n += kWaves;
+        n += step;
         if (n >= ntask) break;
     }
 }
@@ -2640,9 +2641,14 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             wait_geq(line(set, kLineShared), (uint32_t)Is, fault);
             stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
             __syncthreads();
-            down_run<WF, NJD, true>((const uint8_t*)shw, p.w.sh_down_s, h0, Is, nown, (const LDS float*)xs, M, wave_id(),
-                                    []() {},
-                                    [&](int row, int i, float v) { ysh[i * nown + row] = v; });
+            // the slice's rows make one or two tasks, so the tokens are split over the waves instead:
+            // wave w takes every row for tokens [w tw, w tw + tw) (with the rows dealt to the waves,
+            // two waves ran all 16 tokens and FP8 at 16 tokens spent 12.8 us here)
+            const int tw = (M + kWaves - 1) / kWaves, t0 = min(M, wave_id() * tw), t1 = min(M, t0 + tw);
+            if (t1 > t0)
+                down_run<WF, NJD, true>((const uint8_t*)shw, p.w.sh_down_s, h0, Is, nown,
+                                        (const LDS float*)xs + (int64_t)t0 * Is, t1 - t0, 0, []() {},
+                                        [&](int row, int i, float v) { ysh[(t0 + i) * nown + row] = v; }, 1);
             __syncthreads();
         }
     };
