@@ -2529,10 +2529,12 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             // waves round robin (consecutive rows: whole DRAM pages, contiguous write-out)
             const int sa = P0 * b / G, sbnd = P0 * (b + 1) / G;  // task counts * G < 2^31: 32-bit divisions
             const int ns = n_strided(sbnd - sa, w, kWaves);  // static positions of this wave
-            // consecutive workgroups sit on different XCDs (round robin), so pool b mod npool
-            // gathers workgroups of one XCD (measured: stealing across XCDs costs more than it
-            // evens out)
-            const int npool = max(1, G / 8), pool = b % npool;
+            // consecutive workgroups sit on different XCDs (round robin), so pool b / 8 gathers one
+            // workgroup of every XCD: whole XCDs stream at different rates (up to 15% apart at 16
+            // bf16 tokens, depending on the box and the data), and a pool within one XCD could not
+            // even that out (pools per XCD: the XCDs' gate/up ends 15 us apart at 16 bf16 tokens,
+            // these: 4 us; bf16 16 tokens 181.6 -> 180.3 us, 6 tokens 75.4 -> 74.8 us)
+            const int npool = max(1, G / 8), pool = (b / 8) % npool;
             const int pa = P0 + (T - P0) * pool / npool;
             const int pb = P0 + (T - P0) * (pool + 1) / npool;
             const int64_t rb = row_bytes<WF>(H);
