@@ -844,35 +844,49 @@ __device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, ui
         ce(1, 4), ce(3, 6);
         ce(1, 2), ce(3, 4), ce(5, 6);
     };
-    if (bias)
-        sort8(std::true_type{});
-    else
-        sort8(std::false_type{});
     uint32_t my_key = 0u;  // lane r < k: the selection key of the r-th selected expert
     float my_raw = 0.0f;   // with a bias: its raw logit
     int my_id = 0;
-    for (int r = 0; r < k; ++r) {
-        const uint32_t head = (uint32_t)(c[0] >> 32);
-        const uint32_t K = wave_max_u32(head);
-        const uint64_t ball = __ballot(head == K);
-        const int wl = __builtin_amdgcn_readfirstlane(ball ? __ffsll((unsigned long long)ball) - 1 : 0);
-        const int wi = 7 - __builtin_amdgcn_readlane((int)(uint32_t)c[0], wl);
-        const float wr = bias ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rv[0]), wl)) : 0.0f;
-        if (lane == r) {
-            my_key = K;
-            my_raw = wr;
-            my_id = min(8 * wl + wi, E - 1);
+    // The rounds keep each lane's sorted keys as 32-bit words and the entries' indices as nibbles of
+    // one word (nibble j: the index of the j-th largest), and pop the winning lane without a branch:
+    // every lane selects between its word and the next one, so a round is the wave maximum, two
+    // lane reads and a few independent selects (with the 64-bit list shifted inside a branch on the
+    // winning lane, a round was about 80 instructions and 4 branches).
+    auto rounds = [&](auto with_raw) {
+        constexpr bool RAW = decltype(with_raw)::value;
+        sort8(with_raw);
+        uint32_t key[8], ixw = 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            key[i] = (uint32_t)(c[i] >> 32);
+            ixw |= ((7u - (uint32_t)c[i]) & 7u) << (4 * i);
         }
-        if (lane == wl) {
+        for (int r = 0; r < k; ++r) {
+            const uint32_t K = wave_max_u32(key[0]);
+            const uint64_t ball = __ballot(key[0] == K);  // never empty: K is one lane's head
+            const int wl = __builtin_amdgcn_readfirstlane(ball ? __ffsll((unsigned long long)ball) - 1 : 0);
+            const int wi = __builtin_amdgcn_readlane((int)ixw, wl) & 7;
+            const bool mine = lane == r;
+            my_key = mine ? K : my_key;
+            my_id = mine ? min(8 * wl + wi, E - 1) : my_id;
+            if constexpr (RAW)
+                my_raw = mine ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rv[0]), wl))
+                              : my_raw;
+            const bool w = lane == wl;
 #pragma unroll
-            for (int i = 0; i < 7; ++i) c[i] = c[i + 1];
-            c[7] = 0ull;
-            if (bias) {
+            for (int i = 0; i < 7; ++i) key[i] = w ? key[i + 1] : key[i];
+            key[7] = w ? 0u : key[7];
+            ixw = w ? ixw >> 4 : ixw;
+            if constexpr (RAW) {
 #pragma unroll
-                for (int i = 0; i < 7; ++i) rv[i] = rv[i + 1];
+                for (int i = 0; i < 7; ++i) rv[i] = w ? rv[i + 1] : rv[i];
             }
         }
-    }
+    };
+    if (bias)
+        rounds(std::true_type{});
+    else
+        rounds(std::false_type{});
     float my_v;
     if (bias) {
         my_v = lane < k ? my_raw : -INFINITY;
@@ -2102,6 +2116,7 @@ __device__ __forceinline__ void down_slice_mfma(int nun, int npre, int ng, int n
         load_a(u, std::false_type{});
     }
     ready();
+    MOE_TRACE(27);
     for (; q < nun; q += kWaves) {
         if (q != q0 || !pre) {
             unit_of(q, u);
@@ -2110,7 +2125,9 @@ __device__ __forceinline__ void down_slice_mfma(int nun, int npre, int ng, int n
             else
                 load_a(u, std::true_type{});
         }
+        if (q == q0) MOE_TRACE(28);
         compute(u);
+        if (q == q0) MOE_TRACE(29);
     }
 }
 
@@ -2228,8 +2245,11 @@ __device__ __forceinline__ void down_slice_mfma_mx(int nun, int npre, int nown, 
         load_a(a1, u1);
     }
     ready();
+    MOE_TRACE(27);
     while (q < nun) {
+        if (q < kWaves) MOE_TRACE(28);
         compute(a0, u0);
+        if (q < kWaves) MOE_TRACE(29);
         if (q + 2 * kWaves < nun) {
             unit_of(q + 2 * kWaves, u0);
             load_a(a0, u0);
@@ -2243,6 +2263,7 @@ __device__ __forceinline__ void down_slice_mfma_mx(int nun, int npre, int nown, 
         }
         q += kWaves;
     }
+    MOE_TRACE(30);
 }
 
 // Splits a list of U units of n items each (rows or tasks; item i of unit u has flat index
@@ -2655,9 +2676,11 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         if constexpr ((WF == MOE_FMT_BF16 || WF == MOE_FMT_MXFP4) && NJD <= 3) {
             if (has_sh && nown > 0 && mf_sh && !SLICE) {
                 wait_geq(line(set, kLineShared), (uint32_t)Is, fault);
+                MOE_TRACE(25);
                 const int apitch = 2 * p.act_stride + 16;  // rows 4 banks apart: no conflicts among the B columns
                 stage_rows_bf16((LDS char*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is, apitch);
                 __syncthreads();
+                MOE_TRACE(26);
                 auto unit_of = [&](int, SliceUnit& t) {
                     t.prow = 0;
                     t.t = M;
@@ -2674,8 +2697,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         }
         if (has_sh && nown > 0 && !SLICE && !mf_sh) {
             wait_geq(line(set, kLineShared), (uint32_t)Is, fault);
+            MOE_TRACE(25);
             stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
             __syncthreads();
+            MOE_TRACE(26);
             // the slice's rows make one or two tasks, so the tokens are split over the waves instead:
             // wave w takes every row for tokens [w tw, w tw + tw) (with the rows dealt to the waves,
             // two waves ran all 16 tokens and FP8 at 16 tokens spent 12.8 us here)
