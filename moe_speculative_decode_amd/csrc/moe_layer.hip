@@ -3083,11 +3083,12 @@ hipError_t plan_t(Params& p, int G) {
     // per-token cost of a gate/up task and of a down row relative to the weight bytes (kCostBase),
     // from phase traces: bf16 down rows of 5-token units ran ~1.8x longer than 1-token ones; the
     // decode of E2M1 codes makes MXFP4 rows four times denser in work
-    // MXFP4 gate/up rows on the matrix cores: each code is decoded once for all tokens, so the
-    // work per weight byte no longer grows with the unit's token count
-    // FP8 from 3 tokens on (at one token the vector path decodes each code once anyway, and 15 of
-    // the 16 token columns of a product would be empty: 34.0 against 31.8 us at Ling width)
-    p.gu_mfma = (WF == MOE_FMT_MXFP4 || (WF == MOE_FMT_FP8 && M >= 3)) ? 1 : 0;
+    // MXFP4 gate/up rows on the matrix cores from 2 tokens on: each code is decoded once for all
+    // tokens, so the work per weight byte no longer grows with the unit's token count.  At one token
+    // the vector path decodes each code once as well and reads whole rows (MXFP4 22.3 against
+    // 22.6 us).  FP8 from 3 tokens on (15 of the 16 token columns of a product would be empty at
+    // one token: 34.0 against 31.8 us at Ling width)
+    p.gu_mfma = ((WF == MOE_FMT_MXFP4 && M >= 2) || (WF == MOE_FMT_FP8 && M >= 3)) ? 1 : 0;
     // The shared expert's gate/up stays on the vector path at every token count: its rows run while
     // the routing is still pending, and on the matrix cores at 16 tokens the layer took longer
     // (FP8 136.0 against 129.7 us, MXFP4 106.3 against 103.9 us)
