@@ -2577,11 +2577,14 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             LDS int* nwv = qlog + kWaves * cap;                                 // [kWaves]
             // below six tasks per wave the chunks' granularity costs more than the balance gains
             const bool dyn = T >= 6 * kWaves * G;
-            const int Rs = dyn ? (int)(7 * (int64_t)T / (80 * (int64_t)G)) : (T + kWaves * G - 1) / (kWaves * G);
+            const int Rs = dyn ? 7 * T / (80 * G) : (T + kWaves * G - 1) / (kWaves * G);  // 7 T < 2^31
             const int P0 = dyn ? kWaves * G * Rs : T;
             // this workgroup's static tasks: a contiguous range of the static part, dealt to its
-            // waves round robin (consecutive rows: whole DRAM pages, contiguous write-out)
-            const int sa = P0 * b / G, sbnd = P0 * (b + 1) / G;  // task counts * G < 2^31: 32-bit divisions
+            // waves round robin (consecutive rows: whole DRAM pages, contiguous write-out); the
+            // ranges here take one 32-bit division each, as this setup runs on every wave between
+            // the routing and the first gate/up load
+            const int sq = P0 / G, sr = P0 - sq * G;
+            const int sa = b * sq + min(b, sr), sbnd = sa + sq + (b < sr ? 1 : 0);
             const int ns = n_strided(sbnd - sa, w, kWaves);  // static positions of this wave
             // consecutive workgroups sit on different XCDs (round robin), so pool b / 8 gathers one
             // workgroup of every XCD: whole XCDs stream at different rates (up to 15% apart at 16
@@ -2589,10 +2592,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             // even that out (pools per XCD: the XCDs' gate/up ends 15 us apart at 16 bf16 tokens,
             // these: 4 us; bf16 16 tokens 181.6 -> 180.3 us, 6 tokens 75.4 -> 74.8 us)
             const int npool = max(1, G / 8), pool = (b / 8) % npool;
-            const int pa = P0 + (T - P0) * pool / npool;
-            const int pb = P0 + (T - P0) * (pool + 1) / npool;
-            const int64_t rb = row_bytes<WF>(H);
-            const int ch = max(1, (int)(20480 / (2 * RTG * rb)));
+            const int pq = (T - P0) / npool, pr = (T - P0) - pq * npool;
+            const int pa = P0 + pool * pq + min(pool, pr), pb = pa + pq + (pool < pr ? 1 : 0);
+            const int rb = (int)row_bytes<WF>(H);
+            const int ch = max(1, 20480 / (2 * RTG * rb));
             const int nch = (pb - pa + ch - 1) / ch;
             uint32_t* pctr = line(set, kLinePoolC0 + pool);
             bool has_pend = dyn && ns + ch <= cap;
