@@ -313,11 +313,21 @@ __device__ __forceinline__ void dot_x(const Chunk& r, const LDS char* xrow, int 
     }
 }
 
-// Dot of weight chunk c with the matching elements of a SwiGLU output row in LDS, fp32
-// accumulation.  For bf16 and MXFP4 weights the row is staged as two bfloat16 planes, hi = the
-// fp32 value with its low 16 bits cleared and lo = the rest rounded to bfloat16 (at `lo_off` bytes
-// from the row), so hi + lo carries ~16 significant bits and every product pair is one
-// v_dot2_f32_bf16; for binary32 weights it is staged as fp32.
+// How the vector down path stages a SwiGLU output row in LDS (act_mode): 0 fp32 (binary32
+// weights); 1 two bfloat16 planes (bf16 weights), hi = the fp32 value with its low 16 bits cleared
+// and lo = the rest rounded to bfloat16 (at `lo_off` bytes from the row), so hi + lo carries ~16
+// significant bits and every product pair is one v_dot2_f32_bf16; 2 one bfloat16 plane rounded to
+// nearest even (MXFP4 and FP8 weights: the rounding the matrix cores apply; their rows decode to
+// bfloat16 in the same instructions, and the second plane doubled the LDS reads and products of
+// the phase: FP8 at 16 tokens 125.8 -> 122.1 us, at 6 tokens 62.9 -> 59.5 us, MXFP4 at 16 tokens
+// 98.0 -> 93.1 us).
+template <int WF>
+__host__ __device__ constexpr int act_mode() {
+    return WF == MOE_FMT_F32 ? 0 : (WF == MOE_FMT_BF16 ? 1 : 2);
+}
+
+// Dot of weight chunk c with the matching elements of a SwiGLU output row in LDS (staged as
+// act_mode<WF>), fp32 accumulation.
 template <int WF>
 __device__ __forceinline__ void dot_a(const Chunk& r, const LDS char* arow, int lo_off, int c, float (&acc)[kAcc]) {
     if constexpr (WF == MOE_FMT_BF16) {
@@ -338,41 +348,31 @@ __device__ __forceinline__ void dot_a(const Chunk& r, const LDS char* arow, int 
         const float sc = e8m0_to_f32(r.s);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const u32x4 hi = *(const LDS u32x4*)(arow + 64 * c + 16 * d);
-            const u32x4 lo = *(const LDS u32x4*)(arow + lo_off + 64 * c + 16 * d);
+            const u32x4 a = *(const LDS u32x4*)(arow + 64 * c + 16 * d);
             const uint32_t w = r.q[d];
             const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
             const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
             const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
             const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
-            const uint32_t h0 = hi[0], h1 = hi[1], h2 = hi[2], h3 = hi[3];
-            const uint32_t l0 = lo[0], l1 = lo[1], l2 = lo[2], l3 = lo[3];
-            acc[0] = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(h0), acc[0], false);
-            acc[1] = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(h1), acc[1], false);
-            acc[2] = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(h2), acc[2], false);
-            acc[3] = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(h3), acc[3], false);
-            acc[0] = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(l0), acc[0], false);
-            acc[1] = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(l1), acc[1], false);
-            acc[2] = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(l2), acc[2], false);
-            acc[3] = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(l3), acc[3], false);
+            const uint32_t a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
+            acc[0] = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(a0), acc[0], false);
+            acc[1] = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(a1), acc[1], false);
+            acc[2] = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(a2), acc[2], false);
+            acc[3] = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(a3), acc[3], false);
         }
     } else if constexpr (WF == MOE_FMT_FP8) {
-        // as dot_x: chunk c covers elements 16c .. 16c+15, 32 bytes of each bfloat16 plane
-        const LDS u32x4* hp = (const LDS u32x4*)(arow + 32 * c);
-        const LDS u32x4* lp = (const LDS u32x4*)(arow + lo_off + 32 * c);
-        const u32x4 ha = hp[0], hb = hp[1], la = lp[0], lb = lp[1];
-        const uint32_t hd[8] = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
-        const uint32_t ld[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
+        // as dot_x: chunk c covers elements 16c .. 16c+15, 32 bytes of the bfloat16 row
+        const LDS u32x4* ap = (const LDS u32x4*)(arow + 32 * c);
+        const u32x4 aa = ap[0], ab = ap[1];
+        const uint32_t ad[8] = {aa[0], aa[1], aa[2], aa[3], ab[0], ab[1], ab[2], ab[3]};
         const float sc = __uint_as_float(r.s);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const uint32_t w = r.q[d];
             const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
             const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-            float t = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(hd[2 * d]), 0.0f, false);
-            t = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(hd[2 * d + 1]), t, false);
-            t = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(ld[2 * d]), t, false);
-            t = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(ld[2 * d + 1]), t, false);
+            float t = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(ad[2 * d]), 0.0f, false);
+            t = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(ad[2 * d + 1]), t, false);
             acc[d] = fmaf(t, sc, acc[d]);
         }
     } else {
@@ -601,9 +601,10 @@ __device__ __forceinline__ void async_rows_to_lds(char* lds, const uint8_t* src,
 __host__ __device__ __forceinline__ int logit_stride(int E) { return (E + 3) / 4 * 4; }
 
 // Stages `tcount` fp32 SwiGLU rows of K elements (global rows of `stride` floats from `src`) into
-// LDS rows of 4 * K bytes with 16-byte device-scope loads.  SPLIT: each LDS row holds the bfloat16
-// planes hi (K values) then lo (K values) that dot_a reads; otherwise the fp32 values.
-template <bool SPLIT>
+// LDS rows of 4 * K bytes with 16-byte device-scope loads, as dot_a reads them (act_mode MODE):
+// 0 the fp32 values; 1 the bfloat16 planes hi (K values) then lo (K values); 2 the K values
+// rounded to bfloat16 (the rest of the row unused).
+template <int MODE>
 __device__ __forceinline__ void stage_rows(LDS float* dst, const float* src, int stride, int tcount, int K) {
     const __amdgpu_buffer_rsrc_t r = dev_rsrc(src, (uint32_t)(tcount * stride * 4));
     const int q4 = K / 4, n = tcount * q4;
@@ -621,7 +622,13 @@ __device__ __forceinline__ void stage_rows(LDS float* dst, const float* src, int
         for (int u = 0; u < 4; ++u) {
             const int i = i0 + u * kThreads;
             if (i < n) {
-                if constexpr (SPLIT) {
+                if constexpr (MODE == 2) {
+                    const int t = i / q4, c4 = i - t * q4;
+                    LDS char* row = (LDS char*)dst + (int64_t)t * K * 4;
+                    *(LDS u32x2*)(row + 8 * c4) =
+                        u32x2{(uint32_t)f32_to_bf16_rne(v[u][0]) | ((uint32_t)f32_to_bf16_rne(v[u][1]) << 16),
+                              (uint32_t)f32_to_bf16_rne(v[u][2]) | ((uint32_t)f32_to_bf16_rne(v[u][3]) << 16)};
+                } else if constexpr (MODE == 1) {
                     const int t = i / q4, c4 = i - t * q4;
                     uint32_t h[4], l[4];
 #pragma unroll
@@ -2706,7 +2713,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         if (has_sh && nown > 0 && !SLICE && !mf_sh) {
             wait_geq(line(set, kLineShared), (uint32_t)Is, fault);
             MOE_TRACE(25);
-            stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
+            stage_rows<act_mode<WF>()>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
             __syncthreads();
             MOE_TRACE(26);
             // the slice's rows make one or two tasks, so the tokens are split over the waves instead:
@@ -2766,7 +2773,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 wait_units(set, (uint32_t)(U * I), has_sh ? (uint32_t)Is : 0u, fault);
                 call_fault = ld_dev(fault.flag);  // used at the y write, long after it lands
                 MOE_TRACE(9);
-                stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act, astride, NP + (has_sh ? M : 0), astride);
+                stage_rows<act_mode<WF>()>((LDS float*)xs, p.ws.act, astride, NP + (has_sh ? M : 0), astride);
                 __syncthreads();
                 MOE_TRACE(10);
             };
@@ -2939,7 +2946,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 MOE_TRACE(9);
                 for (int sg = 0; sg < nseg; ++sg) {
                     const int u = sg_u[sg];
-                    stage_rows<WF != MOE_FMT_F32>((LDS float*)xs + aoff[sg], p.ws.act + (int64_t)s_off[u] * p.act_stride,
+                    stage_rows<act_mode<WF>()>((LDS float*)xs + aoff[sg], p.ws.act + (int64_t)s_off[u] * p.act_stride,
                                                   p.act_stride, __popc(s_mask[u]), I);
                 }
                 __syncthreads();
@@ -2969,7 +2976,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     if (!staged) {
                         wait_units(set, (uint32_t)(U * I), 0u, fault);
                         if (first) MOE_TRACE(9);
-                        stage_rows<WF != MOE_FMT_F32>((LDS float*)xs, p.ws.act + (int64_t)row0 * p.act_stride, p.act_stride, t, I);
+                        stage_rows<act_mode<WF>()>((LDS float*)xs, p.ws.act + (int64_t)row0 * p.act_stride, p.act_stride, t, I);
                         __syncthreads();
                         if (first) MOE_TRACE(10);
                         staged = true;
