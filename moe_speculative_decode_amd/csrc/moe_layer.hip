@@ -2385,7 +2385,9 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     const bool mf_sh = p.sh_mfma != 0;  // shared down rows on the matrix cores (window stored swizzled)
     // slice mode on the matrix cores rounds the SwiGLU rows to bfloat16 for its B operands: the
     // producers write them as bfloat16 (the same rounding, half the bytes every workgroup stages)
-    const bool bf_act = SLICE && mf_slice;
+    // (and so do the producers for MXFP4 and FP8 weights everywhere: their vector down path takes
+    // the rows as one bfloat16 plane)
+    const bool bf_act = (SLICE && mf_slice) || act_mode<WF>() == 2;
     const uint16_t* act16 = (const uint16_t*)p.ws.act;
     const __amdgpu_buffer_rsrc_t act_rs =
         dev_rsrc(p.ws.act, (uint32_t)((int64_t)(NP + M) * p.act_stride * 4));
@@ -2456,7 +2458,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                         t.slot = (int)r0;
                     },
                     [&](int r, int i, float v) {  // i: the i-th token of the mask, token t0 + i
-                        st_dev(p.ws.act + (int64_t)(NP + t0 + i) * p.act_stride + r, v);
+                        st_dev_bf16(act_rs, (uint32_t)(((int64_t)(NP + t0 + i) * p.act_stride + r) * 2), v);
                     });
             }
         }
@@ -2693,7 +2695,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 wait_geq(line(set, kLineShared), (uint32_t)Is, fault);
                 MOE_TRACE(25);
                 const int apitch = 2 * p.act_stride + 16;  // rows 4 banks apart: no conflicts among the B columns
-                stage_rows_bf16((LDS char*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is, apitch);
+                if (bf_act)
+                    stage_rows_b16((LDS char*)xs, act16 + (int64_t)NP * p.act_stride, p.act_stride, M, Is, apitch);
+                else
+                    stage_rows_bf16((LDS char*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is, apitch);
                 __syncthreads();
                 MOE_TRACE(26);
                 auto unit_of = [&](int, SliceUnit& t) {
@@ -2713,7 +2718,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         if (has_sh && nown > 0 && !SLICE && !mf_sh) {
             wait_geq(line(set, kLineShared), (uint32_t)Is, fault);
             MOE_TRACE(25);
-            stage_rows<act_mode<WF>()>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
+            if constexpr (act_mode<WF>() == 2)
+                stage_rows_b16((LDS char*)xs, act16 + (int64_t)NP * p.act_stride, p.act_stride, M, Is, 4 * Is);
+            else
+                stage_rows<act_mode<WF>()>((LDS float*)xs, p.ws.act + (int64_t)NP * p.act_stride, p.act_stride, M, Is);
             __syncthreads();
             MOE_TRACE(26);
             // the slice's rows make one or two tasks, so the tokens are split over the waves instead:
@@ -2773,7 +2781,10 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 wait_units(set, (uint32_t)(U * I), has_sh ? (uint32_t)Is : 0u, fault);
                 call_fault = ld_dev(fault.flag);  // used at the y write, long after it lands
                 MOE_TRACE(9);
-                stage_rows<act_mode<WF>()>((LDS float*)xs, p.ws.act, astride, NP + (has_sh ? M : 0), astride);
+                if constexpr (act_mode<WF>() == 2)
+                    stage_rows_b16((LDS char*)xs, act16, astride, NP + (has_sh ? M : 0), astride, 4 * astride);
+                else
+                    stage_rows<act_mode<WF>()>((LDS float*)xs, p.ws.act, astride, NP + (has_sh ? M : 0), astride);
                 __syncthreads();
                 MOE_TRACE(10);
             };
@@ -2946,8 +2957,12 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 MOE_TRACE(9);
                 for (int sg = 0; sg < nseg; ++sg) {
                     const int u = sg_u[sg];
-                    stage_rows<act_mode<WF>()>((LDS float*)xs + aoff[sg], p.ws.act + (int64_t)s_off[u] * p.act_stride,
-                                                  p.act_stride, __popc(s_mask[u]), I);
+                    if constexpr (act_mode<WF>() == 2)
+                        stage_rows_b16((LDS char*)((LDS float*)xs + aoff[sg]), act16 + (int64_t)s_off[u] * p.act_stride,
+                                       p.act_stride, __popc(s_mask[u]), I, 4 * I);
+                    else
+                        stage_rows<act_mode<WF>()>((LDS float*)xs + aoff[sg], p.ws.act + (int64_t)s_off[u] * p.act_stride,
+                                                   p.act_stride, __popc(s_mask[u]), I);
                 }
                 __syncthreads();
                 MOE_TRACE(10);
@@ -2976,7 +2991,11 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     if (!staged) {
                         wait_units(set, (uint32_t)(U * I), 0u, fault);
                         if (first) MOE_TRACE(9);
-                        stage_rows<act_mode<WF>()>((LDS float*)xs, p.ws.act + (int64_t)row0 * p.act_stride, p.act_stride, t, I);
+                        if constexpr (act_mode<WF>() == 2)
+                            stage_rows_b16((LDS char*)xs, act16 + (int64_t)row0 * p.act_stride, p.act_stride, t, I, 4 * I);
+                        else
+                            stage_rows<act_mode<WF>()>((LDS float*)xs, p.ws.act + (int64_t)row0 * p.act_stride, p.act_stride, t,
+                                                       I);
                         __syncthreads();
                         if (first) MOE_TRACE(10);
                         staged = true;
