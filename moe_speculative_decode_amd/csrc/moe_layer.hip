@@ -1022,24 +1022,21 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
             }
         }
     }
-    __syncthreads();
+    if (M > 1) __syncthreads();  // one token: wave 0 selected it and builds the tables below
     MOE_TRACE(13);
     if (wave == 0 && M == 1) {
-        // one token: the units are its k experts in ascending id order and pair j is row rank(j);
-        // ties (only possible if a cut-short selection repeated an id) go by slot, so every unit
-        // slot is written once
-        const int id = lane < k ? sid[lane] : 0x7FFFFFFF;
-        int rank = 0;
-        for (int j = 0; j < k; ++j) {
-            const int o = __builtin_amdgcn_readlane(id, j);
-            rank += (o < id || (o == id && j < lane)) ? 1 : 0;
-        }
+        // one token: unit j is the j-th selected expert and pair j its row.  Every workgroup takes
+        // the same order and the combine sums by selection slot, so no ranking is needed here (the
+        // ranks by id, once a barrier and a dependent loop on this path, are taken only where the
+        // dispatch tables are written).  This wave wrote the selection; its LDS operations complete
+        // in order.
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         if (lane < k) {
-            s_mask[rank] = 1u;
-            s_off[rank] = rank;
-            s_exp[rank] = min(max(id, 0), E - 1);
-            s_pair[lane] = rank;
-            s_roww[rank] = sw[lane];
+            s_mask[lane] = 1u;
+            s_off[lane] = lane;
+            s_exp[lane] = min(max(sid[lane], 0), E - 1);
+            s_pair[lane] = lane;
+            s_roww[lane] = sw[lane];
         }
         if (lane == 0) {
             s_mask[k] = has_sh ? 1u : 0u;
@@ -1103,8 +1100,22 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
     const int U = tab[kTabMisc];
 
     if (publish_outputs) {
+        // the caller's tables list the units by ascending expert id; one token keeps its units in
+        // selection order internally, so unit (and row) u is written at its rank by id (ties: slot),
+        // kept in the compaction's scratch (unused at one token)
+        LDS int* rk = offe;
+        if (M == 1) {
+            const int u = threadIdx.x;
+            if (u < k) {
+                int rank = 0;
+                for (int j = 0; j < k; ++j) rank += (s_exp[j] < s_exp[u] || (s_exp[j] == s_exp[u] && j < u)) ? 1 : 0;
+                rk[u] = rank;
+            }
+            __syncthreads();
+        }
+        auto ro = [&](int u) { return M == 1 && u < k ? rk[u] : u; };
         for (int q = threadIdx.x; q < NP; q += kThreads) {
-            const int row = s_pair[q];
+            const int row = ro(s_pair[q]);
             if (p.topk_ids) p.topk_ids[q] = sid[q];
             if (p.topk_w) p.topk_w[q] = sw[q];
             if (p.disp.row_token) p.disp.row_token[row] = q / k;
@@ -1112,8 +1123,9 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
             if (p.disp.row_weight) p.disp.row_weight[row] = sw[q];
         }
         for (int u = threadIdx.x; u < U + (has_sh ? 1 : 0); u += kThreads) {
-            if (p.disp.unit_expert) p.disp.unit_expert[u] = s_exp[u];
-            if (p.disp.unit_off) p.disp.unit_off[u] = s_off[u];
+            const int ru = ro(u);  // one token: the unit's first row is its own index, u
+            if (p.disp.unit_expert) p.disp.unit_expert[ru] = s_exp[u];
+            if (p.disp.unit_off) p.disp.unit_off[ru] = M == 1 ? ru : s_off[u];
         }
         if (threadIdx.x == 0) {
             if (p.disp.unit_count) *p.disp.unit_count = U;
@@ -2485,6 +2497,49 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     }
     MOE_TRACE(3);
 
+    // The vector gate/up's task split (phase C) for nu units: T tasks of RTG rows of the flattened
+    // (unit, row) list.  Each wave first takes a static share (about 70% of the work); the rest is
+    // handed out in chunks of ch tasks from npool pools of eight workgroups each.
+    struct GUPlan {
+        int T, P0, sa, ns, pool, pa, pb, ch, nch;
+        bool dyn;
+    };
+    auto gu_plan = [&](int nu) {
+        GUPlan g;
+        g.T = nu * (I / RTG);
+        // below six tasks per wave the chunks' granularity costs more than the balance gains
+        g.dyn = g.T >= 6 * kWaves * G;
+        const int Rs = g.dyn ? 7 * g.T / (80 * G) : (g.T + kWaves * G - 1) / (kWaves * G);  // 7 T < 2^31
+        g.P0 = g.dyn ? kWaves * G * Rs : g.T;
+        // this workgroup's static tasks: a contiguous range of the static part, dealt to its
+        // waves round robin (consecutive rows: whole DRAM pages, contiguous write-out); one 32-bit
+        // division per split
+        const int sq = g.P0 / G, sr = g.P0 - sq * G;
+        g.sa = b * sq + min(b, sr);
+        const int sbnd = g.sa + sq + (b < sr ? 1 : 0);
+        g.ns = n_strided(sbnd - g.sa, wave_id(), kWaves);  // static positions of this wave
+        // consecutive workgroups sit on different XCDs (round robin), so pool b / 8 gathers one
+        // workgroup of every XCD: whole XCDs stream at different rates (up to 15% apart at 16
+        // bf16 tokens, depending on the box and the data), and a pool within one XCD could not
+        // even that out (pools per XCD: the XCDs' gate/up ends 15 us apart at 16 bf16 tokens,
+        // these: 4 us; bf16 16 tokens 181.6 -> 180.3 us, 6 tokens 75.4 -> 74.8 us)
+        const int npool = max(1, G / 8);
+        g.pool = (b / 8) % npool;
+        const int pq = (g.T - g.P0) / npool, pr = (g.T - g.P0) - pq * npool;
+        g.pa = g.P0 + g.pool * pq + min(g.pool, pr);
+        g.pb = g.pa + pq + (g.pool < pr ? 1 : 0);
+        g.ch = max(1, 20480 / (2 * RTG * (int)row_bytes<WF>(H)));
+        g.nch = (g.pb - g.pa + g.ch - 1) / g.ch;
+        return g;
+    };
+    // One token always has k units: with bf16 weights its split is worked out while the routing is
+    // pending, not between the routing and the first gate/up load (bf16 one token 30.8 -> 30.1 us;
+    // the second copy of the split's code cost the MXFP4 instance 1 us at six tokens)
+    const bool gu_early = WF == MOE_FMT_BF16 && SLICE && M == 1 && !p.gu_mfma && !p.route_only;
+    GUPlan gpe{};
+    if constexpr (SLICE && WF == MOE_FMT_BF16)
+        if (gu_early) gpe = gu_plan(k);
+
     // ---- B: routing barrier, top-k and compaction in every workgroup ----
     // the published expert pairs are polled by the highest wave without shared gate/up tasks (those
     // run on the vector ALU and, at 16 tokens with E2M1 decode, would hold the poll back by µs)
@@ -2536,7 +2591,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         }
     };
     if constexpr (SLICE) {
-        if (nown > 0) nfit = min(U, (int)(p.dn_bytes / (nown * rbI)));
+        if (nown > 0) nfit = min(U, p.dn_bytes / (int)(nown * rbI));  // 32-bit: on the path to gate/up
         if (!late_window) slice_window();
     }
     MOE_TRACE(21);
@@ -2580,37 +2635,19 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             }
             my_rows = nloc * 8;
         } else {
-            // Tasks of RTG rows.  Each wave first takes a static share (about 70% of the work); the rest
-            // is handed out in chunks of ch tasks from npool pools of eight workgroups each: some
-            // CUs stream persistently faster than others, and the fast ones take more chunks.  A wave claims its next chunk one chunk ahead, so the atomic's
-            // round trip overlaps the current chunk, and claims only what its staging room holds
-            // (room for twice the average dynamic share, so the pools always drain).  Each wave
-            // logs the task at every position for the write-out.
-            const int T = (int)(nrows / RTG), cap = p.gu_cap, lane = threadIdx.x & 63, w = wave_id();
+            // Tasks of RTG rows, split by gu_plan: some CUs stream persistently faster than others,
+            // and the fast ones take more chunks.  A wave claims its next chunk one chunk ahead, so
+            // the atomic's round trip overlaps the current chunk, and claims only what its staging
+            // room holds (room for twice the average dynamic share, so the pools always drain).
+            // Each wave logs the task at every position for the write-out.
+            const int cap = p.gu_cap, lane = threadIdx.x & 63, w = wave_id();
             LDS int* qlog = (LDS int*)(cst + (int64_t)kWaves * cap * RTG * M);  // [kWaves][cap]
             LDS int* nwv = qlog + kWaves * cap;                                 // [kWaves]
-            // below six tasks per wave the chunks' granularity costs more than the balance gains
-            const bool dyn = T >= 6 * kWaves * G;
-            const int Rs = dyn ? 7 * T / (80 * G) : (T + kWaves * G - 1) / (kWaves * G);  // 7 T < 2^31
-            const int P0 = dyn ? kWaves * G * Rs : T;
-            // this workgroup's static tasks: a contiguous range of the static part, dealt to its
-            // waves round robin (consecutive rows: whole DRAM pages, contiguous write-out); the
-            // ranges here take one 32-bit division each, as this setup runs on every wave between
-            // the routing and the first gate/up load
-            const int sq = P0 / G, sr = P0 - sq * G;
-            const int sa = b * sq + min(b, sr), sbnd = sa + sq + (b < sr ? 1 : 0);
-            const int ns = n_strided(sbnd - sa, w, kWaves);  // static positions of this wave
-            // consecutive workgroups sit on different XCDs (round robin), so pool b / 8 gathers one
-            // workgroup of every XCD: whole XCDs stream at different rates (up to 15% apart at 16
-            // bf16 tokens, depending on the box and the data), and a pool within one XCD could not
-            // even that out (pools per XCD: the XCDs' gate/up ends 15 us apart at 16 bf16 tokens,
-            // these: 4 us; bf16 16 tokens 181.6 -> 180.3 us, 6 tokens 75.4 -> 74.8 us)
-            const int npool = max(1, G / 8), pool = (b / 8) % npool;
-            const int pq = (T - P0) / npool, pr = (T - P0) - pq * npool;
-            const int pa = P0 + pool * pq + min(pool, pr), pb = pa + pq + (pool < pr ? 1 : 0);
+            const GUPlan g = gu_early ? gpe : gu_plan(U);
+            const int T = g.T, P0 = g.P0, sa = g.sa, ns = g.ns, pool = g.pool, pa = g.pa, pb = g.pb, ch = g.ch,
+                      nch = g.nch;
+            const bool dyn = g.dyn;
             const int rb = (int)row_bytes<WF>(H);
-            const int ch = max(1, 20480 / (2 * RTG * rb));
-            const int nch = (pb - pa + ch - 1) / ch;
             uint32_t* pctr = line(set, kLinePoolC0 + pool);
             bool has_pend = dyn && ns + ch <= cap;
             uint32_t pend = 0;
