@@ -780,8 +780,11 @@ __device__ __forceinline__ void rms_norm_rows(const Params& p, LDS char* xs) {
 // lowest index is kept, so ties resolve to the lower id.  The winning lane drops that logit and
 // recomputes its maximum.  Writes ids, logits and softmax-over-the-k weights in order.  Every id
 // written is in [0, E).
+// With `early` (one token, no bias): after round r, early[r] holds the r-th selected id and
+// early[kMaxTopK] the number of rounds done, so other waves can start on an expert once it is known.
 __device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, uint32_t tag, const Fault& fault,
-                                          const float* bias, LDS int* out_id, LDS float* out_w, LDS float* out_v) {
+                                          const float* bias, LDS int* out_id, LDS float* out_w, LDS float* out_v,
+                                          volatile LDS int* early = nullptr) {
     const int lane = threadIdx.x & 63;
     const __amdgpu_buffer_rsrc_t rs = dev_rsrc(lrow, (uint32_t)E * 8);  // loads past E return 0
     // selection bias of the lane's experts, loaded while the logits are polled (past E: 0)
@@ -873,6 +876,10 @@ __device__ __forceinline__ void wave_topk(const uint64_t* lrow, int E, int k, ui
             const uint64_t ball = __ballot(key[0] == K);  // never empty: K is one lane's head
             const int wl = __builtin_amdgcn_readfirstlane(ball ? __ffsll((unsigned long long)ball) - 1 : 0);
             const int wi = __builtin_amdgcn_readlane((int)ixw, wl) & 7;
+            if (early != nullptr && lane == 0) {
+                early[r] = min(8 * wl + wi, E - 1);
+                early[kMaxTopK] = r + 1;  // after the id (volatile: in this order)
+            }
             const bool mine = lane == r;
             my_key = mine ? K : my_key;
             my_id = mine ? min(8 * wl + wi, E - 1) : my_id;
@@ -949,8 +956,12 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // Top-k of all M tokens (each top-k wave waits for its token's logits of this call, tagged `tag`)
 // and the batch compaction into this workgroup's LDS tables.  Workgroup 0 (`publish_outputs`)
 // also writes the caller-visible routing outputs.  Returns U.
+// early, pre (one token without a bias): the selecting wave publishes each round's expert at early
+// (see wave_topk) and the other waves run pre() while it selects.
+template <typename Pre>
 __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, LDS char* sel, bool publish_outputs,
-                                                 uint32_t tag, int poll_wave, const Fault& fault) {
+                                                 uint32_t tag, int poll_wave, const Fault& fault,
+                                                 volatile LDS int* early, Pre pre) {
     const int E = p.E, M = p.M, k = p.k, NP = M * k;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const bool has_sh = p.Is > 0;
@@ -969,7 +980,8 @@ __device__ __forceinline__ int route_and_compact(const Params& p, LDS int* tab, 
     if (!p.route_delegate) {
         for (int m = wave; m < M; m += kWaves)
             wave_topk(p.ws.logits + (int64_t)m * logit_stride(E), E, k, tag, fault, rbias, sid + m * k,
-                      sw + m * k, sv + m * k);
+                      sw + m * k, sv + m * k, M == 1 ? early : nullptr);
+        if (M == 1 && wave != 0) pre();
     } else {
         // workgroup m < M selects token m's experts and publishes them as tagged words; every
         // workgroup then reads the M * k published (id, weight) pairs instead of M * E logits
@@ -1230,30 +1242,41 @@ struct GUTask {
 // computes the current one; the prefetch is unconditional (the last task re-reads itself) so the
 // number of loads in flight is static and the compiler waits for exactly the task it needs.
 // Returns the number of tasks computed.
+// The loads of one gate/up task into this wave's chunk registers (a stand-in task: one chunk).
+template <int WF, int NJ>
+__device__ __forceinline__ void gateup_load(int H, Chunk (&g)[Geo<WF>::RL_G][NJ], Chunk (&u)[Geo<WF>::RL_G][NJ],
+                                            const GUTask& t) {
+    constexpr int LPR = Geo<WF>::LPR_G, RL = Geo<WF>::RL_G;
+    const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
+    const int nch = H / Geo<WF>::EPC;
+    const int64_t rb = row_bytes<WF>(H), sb = H / 32;
+#pragma unroll
+    for (int rl = 0; rl < RL; ++rl) {
+        const int64_t ro = t.dummy ? 0 : gi * RL + rl;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int c = t.dummy ? 0 : min(sl + LPR * j, nch - 1);
+            ld_chunk<WF>(g[rl][j], t.g + ro * rb, WF == MOE_FMT_FP8 ? t.gs : t.gs + ro * sb, c);
+            ld_chunk<WF>(u[rl][j], t.u + ro * rb, WF == MOE_FMT_FP8 ? t.us : t.us + ro * sb, c);
+        }
+    }
+}
+
+// (pre: the first task's loads were issued into ga / ua before the call, by gateup_load)
 template <int AF, int WF, int NJ, typename Next, typename Info, typename Out>
-__device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, Next next, Info info, Out out) {
+__device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, Next next, Info info, Out out,
+                                          Chunk (&ga)[Geo<WF>::RL_G][NJ], Chunk (&ua)[Geo<WF>::RL_G][NJ],
+                                          bool pre = false) {
     constexpr int LPR = Geo<WF>::LPR_G, RL = Geo<WF>::RL_G;
     const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
     const int H = p.H;
     const int nch = H / Geo<WF>::EPC;
-    const int64_t rb = row_bytes<WF>(H), sb = H / 32;
     static_assert(WF != MOE_FMT_FP8 || kFp8Block % rt_gate<WF>() == 0, "an FP8 gate/up task lies in one row block");
     int q = next(0);
     if (q < 0) return 0;
-    Chunk ga[RL][NJ], ua[RL][NJ], gb[RL][NJ], ub[RL][NJ];
+    Chunk gb[RL][NJ], ub[RL][NJ];
     GUTask ta, tb;
-    auto load = [&](Chunk(&g)[RL][NJ], Chunk(&u)[RL][NJ], const GUTask& t) {
-#pragma unroll
-        for (int rl = 0; rl < RL; ++rl) {
-            const int64_t ro = t.dummy ? 0 : gi * RL + rl;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int c = t.dummy ? 0 : min(sl + LPR * j, nch - 1);
-                ld_chunk<WF>(g[rl][j], t.g + ro * rb, WF == MOE_FMT_FP8 ? t.gs : t.gs + ro * sb, c);
-                ld_chunk<WF>(u[rl][j], t.u + ro * rb, WF == MOE_FMT_FP8 ? t.us : t.us + ro * sb, c);
-            }
-        }
-    };
+    auto load = [&](Chunk(&g)[RL][NJ], Chunk(&u)[RL][NJ], const GUTask& t) { gateup_load<WF, NJ>(H, g, u, t); };
     auto settle_all = [&](Chunk(&g)[RL][NJ], Chunk(&u)[RL][NJ]) {
 #pragma unroll
         for (int rl = 0; rl < RL; ++rl)
@@ -1304,7 +1327,7 @@ __device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, N
     int s = 0;
     info(q, 0, ta);
     ta.dummy = 0;
-    load(ga, ua, ta);
+    if (!pre) load(ga, ua, ta);
     MOE_TRACE(16);
     while (true) {
         const int qb = next(s + 1);
@@ -1334,9 +1357,10 @@ __device__ __forceinline__ int gateup_seq(const Params& p, const LDS char* xs, N
 // The static form: local tasks i = wslot, wslot + kWaves, ... < n; info(i, task) describes task i.
 template <int AF, int WF, int NJ, typename Info, typename Out>
 __device__ __forceinline__ void gateup_run(const Params& p, const LDS char* xs, int n, int wslot, Info info, Out out) {
+    Chunk g[Geo<WF>::RL_G][NJ], u[Geo<WF>::RL_G][NJ];
     gateup_seq<AF, WF, NJ>(
         p, xs, [&](int s) { return wslot + kWaves * s < n ? wslot + kWaves * s : -1; },
-        [&](int i, int, GUTask& t) { info(i, t); }, out);
+        [&](int i, int, GUTask& t) { info(i, t); }, out, g, u);
 }
 
 // Routed gate/up rows on the matrix cores, for MXFP4 weights in slice mode from three tokens on (a
@@ -2413,6 +2437,9 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     }
     if constexpr (AF == MOE_FMT_BF16)
         if (norm) rms_norm_rows<NJ>(p, xs);  // the normed token rows replace x everywhere
+    // one bf16 token: the selection's round counter (see gu_first below) starts at zero
+    if constexpr (SLICE && WF == MOE_FMT_BF16)
+        if (M == 1 && threadIdx.x == 0) ((volatile LDS int*)(lds + p.lds_sel))[kMaxTopK] = 0;
     __builtin_amdgcn_s_waitcnt(0);  // token rows (and the slice's shared down rows) in LDS
     __syncthreads();
     MOE_TRACE(1);
@@ -2539,12 +2566,43 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
     GUPlan gpe{};
     if constexpr (SLICE && WF == MOE_FMT_BF16)
         if (gu_early) gpe = gu_plan(k);
+    // ... and the waves the selection leaves idle issue their first gate/up task as soon as its
+    // expert has been selected (the selecting wave publishes each round's id in LDS; without a bias
+    // the units are the experts in selection order), so those loads run during the selection
+    Chunk gfirst_g[Geo<WF>::RL_G][NJ], gfirst_u[Geo<WF>::RL_G][NJ];
+    bool gfirst = false;
+    volatile LDS int* sel_early =
+        gu_early && !(p.router_flags & MOE_ROUTER_BIAS) ? (volatile LDS int*)(lds + p.lds_sel) : nullptr;
+    auto gu_first = [&]() {
+        if constexpr (SLICE && WF == MOE_FMT_BF16) {
+            if (sel_early != nullptr && gpe.ns > 0) {
+                const int q0 = gpe.sa + wave_id();  // this wave's first static task
+                const int u = q0 / (I / RTG);
+                for (int it = 0; sel_early[kMaxTopK] <= u && it < kSpinLimit; ++it) __builtin_amdgcn_s_sleep(1);
+                if (sel_early[kMaxTopK] > u) {
+                    const int64_t e = uni(sel_early[u]);
+                    const int64_t r0 = (int64_t)q0 * RTG - (int64_t)u * I;
+                    const int64_t rb = row_bytes<WF>(H);
+                    GUTask t;
+                    t.g = (const uint8_t*)p.w.gate + (e * I + r0) * rb;
+                    t.u = (const uint8_t*)p.w.up + (e * I + r0) * rb;
+                    t.gs = t.us = nullptr;
+                    t.mask = 1u;
+                    t.slot = 0;
+                    t.dummy = 0;
+                    gateup_load<WF, NJ>(H, gfirst_g, gfirst_u, t);
+                    gfirst = true;
+                }
+            }
+        }
+    };
 
     // ---- B: routing barrier, top-k and compaction in every workgroup ----
     // the published expert pairs are polled by the highest wave without shared gate/up tasks (those
     // run on the vector ALU and, at 16 tokens with E2M1 decode, would hold the poll back by µs)
     const int U = route_and_compact(p, tab, lds + p.lds_sel, b == 0, call + 1u,
-                                    sh_waves >= kWaves ? kWaves - 1 : kWaves - 1 - sh_waves, fault);
+                                    sh_waves >= kWaves ? kWaves - 1 : kWaves - 1 - sh_waves, fault, sel_early,
+                                    gu_first);
     MOE_TRACE(5);
     if (p.route_only) {
         MOE_TRACE_FLUSH;
@@ -2691,7 +2749,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     t.mask = uni(s_mask[u]);
                     t.slot = (w * cap + s) * RTG;
                 },
-                [&](int r, int i, float v) { cst[r * M + i] = v; });
+                [&](int r, int i, float v) { cst[r * M + i] = v; }, gfirst_g, gfirst_u, gfirst);
             if (lane == 0) nwv[w] = n;
             __syncthreads();
             MOE_TRACE(6);
