@@ -1832,14 +1832,18 @@ __device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* sm
     const int ntask = (nrows + RT - 1) / RT;
     int n = wslot;
     Chunk wa[RL][NJD], wb[RL][NJD];
+    // task >= ntask: the stand-in prefetch after the last task (a static number of loads in flight):
+    // every lane reads the first chunk of row 0, one line, not a task (a re-read of the last task
+    // was in flight when the phase's stores were waited for)
     auto load = [&](Chunk(&w)[RL][NJD], int task) {
+        const bool dummy = task >= ntask;
 #pragma unroll
         for (int rl = 0; rl < RL; ++rl) {
-            const int64_t row = min(task * RT + gi * RL + rl, nrows - 1);
+            const int64_t row = dummy ? 0 : min(task * RT + gi * RL + rl, nrows - 1);
             const uint8_t* srow = scale_row<WF>(smat, srow0 + row, K);
 #pragma unroll
             for (int j = 0; j < NJD; ++j) {
-                const int c = min(sl + LPR * j, nch - 1);
+                const int c = dummy ? 0 : min(sl + LPR * j, nch - 1);
                 if constexpr (FROM_LDS)
                     ld_chunk_lds<WF>(w[rl][j], (const LDS uint8_t*)wbase + row * rb, srow, c);
                 else
@@ -1880,12 +1884,12 @@ __device__ __forceinline__ void down_run(const uint8_t* wbase, const uint8_t* sm
     ready();
     if (n >= ntask) return;
     while (true) {
-        load(wb, min(n + step, ntask - 1));
+        load(wb, n + step);
         settle_all(wa);
         compute(wa, n);
         n += step;
         if (n >= ntask) break;
-        load(wa, min(n + step, ntask - 1));
+        load(wa, n + step);
         settle_all(wb);
         compute(wb, n);
         n += step;
@@ -1905,6 +1909,7 @@ struct DNTask {
     int K;                  // inputs per row
     int orow;               // index of the task's first row in the output slice
     int prow;               // first pair row of the unit
+    int dummy;              // 1: the stand-in prefetch past the list (one line, every lane)
 };
 
 // This wave's tasks n = wslot, wslot + kWaves, ... < ntask of a flattened down-row list described by
@@ -1920,16 +1925,22 @@ __device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Inf
     int n = wslot;
     Chunk wa[RL][NJD], wb[RL][NJD];
     DNTask ta, tb;
+    // task i of the list; past its end the stand-in prefetch (the last task's description, one line
+    // read by every lane) that keeps the number of loads in flight static
+    auto task_of = [&](int i, DNTask& t) {
+        info(min(i, ntask - 1), t);
+        t.dummy = i >= ntask ? 1 : 0;
+    };
     auto load = [&](Chunk(&w)[RL][NJD], const DNTask& t) {
         const int nch = t.K / Geo<WF>::EPC;
         const int64_t rb = row_bytes<WF>(t.K);
 #pragma unroll
         for (int rl = 0; rl < RL; ++rl) {
-            const int64_t row = min(gi * RL + rl, t.nrows - 1);
+            const int64_t row = t.dummy ? 0 : min(gi * RL + rl, t.nrows - 1);
             const uint8_t* srow = scale_row<WF>(t.s, t.srow + row, t.K);
 #pragma unroll
             for (int j = 0; j < NJD; ++j) {
-                const int c = min(sl + LPR * j, nch - 1);
+                const int c = t.dummy ? 0 : min(sl + LPR * j, nch - 1);
                 if (t.lds)
                     ld_chunk_lds<WF>(w[rl][j], (const LDS uint8_t*)t.w + row * rb, srow, c);
                 else
@@ -1969,13 +1980,12 @@ __device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Inf
         }
     };
     if constexpr (PRE2) {
-        // the first two tasks load before ready() (past the list: the last task again, so the
-        // number of loads in flight stays static); then each task's loads go out right after the
-        // compute of the task before the one in flight
+        // the first two tasks load before ready() (past the list: the stand-in); then each task's
+        // loads go out right after the compute of the task before the one in flight
         if (n < ntask) {
-            info(n, ta);
+            task_of(n, ta);
             load(wa, ta);
-            info(min(n + kWaves, ntask - 1), tb);
+            task_of(n + kWaves, tb);
             load(wb, tb);
         }
         ready();
@@ -1985,30 +1995,30 @@ __device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Inf
             compute(wa, ta);
             n += kWaves;
             if (n >= ntask) break;
-            info(min(n + kWaves, ntask - 1), ta);
+            task_of(n + kWaves, ta);
             load(wa, ta);
             settle_all(wb, tb);
             compute(wb, tb);
             n += kWaves;
             if (n >= ntask) break;
-            info(min(n + kWaves, ntask - 1), tb);
+            task_of(n + kWaves, tb);
             load(wb, tb);
         }
     } else {
         if (n < ntask) {
-            info(n, ta);
+            task_of(n, ta);
             load(wa, ta);
         }
         ready();
         if (n >= ntask) return;
         while (true) {
-            info(min(n + kWaves, ntask - 1), tb);
+            task_of(n + kWaves, tb);
             load(wb, tb);
             settle_all(wa, ta);
             compute(wa, ta);
             n += kWaves;
             if (n >= ntask) break;
-            info(min(n + kWaves, ntask - 1), ta);
+            task_of(n + kWaves, ta);
             load(wa, ta);
             settle_all(wb, tb);
             compute(wb, tb);
