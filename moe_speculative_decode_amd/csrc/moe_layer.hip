@@ -3233,9 +3233,9 @@ hipError_t plan_t(Params& p, int G) {
     // (FP8 136.0 against 129.7 us, MXFP4 106.3 against 103.9 us)
     // per-token cost of a down row (a row's bytes cost kCostBase = 8), from sweeps of the
     // whole-layer time: bf16 over 0, 1, 2, 3, 4 and 6 at 6 and 16 tokens (3 is fastest at both);
-    // MXFP4 over 1, 3, 6, 9 and 14 at 16 tokens (6 is fastest: the vector path decodes every
-    // code once per token)
-    p.cost_dn = WF == MOE_FMT_MXFP4 ? 6 : (WF == MOE_FMT_BF16 ? 3 : (WF == MOE_FMT_FP8 ? 6 : 0));
+    // MXFP4 and FP8 over 3, 4, 6 and 9 at 6 and 16 tokens, with their SwiGLU rows as one bf16 plane
+    // (4 is fastest: the vector path decodes every code once per token)
+    p.cost_dn = WF == MOE_FMT_MXFP4 ? 4 : (WF == MOE_FMT_BF16 ? 3 : (WF == MOE_FMT_FP8 ? 4 : 0));
     // gate/up staging: MXFP4 tiles of 8 rows dealt round robin (at most ceil(T / G) per workgroup);
     // otherwise per wave the static share plus up to twice the average dynamic share (the split
     // the kernel makes from the actual number of units, bounded here by its maximum)
