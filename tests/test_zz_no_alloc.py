@@ -41,10 +41,11 @@ def _pair(first, second):
 
 def _small(name, fmt, lens):
     act = synth.F32 if fmt == synth.F32 else synth.BF16
-    return synth.LayerConfig(name, 512, 64, 4, 192, 128, act, fmt, tuple(lens), "shared_base", 7)
+    inter = 256 if fmt == synth.FP8 else 192  # FP8: whole 128 x 128 scale blocks
+    return synth.LayerConfig(name, 512, 64, 4, inter, 128, act, fmt, tuple(lens), "shared_base", 7)
 
 
-@pytest.mark.parametrize("fmt", [synth.BF16, synth.MXFP4], ids=["bf16", "mxfp4"])
+@pytest.mark.parametrize("fmt", [synth.BF16, synth.MXFP4, synth.FP8], ids=["bf16", "mxfp4", "fp8"])
 def test_noalloc_small_two_calls(fmt):
     big = G.Case(_small("na16", fmt, (3, 1, 7, 5)))
     small = G.Case(_small("na3", fmt, (3,)), layer_cfg=big.cfg)
@@ -56,6 +57,15 @@ def test_noalloc_ling_bf16_two_calls():
     cfg1 = synth.CONFIGS["ling_bf16_m1"]
     a = G.Case(cfg6, hidden_seed=G.seeds()["ling_bf16_m6"]["hidden_seed"])
     b = G.Case(cfg1, hidden_seed=G.seeds()["ling_bf16_m1"]["hidden_seed"])
+    _pair(a, b)
+
+
+def test_noalloc_ling_fp8_two_calls():
+    """Sixteen ragged FP8 tokens (unit-major, the largest pair-row count the scratch holds), then one."""
+    cfg16 = synth.CONFIGS["ling_fp8_m16_ragged"]
+    cfg1 = synth.CONFIGS["ling_fp8_m1"]
+    a = G.Case(cfg16, hidden_seed=G.seeds()["ling_fp8_m16_ragged"]["hidden_seed"])
+    b = G.Case(cfg1, hidden_seed=G.seeds()["ling_fp8_m1"]["hidden_seed"])
     _pair(a, b)
 
 
