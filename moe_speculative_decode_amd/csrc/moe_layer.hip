@@ -1915,11 +1915,14 @@ struct DNTask {
 // This wave's tasks n = wslot, wslot + kWaves, ... < ntask of a flattened down-row list described by
 // info(n, task); the source of each task (LDS or HBM) is its own.  The first task (PRE2: the first
 // two) is loaded before ready(), and the next task's loads are in flight during the current task's
-// compute.  out(task, row, i, v) receives row `row` of the task for token i.  Two tasks ahead of the
-// wait pay where the wait is long against the tasks (slice mode: FP8 at one token 27.2 against
-// 28.5 us) and cost where the tasks are many (unit-major FP8: +0.4 us at six tokens, +1.4 at 16).
+// compute.  out(task, row, i, v) receives row `row` of the task for token i.  A task's token rows
+// are `pitch` bytes apart in LDS; the low plane of a bf16 hi/lo row starts 2 * astride bytes into
+// it.  Two tasks ahead of the wait pay where the wait is long against the tasks (slice mode: FP8 at
+// one token 27.2 against 28.5 us) and cost where the tasks are many (unit-major FP8: +0.4 us at six
+// tokens, +1.4 at 16).
 template <int WF, int NJD, bool PRE2, typename Info, typename Ready, typename Out>
-__device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Info info, Ready ready, Out out) {
+__device__ __forceinline__ void down_flat(int ntask, int astride, int pitch, int wslot, Info info, Ready ready,
+                                          Out out) {
     constexpr int LPR = Geo<WF>::LPR_D, RL = Geo<WF>::RL_D;
     const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
     int n = wslot;
@@ -1958,7 +1961,7 @@ __device__ __forceinline__ void down_flat(int ntask, int astride, int wslot, Inf
     auto compute = [&](const Chunk(&w)[RL][NJD], const DNTask& t) {
         const int nch = t.K / Geo<WF>::EPC;
         for (int i = 0; i < t.t; ++i) {
-            const LDS char* arow = (const LDS char*)t.acts + (int64_t)i * astride * 4;
+            const LDS char* arow = (const LDS char*)t.acts + i * pitch;
             float acc[RL][kAcc];
 #pragma unroll
             for (int rl = 0; rl < RL; ++rl)
@@ -2852,6 +2855,8 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         if (nown > 0) {
             LDS float* pst = cst;
             const int astride = p.act_stride;
+            // vector path: a token row takes 2 bytes per element as one bf16 plane, else 4
+            const int spitch = (act_mode<WF>() == 2 ? 2 : 4) * astride;
             const int nblk = (nown + RTD - 1) / RTD;
             const int nun = U + (has_sh ? 1 : 0);
             const int ng = U - nfit;  // routed units read from HBM in this phase
@@ -2880,14 +2885,14 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     t.s = p.w.sh_down_s;
                     t.srow = h0 + r0;
                 }
-                t.acts = (const LDS float*)xs + (int64_t)t.prow * astride;
+                t.acts = (const LDS float*)((const LDS char*)xs + t.prow * spitch);
             };
             auto ready = [&]() {
                 wait_units(set, (uint32_t)(U * I), has_sh ? (uint32_t)Is : 0u, fault);
                 call_fault = ld_dev(fault.flag);  // used at the y write, long after it lands
                 MOE_TRACE(9);
                 if constexpr (act_mode<WF>() == 2)
-                    stage_rows_b16((LDS char*)xs, act16, astride, NP + (has_sh ? M : 0), astride, 4 * astride);
+                    stage_rows_b16((LDS char*)xs, act16, astride, NP + (has_sh ? M : 0), astride, spitch);
                 else
                     stage_rows<act_mode<WF>()>((LDS float*)xs, p.ws.act, astride, NP + (has_sh ? M : 0), astride);
                 __syncthreads();
@@ -2961,7 +2966,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     return;
                 }
             }
-            down_flat<WF, NJD, true>(nun * nblk, astride, wave_id(), info, ready,
+            down_flat<WF, NJD, true>(nun * nblk, astride, spitch, wave_id(), info, ready,
                                [&](const DNTask& t, int row, int i, float v) { pst[(t.prow + i) * nown + t.orow + row] = v; });
             __syncthreads();
             MOE_TRACE(11);
@@ -3072,7 +3077,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 __syncthreads();
                 MOE_TRACE(10);
             };
-            down_flat<WF, NJD, false>(toff[nseg], I, wave_id(), info, ready, [&](const DNTask& t, int row, int i, float v) {
+            down_flat<WF, NJD, false>(toff[nseg], I, 4 * I, wave_id(), info, ready, [&](const DNTask& t, int row, int i, float v) {
                 pst[t.prow + (t.orow + row) * t.t + i] = v;
             });
             __syncthreads();
@@ -3205,11 +3210,15 @@ hipError_t plan_t(Params& p, int G) {
     const int ka = std::max(p.I, p.Is);
     const int nown = (H + G - 1) / G;
     // slice mode (each workgroup finishes its own y columns of every unit) while M * k is small,
-    // and for MXFP4 weights while all pair rows' SwiGLU outputs fit in LDS as bfloat16 (the slices'
-    // 4-bit down rows mostly fit the LDS window; no partial write-out, no down barrier):
-    // then every workgroup stages all pair rows' SwiGLU outputs; otherwise unit-major down rows
-    const bool mx_slice = WF == MOE_FMT_MXFP4 && njd <= 3 && nown <= 16 && (NP + M) * (ka * 2 + 16) <= 96 * 1024;
-    p.slice_mode = (NP <= 16 || mx_slice) ? 1 : 0;
+    // and while all pair rows' SwiGLU outputs fit in 96 KB of LDS as bfloat16 (bf16 and MXFP4 at a
+    // padded pitch for the matrix cores, FP8 packed for the vector path): every workgroup stages
+    // all pair rows' SwiGLU outputs, every workgroup has the same rows to do, and there is no
+    // partial write-out and no hand-off before the combine (six tokens, unit-major against slice:
+    // bf16 73.5 -> 67.9 us, FP8 59.9 -> 54.0 us); otherwise unit-major down rows
+    const bool mf_fit = (WF == MOE_FMT_BF16 || WF == MOE_FMT_MXFP4) && njd <= 3 && nown <= 16 &&
+                        (NP + M) * (ka * 2 + 16) <= 96 * 1024;
+    const bool f8_fit = WF == MOE_FMT_FP8 && nown <= 16 && (NP + M) * ka * 2 <= 96 * 1024;
+    p.slice_mode = (NP <= 16 || mf_fit || f8_fit) ? 1 : 0;
     // from three tokens on, the M * E logits that every workgroup would read are more polling traffic
     // than one extra hand-off costs: workgroup m selects token m's experts and publishes them
     p.route_delegate = (!p.route_only && M >= 3 && M <= G) ? 1 : 0;
@@ -3281,7 +3290,8 @@ hipError_t plan_t(Params& p, int G) {
     // operand then start in 16 different bank groups
     p.xpitch = H * XB + 16;
     int64_t xb = std::max<int64_t>((int64_t)M * p.xpitch, (int64_t)M * ka * 4);
-    if (p.slice_mode) xb = std::max<int64_t>(xb, (NP + M) * (p.slice_mfma ? 2 * ka + 16 : 4 * ka));
+    if (p.slice_mode)
+        xb = std::max<int64_t>(xb, (NP + M) * (p.slice_mfma ? 2 * ka + 16 : (act_mode<WF>() == 2 ? 2 : 4) * ka));
     p.lds_tab = 0;
     p.lds_x = round16(kTabWords * 4);
     p.lds_cst = p.lds_x + round16(xb);

@@ -29,6 +29,10 @@ SMALL = [
     small("bf16_m5", lens=(5,)),
     small("bf16_m16_ragged", lens=(3, 1, 7, 5)),
     small("bf16_tail", H=520, I=200, Is=72, lens=(6,)),
+    # bf16 slice mode with 54 pair and token rows of 768 (84 KB of LDS), two requests; 63 rows
+    # (seven tokens) would not fit and run unit-major
+    small("bf16_slice_i768_m6", E=64, k=8, I=768, lens=(2, 4)),
+    small("bf16_unit_major_i768_m7", E=64, k=8, I=768, lens=(7,)),
     small("mxfp4_m1", MXFP4, lens=(1,), recipe="iid"),
     small("mxfp4_m2", MXFP4, lens=(2,)),  # slice mode, line-form matrix-core gate/up (below three tokens)
     small("mxfp4_m6", MXFP4, lens=(6,)),
@@ -133,8 +137,9 @@ def test_ling_configs(name):
 @pytest.mark.parametrize("fmt", [BF16, MXFP4, FP8], ids=["bf16", "mxfp4", "fp8"])
 def test_deterministic_and_permutation_equivariant(fmt):
     """Unit-major down rows (and the matrix-core gate/up with its per-wave step ranges for MXFP4
-    and FP8): bit-identical across runs and token orders."""
-    cfg = small("perm", fmt, I=256 if fmt == FP8 else 192, lens=(11,))
+    and FP8): bit-identical across runs and token orders.  99 pair and token rows of 768 do not
+    fit the slice mode's 96 KB of bf16 SwiGLU rows, so bf16 and MXFP4 run unit-major too."""
+    cfg = small("perm", fmt, k=8, I=768, lens=(11,))
     case = G.Case(cfg)
     y1, ids1, w1 = case.run()
     y2, ids2, w2 = case.run()
@@ -183,11 +188,17 @@ def test_router_prologue_deterministic_and_permutation_equivariant():
     assert torch.equal(yp, y1[perm])
 
 
-@pytest.mark.parametrize("lens", [(1,), (6,)], ids=["m1_slice", "m6_unit_major"])
-def test_repeated_calls_fewer_experts_than_cus(lens):
+# (tokens, I): slice mode at one and six tokens; sixteen tokens of I = 768 do not fit the slice
+# mode's LDS rows and run unit-major
+MODES = [((1,), 192), ((6,), 192), ((16,), 768)]
+MODE_IDS = ["m1_slice", "m6_slice", "m16_unit_major"]
+
+
+@pytest.mark.parametrize("lens,inter", MODES, ids=MODE_IDS)
+def test_repeated_calls_fewer_experts_than_cus(lens, inter):
     """E = 64 routed experts on 256 compute units: most workgroups own no router row.  Ten calls in
     a row on one workspace, alternating two token batches, each against the oracle."""
-    cfg = small("rep", lens=lens, recipe="iid" if lens == (1,) else "shared_base")
+    cfg = small("rep", I=inter, lens=lens, recipe="iid" if lens == (1,) else "shared_base")
     a = G.Case(cfg)
     b = G.Case(cfg, x_host=G.accepted_hidden(cfg, a.layer, start=50)[0])
     b.ws = a.ws
@@ -201,14 +212,14 @@ def test_repeated_calls_fewer_experts_than_cus(lens):
     assert mdl.moe_read_status(a.ws) == mdl.MOE_OK
 
 
-@pytest.mark.parametrize("lens", [(1,), (6,)], ids=["m1_slice", "m6_unit_major"])
-def test_wait_timeout_writes_nan(lens):
+@pytest.mark.parametrize("lens,inter", MODES, ids=MODE_IDS)
+def test_wait_timeout_writes_nan(lens, inter):
     """A wait that gives up leaves no output that looks valid.  Forced from the host: the workspace
     header's spin-limit word is set to 16 polls and the call counters of every eighth workgroup are
     advanced, so those workgroups take another call index than the rest and their tags and counter
     sets never meet.  Every wait is bounded, so every workgroup exits; y and the routing weights
     come out NaN and the status word reads MOE_ERR_TIMEOUT.  A fresh workspace then works."""
-    cfg = small("timeout", lens=lens, recipe="iid" if lens == (1,) else "shared_base")
+    cfg = small("timeout", I=inter, lens=lens, recipe="iid" if lens == (1,) else "shared_base")
     case = G.Case(cfg)
     cus = min(torch.cuda.get_device_properties(0).multi_processor_count, 1024)
     words = case.ws.view(torch.int32)
