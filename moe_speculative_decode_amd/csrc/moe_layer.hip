@@ -1920,10 +1920,10 @@ struct DNTask {
 // it.  Two tasks ahead of the wait pay where the wait is long against the tasks (slice mode: FP8 at
 // one token 27.2 against 28.5 us) and cost where the tasks are many (unit-major FP8: +0.4 us at six
 // tokens, +1.4 at 16).
-template <int WF, int NJD, bool PRE2, typename Info, typename Ready, typename Out>
+template <int WF, int NJD, bool PRE2, int RLX = 0, typename Info, typename Ready, typename Out>
 __device__ __forceinline__ void down_flat(int ntask, int astride, int pitch, int wslot, Info info, Ready ready,
                                           Out out) {
-    constexpr int LPR = Geo<WF>::LPR_D, RL = Geo<WF>::RL_D;
+    constexpr int LPR = Geo<WF>::LPR_D, RL = RLX > 0 ? RLX : Geo<WF>::RL_D;  // rows per lane group
     const int lane = threadIdx.x & 63, gi = lane / LPR, sl = lane % LPR;
     int n = wslot;
     Chunk wa[RL][NJD], wb[RL][NJD];
@@ -2857,13 +2857,17 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             const int astride = p.act_stride;
             // vector path: a token row takes 2 bytes per element as one bf16 plane, else 4
             const int spitch = (act_mode<WF>() == 2 ? 2 : 4) * astride;
-            const int nblk = (nown + RTD - 1) / RTD;
+            // FP8 tasks of 12 rows (three per lane group): one task covers a 10-row slice of a unit,
+            // where 8-row tasks left every unit a 2-row task
+            constexpr int RLS = WF == MOE_FMT_FP8 ? 3 : Geo<WF>::RL_D;
+            constexpr int RTS = RLS * (64 / Geo<WF>::LPR_D);
+            const int nblk = (nown + RTS - 1) / RTS;
             const int nun = U + (has_sh ? 1 : 0);
             const int ng = U - nfit;  // routed units read from HBM in this phase
             auto info = [&](int tt, DNTask& t) {
                 const int pidx = tt / nblk, bk = tt - pidx * nblk;
-                const int r0 = bk * RTD;
-                t.nrows = min(RTD, nown - r0);
+                const int r0 = bk * RTS;
+                t.nrows = min(RTS, nown - r0);
                 t.orow = r0;
                 if (pidx < U) {
                     const int u = pidx < ng ? nfit + pidx : pidx - ng;
@@ -2966,7 +2970,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                     return;
                 }
             }
-            down_flat<WF, NJD, true>(nun * nblk, astride, spitch, wave_id(), info, ready,
+            down_flat<WF, NJD, true, RLS>(nun * nblk, astride, spitch, wave_id(), info, ready,
                                [&](const DNTask& t, int row, int i, float v) { pst[(t.prow + i) * nown + t.orow + row] = v; });
             __syncthreads();
             MOE_TRACE(11);
