@@ -3038,12 +3038,14 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
             if (abytes > p.lds_cst - p.lds_x) flat = false;
         }
         if (flat && nseg > 0) {
+            constexpr int RLU = WF == MOE_FMT_FP8 ? 3 : Geo<WF>::RL_D;  // FP8: tasks of 12 rows
+            constexpr int RTU = RLU * (64 / Geo<WF>::LPR_D);
             int toff[kMaxSeg + 1], aoff[kMaxSeg], poff[kMaxSeg];
             toff[0] = 0;
             int ao = 0, po = 0;
             for (int sg = 0; sg < nseg; ++sg) {
                 const int t = __popc(s_mask[sg_u[sg]]);
-                toff[sg + 1] = toff[sg] + (sg_hb[sg] - sg_ha[sg] + RTD - 1) / RTD;
+                toff[sg + 1] = toff[sg] + (sg_hb[sg] - sg_ha[sg] + RTU - 1) / RTU;
                 aoff[sg] = ao;
                 poff[sg] = po;
                 ao += t * I;  // floats
@@ -3053,9 +3055,9 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 int sg = 0;
                 while (sg + 1 < nseg && n >= toff[sg + 1]) ++sg;
                 const int u = sg_u[sg], ha = sg_ha[sg];
-                const int r0 = ha + (n - toff[sg]) * RTD;
+                const int r0 = ha + (n - toff[sg]) * RTU;
                 const int64_t e = uni(s_exp[u]);
-                t.nrows = min(RTD, sg_hb[sg] - r0);
+                t.nrows = min(RTU, sg_hb[sg] - r0);
                 t.t = __popc(uni(s_mask[u]));
                 t.K = I;
                 t.orow = r0 - ha;
@@ -3081,7 +3083,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
                 __syncthreads();
                 MOE_TRACE(10);
             };
-            down_flat<WF, NJD, false>(toff[nseg], I, 4 * I, wave_id(), info, ready, [&](const DNTask& t, int row, int i, float v) {
+            down_flat<WF, NJD, false, RLU>(toff[nseg], I, 4 * I, wave_id(), info, ready, [&](const DNTask& t, int row, int i, float v) {
                 pst[t.prow + (t.orow + row) * t.t + i] = v;
             });
             __syncthreads();
