@@ -194,6 +194,15 @@ __host__ __device__ constexpr int64_t row_bytes(int64_t K) {
     return WF == MOE_FMT_F32 ? 4 * K : (WF == MOE_FMT_BF16 ? 2 * K : (WF == MOE_FMT_FP8 ? K : K / 2));
 }
 
+// Tasks per gate/up pool chunk (about 20 KB of weights: 10 KB went no faster and 40 KB was slower
+// at six bf16 tokens).  The kernel claims chunks of this size and the host sizes each wave's
+// staging room for two of them, so both must use this one definition.
+template <int WF>
+__host__ __device__ constexpr int gu_chunk_tasks(int H) {
+    const int c = 20480 / (2 * rt_gate<WF>() * (int)row_bytes<WF>(H));  // 32-bit: on the path to gate/up
+    return c > 1 ? c : 1;
+}
+
 // Block scales.  scale_mat: the scales of matrix e of a stack [E][rows][K]; scale_row: the scales
 // that apply to absolute row r of one matrix (MXFP4: its K / 32 E8M0 bytes; FP8: the K / 128
 // binary32 scales of its 128-row block).  Other formats have none.
@@ -2568,7 +2577,7 @@ __global__ __launch_bounds__(kThreads) void k_layer(Params p) {
         const int pq = (g.T - g.P0) / npool, pr = (g.T - g.P0) - pq * npool;
         g.pa = g.P0 + g.pool * pq + min(g.pool, pr);
         g.pb = g.pa + pq + (g.pool < pr ? 1 : 0);
-        g.ch = max(1, 20480 / (2 * RTG * (int)row_bytes<WF>(H)));
+        g.ch = gu_chunk_tasks<WF>(H);
         g.nch = (g.pb - g.pa + g.ch - 1) / g.ch;
         return g;
     };
@@ -3289,7 +3298,7 @@ hipError_t plan_t(Params& p, int G) {
         const int64_t rtg = rt_gate<WF>();
         const int64_t T = units * p.I / rtg;
         const int64_t Rs = 7 * T / (80 * (int64_t)G), dyn = T - (int64_t)kWaves * G * Rs;
-        const int64_t ch = std::max<int64_t>(1, 20480 / (2 * rtg * row_bytes<WF>(H)));
+        const int64_t ch = gu_chunk_tasks<WF>(H);
         p.gu_cap = (int)(Rs + 2 * ((dyn + kWaves * G - 1) / (kWaves * G)) + 2 * ch + 5);
         cst = (int64_t)kWaves * p.gu_cap * (rtg * M * 4 + 4) + kWaves * 4;
     }
